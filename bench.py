@@ -1,0 +1,238 @@
+#!/usr/bin/env python3
+"""MLA latent-KV decode benchmark on one MI355X.
+
+A step is one decode step of the whole model's attention: for each of the
+40 layers, the hot path runs once over the batch's new query tokens: YaRN
+RoPE of their query and key rope parts, append of their cache rows,
+absorption of W_UK into the query, split-KV flash decoding over the latent
+cache, LSE combine and the W_UV up-projection.  Every layer has its own
+cache and kv_b_proj weights, all resident in HBM before timing starts.
+
+Default workload: batch 1, one query token, context 32768, contiguous cache
+(the 32K configuration of the headline metric).  The 256K configuration
+(context 262144, KV chunks of 4096) is reported alongside under "ctx256k".
+
+Output: one JSON line.  "value" is decode tokens/s (batch * query tokens per
+step / step time, timed over --steps replays of a HIP graph of the step).
+"roofline" covers the split-KV kernel: algorithmic latent bytes per launch
+(1152 B per visible cached token) over its average duration, measured with
+HIP events recorded by the library on the launch stream.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode tokens/s + latent-KV GB/s (% HBM peak) at 32K and 256K ctx, 1 GPU"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
+BYTES_PER_TOKEN_LAYER = 1152    # 576 bf16 cached values per token per layer
+COUNTERS = os.path.join(ROOT, "profiles", "splitkv_decode_counters.json")
+DECODE_SRC = os.path.join(ROOT, "mla_latent_kv_absorbed_amd", "csrc", "decode.hip")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    with open(DECODE_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def run_workload(k: int, steps: int, warmup: int, use_graph: bool, kv_chunk=None, label=""):
+    import torch
+    import mla_latent_kv_absorbed_amd as M
+    from mla_latent_kv_absorbed_amd.workload import DeviceWorkload
+    from synth.configs import workload
+
+    wl = workload(k)
+    dw = DeviceWorkload(wl, kv_chunk=kv_chunk)
+    t0 = time.perf_counter()
+    layers = [dw.build_layer(l) for l in range(wl.layers)]
+    torch.cuda.synchronize()
+    log(f"[{label}] built {wl.layers} layers of {wl.name} in {time.perf_counter() - t0:.1f}s "
+        f"(chunk {dw.chunk_used}, {'paged' if dw.paged else 'contiguous'})")
+    B, Sq = dw.B, dw.Sq
+    outs = [torch.empty((B, Sq, 32, 128), dtype=torch.bfloat16, device=dw.dev) for _ in layers]
+    lses = [torch.empty((B, Sq, 32), dtype=torch.float32, device=dw.dev) for _ in layers]
+
+    def step():
+        for li, o, l in zip(layers, outs, lses):
+            dw.step(li, out=o, lse=l)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+
+    graph = None
+    if use_graph:
+        try:
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                step()
+            torch.cuda.current_stream().wait_stream(side)
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                step()
+            for _ in range(3):
+                graph.replay()
+                torch.cuda.synchronize()
+                if not all(torch.equal(o, r) for o, r in zip(outs, ref)):
+                    raise RuntimeError("graph replay differs from eager step")
+        except Exception as e:  # noqa: BLE001
+            log(f"[{label}] graph capture unavailable ({e}); timing eager launches")
+            graph = None
+
+    run = graph.replay if graph is not None else step
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        run()
+    end.record()
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / steps
+    if not all(torch.equal(o, r) for o, r in zip(outs, ref)):
+        raise RuntimeError("timed steps changed the result")
+
+    # split-KV kernel durations: HIP events recorded by the library around
+    # the kernel, on the stream it is launched on, over `steps` eager steps
+    M.mla_timing_enable(steps * len(layers))
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    kern_ms, launches = M.mla_timing_collect()
+    M.mla_timing_disable()
+
+    tokens_ctx = sum(dw.lens)
+    bytes_per_launch = tokens_ctx * BYTES_PER_TOKEN_LAYER
+    avg_kernel_s = kern_ms / 1e3 / launches
+    step_bytes = bytes_per_launch * len(layers)
+    res = dict(
+        workload=wl.name, batch=B, query_tokens=Sq, context=list(dw.lens) if B <= 4 else f"{B} seqs, sum {tokens_ctx}",
+        layers=len(layers), layout="paged" if dw.paged else "contiguous", kv_chunk=dw.chunk_used,
+        graph=graph is not None, ms_per_step=ms_per_step, tokens_per_s=B * Sq / (ms_per_step / 1e3),
+        step_latent_gbps=step_bytes / (ms_per_step / 1e3) / 1e9,
+        kernel_avg_us=avg_kernel_s * 1e6, kernel_bytes_per_launch=bytes_per_launch,
+        kernel_latent_gbps=bytes_per_launch / avg_kernel_s / 1e9,
+    )
+    del layers, outs, lses, ref, graph
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(k: int, budget_s: float = 15.0):
+    """The un-absorbed oracle on the host: layer 0 of workload k, a head subset."""
+    import numpy as np
+    import threadpoolctl
+    import oracle as O
+    import synth
+    from synth.configs import workload
+
+    wl = workload(k)
+    L, Sq, seed = wl.lens[0], wl.sq, wl.seed
+    f = O.bf16_bits_to_float
+    inv = O.yarn_inv_freq()
+    c = f(synth.latent_bits(seed, 0, 0, 0, L))
+    kk = O.round_to_bf16(O.rope_rotate(f(synth.kpe_bits(seed, 0, 0, 0, L)), np.arange(L), inv))
+    qn = f(synth.qnope_bits(seed, 0, 0, Sq))
+    qp = O.round_to_bf16(O.rope_rotate(f(synth.qpe_bits(seed, 0, 0, Sq)), (L - Sq + np.arange(Sq))[:, None], inv))
+    w = f(synth.wkvb_bits(seed, 0))
+    scale = O.softmax_scale()
+    t0 = time.perf_counter()
+    O.mla_attention_unabsorbed(qn, qp, c, kk, w, scale, heads=[0])
+    one = time.perf_counter() - t0
+    nheads = int(max(1, min(32, budget_s // max(one, 1e-3))))
+    t0 = time.perf_counter()
+    O.mla_attention_unabsorbed(qn, qp, c, kk, w, scale, heads=list(range(nheads)))
+    dt = time.perf_counter() - t0
+    step_s = dt * (32 / nheads) * wl.layers
+    threads = sum(p.get("num_threads", 0) for p in threadpoolctl.threadpool_info() if p.get("user_api") == "blas")
+    return {"value": wl.batch * Sq / step_s, "unit": "tokens/s", "cores": threads or os.cpu_count(),
+            "kind": "oracle",
+            "sample": (f"un-absorbed fp64 oracle, layer 0, heads 0..{nheads - 1} of 32, full {L}-token "
+                       f"context, {dt:.1f}s; scaled x{32 / nheads:g} (heads) x{wl.layers} (layers) to one step")}
+
+
+def traffic_from_counters(bytes_per_launch):
+    """HBM bytes per launch from committed rocprofv3 counters, if they match this kernel source."""
+    if not os.path.exists(COUNTERS):
+        return None
+    with open(COUNTERS) as fh:
+        c = json.load(fh)
+    if c.get("source_hash") != source_hash():
+        return None
+    return c.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=1, help="workload index (1 = 32K, 3 = 256K)")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a HIP graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-256k", action="store_true", help="skip the 256K report")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    torch.cuda.init()
+    main_res = run_workload(args.config, args.steps, args.warmup, not args.no_graph, label=f"config{args.config}")
+    log(f"[config{args.config}] {json.dumps(main_res)}")
+    extra = None
+    if not args.no_256k and args.config != 3:
+        extra = {}
+        for name, chunk in (("kv_chunk_4096", 4096), ("kv_chunk_auto", 0)):
+            r = run_workload(3, max(3, min(args.steps, 10)), 2, not args.no_graph, kv_chunk=chunk, label=f"256k-{name}")
+            log(f"[256k {name}] {json.dumps(r)}")
+            extra[name] = {k: r[k] for k in ("tokens_per_s", "ms_per_step", "step_latent_gbps", "kernel_avg_us",
+                                            "kernel_latent_gbps", "kv_chunk")}
+            extra[name]["kernel_hbm_frac"] = r["kernel_latent_gbps"] / HBM_PEAK_GBPS
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.config)
+
+    bpl = main_res["kernel_bytes_per_launch"]
+    achieved = main_res["kernel_latent_gbps"]
+    line = {
+        "metric": METRIC,
+        "value": main_res["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) latents, rope keys and queries, N(0,1/512) kv_b_proj per layer; no trained weights",
+        "config": {k: main_res[k] for k in ("workload", "batch", "query_tokens", "context", "layers", "layout",
+                                           "kv_chunk", "graph")},
+        "latent_gbps_step": main_res["step_latent_gbps"],
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic_from_counters(bpl),
+            "kernel": "splitkv_decode", "bytes_per_launch": bpl, "avg_launch_us": main_res["kernel_avg_us"],
+        },
+        "cpu_baseline": cpu,
+        "ctx256k": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

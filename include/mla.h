@@ -1,0 +1,188 @@
+/*
+ * mla.h - C ABI of the MI355X (gfx950) MLA latent-KV decode library.
+ *
+ * Multi-head Latent Attention decode over a compressed KV cache in the
+ * Xing4.0-29B-A4B attention shape: 32 heads, kv_lora_rank 512, qk_nope 128,
+ * qk_rope 64, v_head 128, YaRN rope (factor 64, 4096 -> 262144).
+ *
+ * Pages cited:
+ *  [KV-ledger] "256K 长上下文真能本地用？Xing4.0 原生长上下文的工程代价拆解",
+ *              §一 (config.json: kv_lora_rank, v_head_dim, rope_scaling,
+ *              attention_bias) and §二 (what the cache holds per token).
+ *  [MLA-arch]  "mHC+MLA+MTP 是什么？拆开给 Agent 用的百亿 MoE", section
+ *              "MLA：256K 上下文的内存革命" (kv_a_proj_with_mqa writes a 512-wide
+ *              latent plus a 64-wide rope component per token into the cache;
+ *              kv_b_proj expands per-head keys and values from the latent at
+ *              attention time; YaRN rope with yarn_get_mscale).
+ *
+ * General conventions
+ *  - Every pointer argument is a DEVICE pointer unless marked "host".
+ *  - bf16 is bfloat16 (1-8-7), passed as raw 16-bit values.
+ *  - The caller owns every buffer.  The library allocates nothing, keeps no
+ *    pointer after a call returns and holds no state between calls (the
+ *    opt-in kernel timing at the end of this header aside).
+ *  - All work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *    stream).  MLA_OK means "enqueued"; device faults show up at the
+ *    caller's next synchronisation.  No call synchronises the host.
+ *  - Arguments are validated on the host before anything is enqueued; a bad
+ *    argument returns an error code and enqueues nothing.  Contents of device
+ *    arrays (block tables, context lengths, slot mappings) are not read by
+ *    the host, so out-of-range values there are the caller's responsibility.
+ *  - The library is reentrant; concurrent calls on different streams must
+ *    use different workspaces.
+ */
+#ifndef MLA_LATENT_KV_ABSORBED_MLA_H
+#define MLA_LATENT_KV_ABSORBED_MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t mla_status;
+#define MLA_OK               0
+#define MLA_ERR_NULL         1   /* a required pointer is NULL                       */
+#define MLA_ERR_SHAPE        2   /* shape constants or sizes are not supported       */
+#define MLA_ERR_RANGE        3   /* a size is out of range (e.g. Sq > max_ctx_len)   */
+#define MLA_ERR_ALIGN        4   /* a pointer or leading dimension is misaligned     */
+#define MLA_ERR_WORKSPACE    5   /* workspace too small                              */
+#define MLA_ERR_DEVICE       6   /* a HIP runtime call failed                        */
+#define MLA_ERR_UNSUPPORTED  7   /* a valid request this build does not implement    */
+
+/* Attention shape.  The library implements exactly num_heads 32,
+ * kv_lora_rank 512, qk_nope_head_dim 128, qk_rope_head_dim 64, v_head_dim 128
+ * and page_size 64 ([KV-ledger §一]; [MLA-arch]); anything else returns
+ * MLA_ERR_SHAPE.  softmax_scale multiplies q.k; for this model it is
+ * (qk_nope + qk_rope)^-1/2 * mscale^2 with mscale = 0.1 ln(64) + 1
+ * (YaRN's attention-logit correction named by [MLA-arch]); see
+ * mla_default_softmax_scale(). */
+typedef struct {
+    int32_t num_heads;
+    int32_t kv_lora_rank;
+    int32_t qk_nope_head_dim;
+    int32_t qk_rope_head_dim;
+    int32_t v_head_dim;
+    int32_t page_size;
+    float   softmax_scale;
+} mla_shape;
+
+/* YaRN rope parameters ([KV-ledger §一] rope_scaling; base not printed for
+ * this model, 10000 is the customary value).  Rotation pairs element i with
+ * element i + rope_dim/2 of each rope vector. */
+typedef struct {
+    double  base;                 /* rope theta                        */
+    double  factor;               /* 64                                */
+    double  original_max_position;/* 4096                              */
+    double  beta_fast;            /* 32                                */
+    double  beta_slow;            /* 1                                 */
+    int32_t rope_dim;             /* 64                                */
+} mla_rope_params;
+
+/* Fills *shape with the model's shape and its softmax scale (host). */
+mla_status mla_default_shape(mla_shape* shape /* host */);
+
+/* Fills *params with the model's YaRN parameters, base 10000 (host). */
+mla_status mla_default_rope(mla_rope_params* params /* host */);
+
+/* Human-readable name of a status code (static string). */
+const char* mla_status_string(mla_status status);
+
+/* Apply YaRN rotary position embedding: dst row r = rot(src row r, positions[r]).
+ * [MLA-arch]: the rope component uses YaRN scaling (factor 64 from 4096
+ * positions); [KV-ledger §一] prints the rope_scaling fields.
+ *   src, ld_src  bf16 rows; row r's rope vector is src[r*ld_src .. + rope_dim)
+ *   dst, ld_dst  bf16 rows receiving the rotated vectors (dst == src with
+ *                ld_dst == ld_src rotates in place; other elements of a dst
+ *                row are not touched)
+ *   positions    int32 [n] position of each row (0 <= pos < 2^24)
+ *   n            rows (0 is a no-op)
+ * Element i pairs with element i + rope_dim/2.  Angles pos * inv_freq and
+ * their cos/sin are formed in fp64; each rotated value is rounded once from
+ * fp64 to bf16 (nearest, ties to even).  src and dst must be 16-byte
+ * aligned with leading dimensions >= rope_dim and multiples of 8; src and dst
+ * rows must not partially overlap. */
+mla_status mla_rope_yarn(const mla_rope_params* params /* host */, const void* src, int64_t ld_src,
+                         void* dst, int64_t ld_dst, const int32_t* positions, int64_t n, void* stream);
+
+/* Write cache rows: cache[slot] = [c_kv row (512) | k_pe row (64)], a bit copy.
+ * [MLA-arch]: only the compressed latent and the rope component are cached
+ * per token, no per-head K or V.
+ *   cache         bf16 [num_slots][576]; for the paged layout slot =
+ *                 page * page_size + offset, for the contiguous layout slot =
+ *                 b * stride + t
+ *   c_kv, ld_c    bf16 latent rows [n][ld_c] (ld_c >= 512)
+ *   k_pe, ld_k    bf16 rope rows [n][ld_k] (ld_k >= 64), already rotated
+ *   slot_mapping  int64 [n]; a negative slot skips the row
+ * Requires 16-byte aligned cache, c_kv and k_pe and ld_c, ld_k multiples
+ * of 8 (MLA_ERR_ALIGN otherwise). */
+mla_status mla_cache_append(const mla_shape* shape /* host */, void* cache, int64_t num_slots,
+                            const void* c_kv, int64_t ld_c, const void* k_pe, int64_t ld_k,
+                            const int64_t* slot_mapping, int64_t n, void* stream);
+
+/* Decode attention against a contiguous cache.
+ * For query token j of sequence b (position p = L_b - Sq + j, whose own row
+ * is already in the cache) and head h:
+ *   q_lat = W_UK[h]^T q_nope            (W_UK folded into the query)
+ *   s_t   = softmax_scale * (q_lat . c_t + q_pe . k_pe_t),  t = 0..p
+ *   o     = W_UV[h] * sum_t softmax(s)_t c_t
+ * which equals attention with keys [W_UK c_t ; k_pe_t] and values W_UV c_t
+ * expanded by kv_b_proj ([MLA-arch]).  W_UK[h] and W_UV[h] are rows
+ * [h*256, h*256+128) and [h*256+128, h*256+256) of w_kv_b.
+ *   q_nope       bf16 [B][Sq][32][128]
+ *   q_pe         bf16 [B][Sq][32][64], already rotated
+ *   w_kv_b       bf16 [8192][512] (nn.Linear storage: out x in)
+ *   cache        bf16 [B][stride_tokens][576]
+ *   ctx_lens     int32 [B], Sq <= L_b <= min(max_ctx_len, stride_tokens)
+ *   max_ctx_len  host upper bound of ctx_lens
+ *   kv_chunk     tokens per split, a multiple of 64, or 0 to let the
+ *                library choose
+ *   out          bf16 [B][Sq][32][128]
+ *   lse          fp32 [B][Sq][32] natural-log sum of exp(s_t), or NULL
+ *   workspace    device scratch of mla_decode_workspace_size() bytes,
+ *                256-byte aligned
+ * Supports 1 <= Sq <= 16.  B = 0 is a no-op. */
+mla_status mla_decode(const mla_shape* shape /* host */, const void* q_nope, const void* q_pe,
+                      const void* w_kv_b, const void* cache, int64_t stride_tokens,
+                      const int32_t* ctx_lens, int32_t max_ctx_len, int32_t B, int32_t Sq,
+                      int32_t kv_chunk, void* out, float* lse, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* Decode attention against a paged cache: as mla_decode, but token t of
+ * sequence b lives in slot block_table[b][t / 64] * 64 + t % 64 of
+ *   cache        bf16 [num_pages][64][576]
+ *   block_table  int32 [B][max_pages_per_seq]
+ * Every page a sequence uses must be in [0, num_pages). */
+mla_status mla_decode_paged(const mla_shape* shape /* host */, const void* q_nope, const void* q_pe,
+                            const void* w_kv_b, const void* cache, int64_t num_pages,
+                            const int32_t* block_table, int32_t max_pages_per_seq,
+                            const int32_t* ctx_lens, int32_t max_ctx_len, int32_t B, int32_t Sq,
+                            int32_t kv_chunk, void* out, float* lse, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* Workspace bytes mla_decode / mla_decode_paged need for these sizes (host).
+ * kv_chunk as in mla_decode (0 = the library's choice). */
+mla_status mla_decode_workspace_size(const mla_shape* shape /* host */, int32_t B, int32_t Sq,
+                                     int32_t max_ctx_len, int32_t kv_chunk,
+                                     size_t* bytes /* host */);
+
+/* The kv_chunk the library would use for kv_chunk = 0 (host). */
+mla_status mla_decode_auto_chunk(int32_t B, int32_t Sq, int32_t max_ctx_len, int32_t* kv_chunk /* host */);
+
+/* Kernel timing, a profiling aid (not needed to compute anything).
+ * After mla_timing_enable(n), each of the next n decode calls records a HIP
+ * event pair on its stream around its split-KV attention kernel(s); calls
+ * beyond n are not timed.  mla_timing_collect() waits for the recorded
+ * events and returns the summed kernel time in milliseconds and the number
+ * of timed kernel launches; mla_timing_disable() releases the events.  This
+ * is the library's only global state: enable it outside HIP graph capture,
+ * from one host thread. */
+mla_status mla_timing_enable(int32_t max_calls);
+mla_status mla_timing_collect(double* total_ms /* host */, int32_t* launches /* host */);
+mla_status mla_timing_disable(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MLA_LATENT_KV_ABSORBED_MLA_H */

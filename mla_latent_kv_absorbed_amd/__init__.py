@@ -1,0 +1,263 @@
+"""Python binding of the MLA latent-KV decode library (lib/libmla.so).
+
+Argument marshalling only: every step runs in the HIP library.  Tensors are
+torch tensors on the GPU (torch provides device memory and the stream); the
+functions pass their pointers, sizes and the current HIP stream to the C ABI
+declared in include/mla.h and raise ``MlaError`` on any non-zero status.
+There is no CPU path: without the built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from .build import lib_path
+
+__all__ = [
+    "MlaError", "MlaShape", "MlaRopeParams", "default_shape", "default_rope", "library",
+    "mla_rope_yarn", "mla_cache_append", "mla_decode", "mla_decode_paged",
+    "mla_decode_workspace_size", "mla_decode_auto_chunk", "mla_status_string",
+    "mla_timing_enable", "mla_timing_collect", "mla_timing_disable",
+]
+
+
+class MlaError(RuntimeError):
+    pass
+
+
+class MlaShape(ctypes.Structure):
+    _fields_ = [("num_heads", ctypes.c_int32), ("kv_lora_rank", ctypes.c_int32),
+                ("qk_nope_head_dim", ctypes.c_int32), ("qk_rope_head_dim", ctypes.c_int32),
+                ("v_head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float)]
+
+
+class MlaRopeParams(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_double), ("factor", ctypes.c_double),
+                ("original_max_position", ctypes.c_double), ("beta_fast", ctypes.c_double),
+                ("beta_slow", ctypes.c_double), ("rope_dim", ctypes.c_int32)]
+
+
+_LIB = None
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+
+
+def library() -> ctypes.CDLL:
+    """The loaded libmla.so; raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        path = lib_path()
+        if not os.path.exists(path):
+            raise MlaError(f"{path} is missing: build it with __graft_entry__.build() "
+                           "(hipcc, gfx950); there is no fallback")
+        lib = ctypes.CDLL(path)
+        sig = {
+            "mla_default_shape": [ctypes.POINTER(MlaShape)],
+            "mla_default_rope": [ctypes.POINTER(MlaRopeParams)],
+            "mla_rope_yarn": [ctypes.POINTER(MlaRopeParams), _P, _I64, _P, _I64, _P, _I64, _P],
+            "mla_cache_append": [ctypes.POINTER(MlaShape), _P, _I64, _P, _I64, _P, _I64, _P, _I64, _P],
+            "mla_decode": [ctypes.POINTER(MlaShape), _P, _P, _P, _P, _I64, _P, _I32, _I32, _I32, _I32,
+                           _P, _P, _P, ctypes.c_size_t, _P],
+            "mla_decode_paged": [ctypes.POINTER(MlaShape), _P, _P, _P, _P, _I64, _P, _I32, _P, _I32,
+                                 _I32, _I32, _I32, _P, _P, _P, ctypes.c_size_t, _P],
+            "mla_decode_workspace_size": [ctypes.POINTER(MlaShape), _I32, _I32, _I32, _I32,
+                                          ctypes.POINTER(ctypes.c_size_t)],
+            "mla_decode_auto_chunk": [_I32, _I32, _I32, ctypes.POINTER(_I32)],
+            "mla_timing_enable": [_I32],
+            "mla_timing_collect": [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I32)],
+            "mla_timing_disable": [],
+        }
+        for name, args in sig.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int32
+        lib.mla_status_string.argtypes = [ctypes.c_int32]
+        lib.mla_status_string.restype = ctypes.c_char_p
+        _LIB = lib
+    return _LIB
+
+
+def mla_status_string(code: int) -> str:
+    return library().mla_status_string(code).decode()
+
+
+def _check(code: int, what: str):
+    if code != 0:
+        raise MlaError(f"{what}: {mla_status_string(code)} ({code})")
+
+
+def default_shape() -> MlaShape:
+    s = MlaShape()
+    _check(library().mla_default_shape(ctypes.byref(s)), "mla_default_shape")
+    return s
+
+
+def default_rope() -> MlaRopeParams:
+    p = MlaRopeParams()
+    _check(library().mla_default_rope(ctypes.byref(p)), "mla_default_rope")
+    return p
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, dtype, name, last_contig=True):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise MlaError(f"{name} must be on the GPU (got {t.device})")
+    if t.dtype != dtype:
+        raise MlaError(f"{name} must be {dtype} (got {t.dtype})")
+    if last_contig and not t.is_contiguous():
+        raise MlaError(f"{name} must be contiguous")
+
+
+def _rows2d(x, name):
+    if x.dtype != torch.bfloat16 or x.device.type != "cuda":
+        raise MlaError(f"{name} must be a bf16 GPU tensor")
+    if x.dim() == 1:
+        return x.view(1, -1)
+    if x.is_contiguous():
+        return x.reshape(-1, x.shape[-1])
+    if x.dim() == 2 and x.stride(1) == 1:
+        return x
+    raise MlaError(f"{name} must be contiguous or a 2-D row-strided view")
+
+
+def mla_rope_yarn(src: torch.Tensor, positions: torch.Tensor, dst: torch.Tensor | None = None,
+                  params: MlaRopeParams | None = None, stream=None) -> torch.Tensor:
+    """dst rows = YaRN RoPE of src rows (first 64 elements) at ``positions``.
+
+    Rows run along the last dimension; ``dst`` defaults to ``src`` (in place).
+    """
+    _need(positions, torch.int32, "positions")
+    s2 = _rows2d(src, "src")
+    d2 = s2 if dst is None else _rows2d(dst, "dst")
+    n = s2.shape[0]
+    if d2.shape[0] != n or positions.numel() != n:
+        raise MlaError(f"src has {n} rows, dst {d2.shape[0]}, positions {positions.numel()}")
+    p = params if params is not None else default_rope()
+    _check(library().mla_rope_yarn(ctypes.byref(p), _ptr(s2), s2.stride(0), _ptr(d2), d2.stride(0),
+                                   _ptr(positions), n, _stream(stream)), "mla_rope_yarn")
+    return src if dst is None else dst
+
+
+def mla_cache_append(cache: torch.Tensor, c_kv: torch.Tensor, k_pe: torch.Tensor,
+                     slot_mapping: torch.Tensor, shape: MlaShape | None = None, stream=None):
+    """cache.view(-1, 576)[slot] = [c_kv row | k_pe row] (bit copy); slot < 0 skips."""
+    _need(cache, torch.bfloat16, "cache")
+    _need(slot_mapping, torch.int64, "slot_mapping")
+    for t, name in ((c_kv, "c_kv"), (k_pe, "k_pe")):
+        if t.dtype != torch.bfloat16 or t.device.type != "cuda" or t.dim() != 2 or t.stride(1) != 1:
+            raise MlaError(f"{name} must be a 2-D bf16 GPU tensor with unit column stride")
+    n = c_kv.shape[0]
+    if k_pe.shape[0] != n or slot_mapping.numel() != n:
+        raise MlaError("c_kv, k_pe and slot_mapping need the same number of rows")
+    num_slots = cache.numel() // 576
+    s = shape if shape is not None else default_shape()
+    _check(library().mla_cache_append(ctypes.byref(s), _ptr(cache), num_slots, _ptr(c_kv), c_kv.stride(0),
+                                      _ptr(k_pe), k_pe.stride(0), _ptr(slot_mapping), n, _stream(stream)),
+           "mla_cache_append")
+
+
+def mla_decode_workspace_size(B: int, Sq: int, max_ctx_len: int, kv_chunk: int = 0,
+                              shape: MlaShape | None = None) -> int:
+    s = shape if shape is not None else default_shape()
+    out = ctypes.c_size_t()
+    _check(library().mla_decode_workspace_size(ctypes.byref(s), B, Sq, max_ctx_len, kv_chunk,
+                                               ctypes.byref(out)), "mla_decode_workspace_size")
+    return out.value
+
+
+def mla_decode_auto_chunk(B: int, Sq: int, max_ctx_len: int) -> int:
+    out = _I32()
+    _check(library().mla_decode_auto_chunk(B, Sq, max_ctx_len, ctypes.byref(out)), "mla_decode_auto_chunk")
+    return out.value
+
+
+def _decode_io(q_nope, q_pe, w_kv_b, ctx_lens, out, lse, workspace, B, Sq, max_ctx_len, kv_chunk, shape):
+    _need(q_nope, torch.bfloat16, "q_nope")
+    _need(q_pe, torch.bfloat16, "q_pe")
+    _need(w_kv_b, torch.bfloat16, "w_kv_b")
+    _need(ctx_lens, torch.int32, "ctx_lens")
+    if tuple(q_nope.shape) != (B, Sq, 32, 128) or tuple(q_pe.shape) != (B, Sq, 32, 64):
+        raise MlaError("q_nope must be [B, Sq, 32, 128] and q_pe [B, Sq, 32, 64]")
+    if tuple(w_kv_b.shape) != (8192, 512):
+        raise MlaError("w_kv_b must be [8192, 512]")
+    if ctx_lens.numel() != B:
+        raise MlaError("ctx_lens must have B entries")
+    dev = q_nope.device
+    if out is None:
+        out = torch.empty((B, Sq, 32, 128), dtype=torch.bfloat16, device=dev)
+    _need(out, torch.bfloat16, "out")
+    if lse is not None:
+        _need(lse, torch.float32, "lse")
+    s = shape if shape is not None else default_shape()
+    need = mla_decode_workspace_size(B, Sq, max_ctx_len, kv_chunk, s)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _need(workspace, torch.uint8, "workspace")
+    return out, lse, workspace, s
+
+
+def mla_decode(q_nope, q_pe, w_kv_b, cache, ctx_lens, max_ctx_len: int, kv_chunk: int = 0,
+               out=None, lse=None, workspace=None, shape: MlaShape | None = None, stream=None):
+    """Decode against a contiguous cache [B, stride, 576]; returns (out, lse)."""
+    _need(cache, torch.bfloat16, "cache")
+    B, Sq = q_nope.shape[0], q_nope.shape[1]
+    if cache.dim() != 3 or cache.shape[0] != B or cache.shape[2] != 576:
+        raise MlaError("cache must be [B, stride, 576]")
+    out, lse, workspace, s = _decode_io(q_nope, q_pe, w_kv_b, ctx_lens, out, lse, workspace, B, Sq,
+                                        max_ctx_len, kv_chunk, shape)
+    _check(library().mla_decode(ctypes.byref(s), _ptr(q_nope), _ptr(q_pe), _ptr(w_kv_b), _ptr(cache),
+                                cache.shape[1], _ptr(ctx_lens), max_ctx_len, B, Sq, kv_chunk, _ptr(out),
+                                _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream)),
+           "mla_decode")
+    return out, lse
+
+
+def mla_decode_paged(q_nope, q_pe, w_kv_b, cache, block_table, ctx_lens, max_ctx_len: int,
+                     kv_chunk: int = 0, out=None, lse=None, workspace=None,
+                     shape: MlaShape | None = None, stream=None):
+    """Decode against a paged cache [num_pages, 64, 576]; returns (out, lse)."""
+    _need(cache, torch.bfloat16, "cache")
+    _need(block_table, torch.int32, "block_table")
+    B, Sq = q_nope.shape[0], q_nope.shape[1]
+    if cache.dim() != 3 or cache.shape[1] != 64 or cache.shape[2] != 576:
+        raise MlaError("cache must be [num_pages, 64, 576]")
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise MlaError("block_table must be [B, max_pages_per_seq]")
+    out, lse, workspace, s = _decode_io(q_nope, q_pe, w_kv_b, ctx_lens, out, lse, workspace, B, Sq,
+                                        max_ctx_len, kv_chunk, shape)
+    _check(library().mla_decode_paged(ctypes.byref(s), _ptr(q_nope), _ptr(q_pe), _ptr(w_kv_b), _ptr(cache),
+                                      cache.shape[0], _ptr(block_table), block_table.shape[1],
+                                      _ptr(ctx_lens), max_ctx_len, B, Sq, kv_chunk, _ptr(out), _ptr(lse),
+                                      _ptr(workspace), workspace.numel(), _stream(stream)),
+           "mla_decode_paged")
+    return out, lse
+
+
+def mla_timing_enable(max_calls: int):
+    """Record HIP events around the split-KV kernel of the next max_calls decode calls."""
+    _check(library().mla_timing_enable(max_calls), "mla_timing_enable")
+
+
+def mla_timing_collect():
+    """(summed split-KV kernel milliseconds, timed decode calls); waits for the events."""
+    ms, n = ctypes.c_double(), _I32()
+    _check(library().mla_timing_collect(ctypes.byref(ms), ctypes.byref(n)), "mla_timing_collect")
+    return ms.value, n.value
+
+
+def mla_timing_disable():
+    _check(library().mla_timing_disable(), "mla_timing_disable")

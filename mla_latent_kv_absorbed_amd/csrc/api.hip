@@ -1,0 +1,315 @@
+// C ABI of the MLA latent-KV decode library (declarations and contracts in
+// include/mla.h).  Host side only: argument checks, split selection,
+// workspace carving and kernel launches on the caller's stream.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/mla.h"
+#include "mla_internal.h"
+
+using namespace mla;
+
+namespace {
+
+constexpr int kMaxSq = 16;
+
+// Opt-in kernel timing (mla_timing_*): event pairs around split-KV launches.
+struct Timing {
+  bool on = false;
+  int capacity = 0;       // event pairs
+  int used = 0;
+  hipEvent_t* ev = nullptr;   // 2 * capacity events
+} g_timing;
+
+void timing_free() {
+  if (g_timing.ev != nullptr) {
+    for (int i = 0; i < 2 * g_timing.capacity; ++i) (void)hipEventDestroy(g_timing.ev[i]);
+    delete[] g_timing.ev;
+  }
+  g_timing = Timing();
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+mla_status check_shape(const mla_shape* s) {
+  if (s == nullptr) return MLA_ERR_NULL;
+  if (s->num_heads != kHeads || s->kv_lora_rank != kLatent || s->qk_nope_head_dim != kNope ||
+      s->qk_rope_head_dim != kRope || s->v_head_dim != kVDim || s->page_size != kPage)
+    return MLA_ERR_SHAPE;
+  if (!(s->softmax_scale > 0.f) || !isfinite(s->softmax_scale)) return MLA_ERR_RANGE;
+  return MLA_OK;
+}
+
+// Tokens per split when the caller passes 0: aim at one workgroup per compute
+// unit for a single sequence and about four per unit for batches (sequences
+// of a batch may be shorter than max_ctx_len), never below two tiles.
+int auto_chunk(int B, int max_ctx) {
+  if (B < 1) B = 1;
+  const int tiles = (max_ctx + kPage - 1) / kPage;
+  const int target_units = (B <= 1) ? 256 : 1024;
+  int splits = (target_units + B - 1) / B;
+  if (splits < 1) splits = 1;
+  int tiles_per_split = (tiles + splits - 1) / splits;
+  if (tiles_per_split < 2) tiles_per_split = 2;
+  return tiles_per_split * kPage;
+}
+
+int splits_for(int max_ctx, int chunk) { return (max_ctx + chunk - 1) / chunk; }
+
+// YaRN NTK-by-parts frequencies (Peng et al., 2023): pairs turning more than
+// beta_fast times over the original context keep base^(-2i/d); pairs turning
+// fewer than beta_slow times are divided by the factor; a linear ramp over
+// the pair index joins the two.
+void yarn_frequencies(const mla_rope_params& p, double* out) {
+  const int half = p.rope_dim / 2;
+  const double two_pi = 6.283185307179586476925286766559;
+  for (int i = 0; i < half; ++i) {
+    const double f = pow(p.base, -2.0 * i / p.rope_dim);
+    out[i] = f;
+  }
+  if (p.factor <= 1.0) return;
+  auto index_of_turns = [&](double turns) {
+    return p.rope_dim * log(p.original_max_position / (two_pi * turns)) / (2.0 * log(p.base));
+  };
+  double lo = floor(index_of_turns(p.beta_fast));
+  double hi = ceil(index_of_turns(p.beta_slow));
+  if (lo < 0) lo = 0;
+  if (hi > p.rope_dim - 1) hi = p.rope_dim - 1;
+  if (hi == lo) hi = lo + 1e-3;
+  for (int i = 0; i < half; ++i) {
+    double ramp = (i - lo) / (hi - lo);
+    ramp = ramp < 0 ? 0 : (ramp > 1 ? 1 : ramp);
+    out[i] = out[i] * (1.0 - ramp) + (out[i] / p.factor) * ramp;
+  }
+}
+
+mla_status decode_common(const mla_shape* shape, const void* q_nope, const void* q_pe,
+                         const void* w_kv_b, const void* cache, int64_t stride_tokens,
+                         int64_t num_pages, const int32_t* block_table, int32_t max_pages,
+                         const int32_t* ctx_lens, int32_t max_ctx_len, int32_t B, int32_t Sq,
+                         int32_t kv_chunk, void* out, float* lse, void* workspace,
+                         size_t workspace_bytes, void* stream, bool paged) {
+  mla_status st = check_shape(shape);
+  if (st != MLA_OK) return st;
+  if (B < 0 || Sq < 1 || Sq > kMaxSq || max_ctx_len < Sq) return MLA_ERR_RANGE;
+  if (B == 0) return MLA_OK;
+  if (!q_nope || !q_pe || !w_kv_b || !cache || !ctx_lens || !out || !workspace) return MLA_ERR_NULL;
+  if (paged) {
+    if (!block_table) return MLA_ERR_NULL;
+    if (num_pages < 1 || max_pages < (max_ctx_len + kPage - 1) / kPage) return MLA_ERR_RANGE;
+  } else {
+    if (stride_tokens < max_ctx_len) return MLA_ERR_RANGE;
+  }
+  if (kv_chunk < 0 || kv_chunk % kPage != 0) return MLA_ERR_RANGE;
+  if (!aligned16(q_nope) || !aligned16(q_pe) || !aligned16(w_kv_b) || !aligned16(cache) ||
+      !aligned16(out) || ((uintptr_t)workspace & 255u) != 0)
+    return MLA_ERR_ALIGN;
+  if (lse != nullptr && ((uintptr_t)lse & 3u) != 0) return MLA_ERR_ALIGN;
+  const int chunk = kv_chunk ? kv_chunk : auto_chunk(B, max_ctx_len);
+  const int splits = splits_for(max_ctx_len, chunk);
+  if ((int64_t)B * splits > 0x7FFFFFFF) return MLA_ERR_RANGE;
+  const WorkspaceLayout wl = workspace_layout(B, Sq, splits);
+  if (workspace_bytes < wl.total) return MLA_ERR_WORKSPACE;
+
+  uint8_t* ws = (uint8_t*)workspace;
+  uint16_t* qabs = (uint16_t*)(ws + wl.qabs);
+  float* qres = (float*)(ws + wl.qres);
+  float* lse2 = (float*)(ws + wl.lse2);
+  float* part_o = (float*)(ws + wl.part_o);
+  float* part_lse = (float*)(ws + wl.part_lse);
+  float* o_lat = (float*)(ws + wl.o_lat);
+  hipStream_t s = (hipStream_t)stream;
+  const int rows = B * Sq;
+
+  if (launch_absorb((const uint16_t*)q_nope, (const uint16_t*)q_pe, (const uint16_t*)w_kv_b, qabs,
+                    qres, rows, s) != hipSuccess)
+    return MLA_ERR_DEVICE;
+  DecodeParams p;
+  p.qabs = qabs;
+  p.cache = (const uint8_t*)cache;
+  p.stride_tokens = stride_tokens;
+  p.block_table = block_table;
+  p.max_pages = max_pages;
+  p.ctx_lens = ctx_lens;
+  p.Sq = Sq;
+  p.kv_chunk = chunk;
+  p.splits = splits;
+  p.scale_log2 = shape->softmax_scale * 1.44269504088896340736f;
+  p.part_o = part_o;
+  p.part_lse = part_lse;
+  const bool timed = g_timing.on && g_timing.used < g_timing.capacity;
+  if (timed && hipEventRecord(g_timing.ev[2 * g_timing.used], s) != hipSuccess) return MLA_ERR_DEVICE;
+  for (int j0 = 0; j0 < Sq; j0 += kMaxQueryGroup) {
+    const int qg = (Sq - j0 >= 2) ? 2 : 1;
+    p.j0 = j0;
+    if (launch_decode(p, B, qg, paged, s) != hipSuccess) return MLA_ERR_DEVICE;
+  }
+  if (timed) {
+    if (hipEventRecord(g_timing.ev[2 * g_timing.used + 1], s) != hipSuccess) return MLA_ERR_DEVICE;
+    ++g_timing.used;
+  }
+  if (launch_combine(part_o, part_lse, ctx_lens, B, Sq, splits, chunk, o_lat, lse2, s) != hipSuccess)
+    return MLA_ERR_DEVICE;
+  if (launch_upproj(o_lat, (const uint16_t*)w_kv_b, qres, lse2, p.scale_log2, (uint16_t*)out, lse, rows,
+                    s) != hipSuccess)
+    return MLA_ERR_DEVICE;
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_default_shape(mla_shape* shape) {
+  if (shape == nullptr) return MLA_ERR_NULL;
+  shape->num_heads = kHeads;
+  shape->kv_lora_rank = kLatent;
+  shape->qk_nope_head_dim = kNope;
+  shape->qk_rope_head_dim = kRope;
+  shape->v_head_dim = kVDim;
+  shape->page_size = kPage;
+  const double mscale = 0.1 * 1.0 * log(64.0) + 1.0;      // mscale_all_dim 1.0, factor 64
+  shape->softmax_scale = (float)(mscale * mscale / sqrt((double)(kNope + kRope)));
+  return MLA_OK;
+}
+
+mla_status mla_default_rope(mla_rope_params* p) {
+  if (p == nullptr) return MLA_ERR_NULL;
+  p->base = 10000.0;
+  p->factor = 64.0;
+  p->original_max_position = 4096.0;
+  p->beta_fast = 32.0;
+  p->beta_slow = 1.0;
+  p->rope_dim = kRope;
+  return MLA_OK;
+}
+
+const char* mla_status_string(mla_status s) {
+  switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_NULL: return "MLA_ERR_NULL: a required pointer is NULL";
+    case MLA_ERR_SHAPE: return "MLA_ERR_SHAPE: unsupported shape";
+    case MLA_ERR_RANGE: return "MLA_ERR_RANGE: a size is out of range";
+    case MLA_ERR_ALIGN: return "MLA_ERR_ALIGN: misaligned pointer or leading dimension";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace too small";
+    case MLA_ERR_DEVICE: return "MLA_ERR_DEVICE: a HIP runtime call failed";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: not implemented";
+    default: return "MLA_ERR_UNKNOWN";
+  }
+}
+
+mla_status mla_rope_yarn(const mla_rope_params* params, const void* src, int64_t ld_src, void* dst,
+                         int64_t ld_dst, const int32_t* positions, int64_t n, void* stream) {
+  if (params == nullptr) return MLA_ERR_NULL;
+  if (params->rope_dim != kRope || !(params->base > 1.0) || !(params->factor >= 1.0) ||
+      !(params->original_max_position > 0) || !(params->beta_fast > params->beta_slow) ||
+      !(params->beta_slow > 0))
+    return MLA_ERR_SHAPE;
+  if (n < 0 || ld_src < params->rope_dim || ld_dst < params->rope_dim) return MLA_ERR_RANGE;
+  if (n == 0) return MLA_OK;
+  if (!src || !dst || !positions) return MLA_ERR_NULL;
+  if (!aligned16(src) || !aligned16(dst) || ld_src % 8 != 0 || ld_dst % 8 != 0) return MLA_ERR_ALIGN;
+  if (n > (int64_t)1 << 40) return MLA_ERR_RANGE;
+  double inv[32];
+  yarn_frequencies(*params, inv);
+  return launch_rope((const uint16_t*)src, ld_src, (uint16_t*)dst, ld_dst, positions, n, inv,
+                     params->rope_dim, (hipStream_t)stream) == hipSuccess
+             ? MLA_OK
+             : MLA_ERR_DEVICE;
+}
+
+mla_status mla_cache_append(const mla_shape* shape, void* cache, int64_t num_slots, const void* c_kv,
+                            int64_t ld_c, const void* k_pe, int64_t ld_k, const int64_t* slot_mapping,
+                            int64_t n, void* stream) {
+  mla_status st = check_shape(shape);
+  if (st != MLA_OK) return st;
+  if (n < 0 || num_slots < 0 || ld_c < kLatent || ld_k < kRope) return MLA_ERR_RANGE;
+  if (n == 0) return MLA_OK;
+  if (!cache || !c_kv || !k_pe || !slot_mapping) return MLA_ERR_NULL;
+  if (!aligned16(cache) || !aligned16(c_kv) || !aligned16(k_pe) || ld_c % 8 != 0 || ld_k % 8 != 0 ||
+      ((uintptr_t)slot_mapping & 7u) != 0)
+    return MLA_ERR_ALIGN;
+  if (n > (int64_t)1 << 40) return MLA_ERR_RANGE;
+  return launch_append((uint8_t*)cache, num_slots, (const uint16_t*)c_kv, ld_c, (const uint16_t*)k_pe,
+                       ld_k, slot_mapping, n, (hipStream_t)stream) == hipSuccess
+             ? MLA_OK
+             : MLA_ERR_DEVICE;
+}
+
+mla_status mla_decode(const mla_shape* shape, const void* q_nope, const void* q_pe, const void* w_kv_b,
+                      const void* cache, int64_t stride_tokens, const int32_t* ctx_lens,
+                      int32_t max_ctx_len, int32_t B, int32_t Sq, int32_t kv_chunk, void* out,
+                      float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_common(shape, q_nope, q_pe, w_kv_b, cache, stride_tokens, 0, nullptr, 0, ctx_lens,
+                       max_ctx_len, B, Sq, kv_chunk, out, lse, workspace, workspace_bytes, stream, false);
+}
+
+mla_status mla_decode_paged(const mla_shape* shape, const void* q_nope, const void* q_pe,
+                            const void* w_kv_b, const void* cache, int64_t num_pages,
+                            const int32_t* block_table, int32_t max_pages_per_seq,
+                            const int32_t* ctx_lens, int32_t max_ctx_len, int32_t B, int32_t Sq,
+                            int32_t kv_chunk, void* out, float* lse, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return decode_common(shape, q_nope, q_pe, w_kv_b, cache, 0, num_pages, block_table, max_pages_per_seq,
+                       ctx_lens, max_ctx_len, B, Sq, kv_chunk, out, lse, workspace, workspace_bytes,
+                       stream, true);
+}
+
+mla_status mla_decode_workspace_size(const mla_shape* shape, int32_t B, int32_t Sq, int32_t max_ctx_len,
+                                     int32_t kv_chunk, size_t* bytes) {
+  mla_status st = check_shape(shape);
+  if (st != MLA_OK) return st;
+  if (bytes == nullptr) return MLA_ERR_NULL;
+  if (B < 0 || Sq < 1 || Sq > kMaxSq || max_ctx_len < Sq) return MLA_ERR_RANGE;
+  if (kv_chunk < 0 || kv_chunk % kPage != 0) return MLA_ERR_RANGE;
+  const int chunk = kv_chunk ? kv_chunk : auto_chunk(B, max_ctx_len);
+  *bytes = workspace_layout(B, Sq, splits_for(max_ctx_len, chunk)).total;
+  return MLA_OK;
+}
+
+mla_status mla_timing_enable(int32_t max_calls) {
+  if (max_calls < 1 || max_calls > (1 << 20)) return MLA_ERR_RANGE;
+  timing_free();
+  g_timing.ev = new hipEvent_t[2 * (size_t)max_calls];
+  for (int i = 0; i < 2 * max_calls; ++i) {
+    if (hipEventCreate(&g_timing.ev[i]) != hipSuccess) {
+      g_timing.capacity = i / 2;
+      for (int k = 2 * g_timing.capacity; k < i; ++k) (void)hipEventDestroy(g_timing.ev[k]);
+      timing_free();
+      return MLA_ERR_DEVICE;
+    }
+  }
+  g_timing.capacity = max_calls;
+  g_timing.used = 0;
+  g_timing.on = true;
+  return MLA_OK;
+}
+
+mla_status mla_timing_collect(double* total_ms, int32_t* launches) {
+  if (total_ms == nullptr || launches == nullptr) return MLA_ERR_NULL;
+  double sum = 0.0;
+  for (int i = 0; i < g_timing.used; ++i) {
+    if (hipEventSynchronize(g_timing.ev[2 * i + 1]) != hipSuccess) return MLA_ERR_DEVICE;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, g_timing.ev[2 * i], g_timing.ev[2 * i + 1]) != hipSuccess)
+      return MLA_ERR_DEVICE;
+    sum += ms;
+  }
+  *total_ms = sum;
+  *launches = g_timing.used;
+  return MLA_OK;
+}
+
+mla_status mla_timing_disable(void) {
+  timing_free();
+  return MLA_OK;
+}
+
+mla_status mla_decode_auto_chunk(int32_t B, int32_t Sq, int32_t max_ctx_len, int32_t* kv_chunk) {
+  if (kv_chunk == nullptr) return MLA_ERR_NULL;
+  if (B < 0 || Sq < 1 || Sq > kMaxSq || max_ctx_len < Sq) return MLA_ERR_RANGE;
+  *kv_chunk = auto_chunk(B, max_ctx_len);
+  return MLA_OK;
+}
+
+}  // extern "C"

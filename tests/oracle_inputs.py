@@ -1,0 +1,63 @@
+"""Oracle-side view of a workload: host-generated inputs and expected outputs.
+
+Everything here comes from ``synth`` (host generator) and ``oracle``; nothing
+is read back from the GPU.
+"""
+import numpy as np
+
+import oracle as O
+import synth
+
+
+def f(bits):
+    return O.bf16_bits_to_float(bits)
+
+
+def sequence_inputs(seed, layer, length, sq, b):
+    """(q_nope, q_pe rotated, c_kv, k_pe rotated, w) of sequence b, fp64 arrays."""
+    inv = O.yarn_inv_freq()
+    c = f(synth.latent_bits(seed, layer, b, 0, length))
+    k = O.round_to_bf16(O.rope_rotate(f(synth.kpe_bits(seed, layer, b, 0, length)), np.arange(length), inv))
+    qn = f(synth.qnope_bits(seed, layer, b, sq))
+    qpos = (length - sq + np.arange(sq))[:, None]
+    qp = O.round_to_bf16(O.rope_rotate(f(synth.qpe_bits(seed, layer, b, sq)), qpos, inv))
+    return qn, qp, c, k
+
+
+_W_CACHE = {}
+
+
+def weights(seed, layer):
+    key = (seed, layer)
+    if key not in _W_CACHE:
+        _W_CACHE.clear()
+        _W_CACHE[key] = f(synth.wkvb_bits(seed, layer))
+    return _W_CACHE[key]
+
+
+def expected(seed, layer, length, sq, b, heads=None, absorbed=False):
+    """Oracle (out [Sq, H', 128], lse [Sq, H']) for sequence b."""
+    qn, qp, c, k = sequence_inputs(seed, layer, length, sq, b)
+    fn = O.mla_attention_absorbed if absorbed else O.mla_attention_unabsorbed
+    return fn(qn, qp, c, k, weights(seed, layer), O.softmax_scale(), heads)
+
+
+# Tolerances: outputs as stated for the path (bf16 outputs, fp32 accumulation);
+# LSE bound derived from bf16 rounding of the absorbed query.
+OUT_MAX_ABS = 2e-2
+OUT_REL_L2 = 5e-3
+LSE_MAX_ABS = 5e-3
+
+
+def compare(out_gpu, lse_gpu, out_ref, lse_ref):
+    """Returns (max_abs, rel_l2, lse_max_abs); asserts the tolerances."""
+    og = np.asarray(out_gpu, dtype=np.float64)
+    d = og - out_ref
+    max_abs = float(np.abs(d).max())
+    rel = float(np.linalg.norm(d) / max(np.linalg.norm(out_ref), 1e-30))
+    lmax = float(np.abs(np.asarray(lse_gpu, dtype=np.float64) - lse_ref).max()) if lse_gpu is not None else 0.0
+    assert np.isfinite(og).all(), "non-finite GPU output"
+    assert max_abs <= OUT_MAX_ABS, f"max abs {max_abs}"
+    assert rel <= OUT_REL_L2, f"rel L2 {rel}"
+    assert lmax <= LSE_MAX_ABS, f"lse max abs {lmax}"
+    return max_abs, rel, lmax

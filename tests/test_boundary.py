@@ -1,0 +1,118 @@
+"""C-ABI boundary on the host: the library loads, exports every declared entry
+point, and rejects bad arguments before enqueuing anything (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mla_latent_kv_absorbed_amd as M
+import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_RANGE, ERR_ALIGN, ERR_WORKSPACE = 0, 1, 2, 3, 4, 5
+FAKE = 1 << 20   # an aligned non-null address; validation fails before any use
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:mla_status|const char\*)\s+(mla_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) >= 9
+    lib = ctypes.CDLL(M.build.lib_path())
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_default_shape_and_scale():
+    s = M.default_shape()
+    assert (s.num_heads, s.kv_lora_rank, s.qk_nope_head_dim, s.qk_rope_head_dim, s.v_head_dim,
+            s.page_size) == (32, 512, 128, 64, 128, 64)
+    assert s.softmax_scale == pytest.approx(O.softmax_scale(), rel=1e-7)
+    r = M.default_rope()
+    assert (r.base, r.factor, r.original_max_position, r.beta_fast, r.beta_slow, r.rope_dim) == \
+        (10000.0, 64.0, 4096.0, 32.0, 1.0, 64)
+
+
+def test_status_strings():
+    for code in range(8):
+        assert M.mla_status_string(code).startswith("MLA_")
+
+
+def _decode(lib, shape, **kw):
+    a = dict(q=FAKE, qp=FAKE, w=FAKE, cache=FAKE, stride=1024, lens=FAKE, maxctx=1024, B=1, Sq=1,
+             chunk=0, out=FAKE, lse=None, ws=FAKE, wsb=1 << 40)
+    a.update(kw)
+    return lib.mla_decode(ctypes.byref(shape), a["q"], a["qp"], a["w"], a["cache"], a["stride"], a["lens"],
+                          a["maxctx"], a["B"], a["Sq"], a["chunk"], a["out"], a["lse"], a["ws"], a["wsb"], None)
+
+
+def test_decode_argument_errors():
+    lib = M.library()
+    s = M.default_shape()
+    assert _decode(lib, s, q=None) == ERR_NULL
+    assert _decode(lib, s, ws=None) == ERR_NULL
+    assert _decode(lib, s, chunk=100) == ERR_RANGE          # not a multiple of 64
+    assert _decode(lib, s, Sq=0) == ERR_RANGE
+    assert _decode(lib, s, Sq=17) == ERR_RANGE
+    assert _decode(lib, s, maxctx=1, Sq=2) == ERR_RANGE
+    assert _decode(lib, s, stride=512) == ERR_RANGE          # stride < max_ctx_len
+    assert _decode(lib, s, q=FAKE + 2) == ERR_ALIGN
+    assert _decode(lib, s, ws=FAKE + 16) == ERR_ALIGN
+    assert _decode(lib, s, wsb=10) == ERR_WORKSPACE
+    assert _decode(lib, s, B=0, q=None) == OK                # empty batch: no-op
+    bad = M.default_shape()
+    bad.num_heads = 16
+    assert _decode(lib, bad) == ERR_SHAPE
+    bad = M.default_shape()
+    bad.softmax_scale = float("nan")
+    assert _decode(lib, bad) == ERR_RANGE
+
+
+def test_paged_argument_errors():
+    lib = M.library()
+    s = M.default_shape()
+
+    def call(**kw):
+        a = dict(bt=FAKE, maxpages=16, pages=100, maxctx=1024)
+        a.update(kw)
+        return lib.mla_decode_paged(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, a["pages"], a["bt"], a["maxpages"],
+                                    FAKE, a["maxctx"], 1, 1, 0, FAKE, None, FAKE, 1 << 40, None)
+    assert call(bt=None) == ERR_NULL
+    assert call(maxpages=15) == ERR_RANGE                    # 1024 tokens need 16 pages
+    assert call(pages=0) == ERR_RANGE
+
+
+def test_append_and_rope_argument_errors():
+    lib = M.library()
+    s = M.default_shape()
+    assert lib.mla_cache_append(ctypes.byref(s), FAKE, 10, FAKE, 512, FAKE, 64, FAKE, 0, None) == OK
+    assert lib.mla_cache_append(ctypes.byref(s), None, 10, FAKE, 512, FAKE, 64, FAKE, 1, None) == ERR_NULL
+    assert lib.mla_cache_append(ctypes.byref(s), FAKE, 10, FAKE, 500, FAKE, 64, FAKE, 1, None) == ERR_RANGE
+    assert lib.mla_cache_append(ctypes.byref(s), FAKE, 10, FAKE, 516, FAKE, 64, FAKE, 1, None) == ERR_ALIGN
+    p = M.default_rope()
+    assert lib.mla_rope_yarn(ctypes.byref(p), FAKE, 64, FAKE, 64, FAKE, 0, None) == OK
+    assert lib.mla_rope_yarn(ctypes.byref(p), None, 64, FAKE, 64, FAKE, 3, None) == ERR_NULL
+    assert lib.mla_rope_yarn(ctypes.byref(p), FAKE, 60, FAKE, 64, FAKE, 3, None) == ERR_RANGE
+    p.rope_dim = 32
+    assert lib.mla_rope_yarn(ctypes.byref(p), FAKE, 64, FAKE, 64, FAKE, 3, None) == ERR_SHAPE
+
+
+def test_workspace_size_and_auto_chunk():
+    assert M.mla_decode_auto_chunk(1, 1, 32768) % 64 == 0
+    for B, Sq, L in [(1, 1, 1024), (1, 1, 32768), (16, 1, 65536), (1, 1, 262144), (32, 2, 131072), (3, 5, 100)]:
+        chunk = M.mla_decode_auto_chunk(B, Sq, L)
+        assert chunk % 64 == 0 and chunk >= 128
+        splits = -(-L // chunk)
+        need = M.mla_decode_workspace_size(B, Sq, L)
+        assert need >= B * Sq * 32 * (576 * 2 + 512 * 4) + B * splits * Sq * 32 * 513 * 4
+    with pytest.raises(M.MlaError):
+        M.mla_decode_workspace_size(1, 1, 100, kv_chunk=65)
+    # an empty batch needs no workspace and must not trip the split heuristic
+    assert M.mla_decode_workspace_size(0, 1, 1024) == 0
+    assert M.mla_decode_auto_chunk(0, 1, 1024) % 64 == 0

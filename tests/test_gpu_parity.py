@@ -1,0 +1,218 @@
+"""GPU parity of the HIP path against the CPU oracle (small and medium sizes).
+
+Every device call goes through the C ABI via the ctypes binding.  Inputs are
+seeded: the GPU side draws them with the device generator and prepares the
+cache with its own RoPE and append kernels; the oracle draws the same values
+on the host and prepares them with its own fp64 RoPE.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+import synth.gpu as sgpu
+from synth.configs import Workload, workload
+
+import mla_latent_kv_absorbed_amd as M
+from mla_latent_kv_absorbed_amd.workload import DeviceWorkload
+
+from oracle_inputs import compare, expected
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def gpu_out(out):
+    return out.float().cpu().numpy().astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# generator twin, RoPE, append
+# ---------------------------------------------------------------------------
+
+def test_device_generator_matches_host_generator():
+    c = torch.empty((300, 512), dtype=torch.bfloat16, device=DEV)
+    sgpu.latent(c, 3, 5, 2, 1000)
+    np.testing.assert_array_equal(bits(c), synth.latent_bits(3, 5, 2, 1000, 1300))
+    q = torch.empty((2, 32, 64), dtype=torch.bfloat16, device=DEV)
+    sgpu.qpe(q, 4, 7, 9)
+    np.testing.assert_array_equal(bits(q), synth.qpe_bits(4, 7, 9, 2))
+    w = torch.empty((8192, 512), dtype=torch.bfloat16, device=DEV)
+    sgpu.wkvb(w, 1, 39)
+    np.testing.assert_array_equal(bits(w), synth.wkvb_bits(1, 39))
+
+
+def test_rope_matches_oracle_bit_exact():
+    n = 4096
+    raw = torch.empty((n, 64), dtype=torch.bfloat16, device=DEV)
+    sgpu.kpe(raw, 0, 0, 0, 0)
+    rng = np.random.default_rng(0)
+    pos = np.concatenate([[0, 1, 4095, 4096, 131071, 262143], rng.integers(0, 262144, n - 6)]).astype(np.int32)
+    dst = torch.empty_like(raw)
+    M.mla_rope_yarn(raw, torch.from_numpy(pos).to(DEV), dst=dst)
+    want = O.round_to_bf16(O.rope_rotate(O.bf16_bits_to_float(synth.kpe_bits(0, 0, 0, 0, n)), pos, O.yarn_inv_freq()))
+    got = O.bf16_bits_to_float(bits(dst))
+    mism = int((got != want).sum())
+    # fp64 on both sides, one rounding to bf16: equal unless a value lies within
+    # a few fp64 ulps of a bf16 rounding boundary
+    assert mism <= 2, f"{mism} mismatches"
+    assert np.abs(got - want).max() <= 2.0 ** -7 * np.abs(want).max()
+    # in place gives the same bits
+    M.mla_rope_yarn(raw, torch.from_numpy(pos).to(DEV))
+    np.testing.assert_array_equal(bits(raw), bits(dst))
+
+
+def test_rope_strided_rows_touch_only_the_rope_part():
+    x = torch.zeros((10, 576), dtype=torch.bfloat16, device=DEV)
+    sgpu.fill(x, 9, 2, 0, 0)
+    before = bits(x).copy()
+    view = x[:, 512:]
+    M.mla_rope_yarn(view, torch.arange(10, dtype=torch.int32, device=DEV) * 1000)
+    after = bits(x)
+    np.testing.assert_array_equal(after[:, :512], before[:, :512])
+    want = O.round_to_bf16(O.rope_rotate(O.bf16_bits_to_float(before[:, 512:]), np.arange(10) * 1000, O.yarn_inv_freq()))
+    assert int((O.bf16_bits_to_float(after[:, 512:]) != want).sum()) <= 1
+
+
+def test_cache_append_bit_exact_and_skips():
+    num_slots = 500
+    cache = torch.full((num_slots, 576), 0, dtype=torch.int16, device=DEV)
+    cache.fill_(0x7FC1)
+    cache = cache.view(torch.bfloat16)
+    n = 300
+    src = torch.randint(-32768, 32767, (n, 640), dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    c_kv = src[:, :512]            # row stride 640
+    k_pe = src[:, 576:]            # offset rows, stride 640
+    rng = np.random.default_rng(1)
+    slots = rng.permutation(num_slots)[:n].astype(np.int64)
+    slots[::7] = -1
+    M.mla_cache_append(cache, c_kv, k_pe, torch.from_numpy(slots).to(DEV))
+    got = bits(cache)
+    s_host = bits(src)
+    for i in range(n):
+        if slots[i] >= 0:
+            np.testing.assert_array_equal(got[slots[i], :512], s_host[i, :512])
+            np.testing.assert_array_equal(got[slots[i], 512:], s_host[i, 576:640])
+    untouched = np.setdiff1d(np.arange(num_slots), slots[slots >= 0])
+    assert np.all(got[untouched] == 0x7FC1)
+
+
+def test_paged_cache_rows_follow_the_block_table():
+    wl = Workload(90, "paging", 3, 1, 1, (65, 200, 1), True)
+    dw = DeviceWorkload(wl, poison=True)
+    li = dw.build_layer(0)
+    cache = bits(li.cache).reshape(-1, 576)
+    inv = O.yarn_inv_freq()
+    for b, L in enumerate(wl.lens):
+        lat = synth.latent_bits(wl.seed, 0, b, 0, L)
+        kr = O.round_to_bf16(O.rope_rotate(O.bf16_bits_to_float(synth.kpe_bits(wl.seed, 0, b, 0, L)), np.arange(L), inv))
+        slots = O.paged_slot(dw.block_table_host[b], np.arange(L))
+        np.testing.assert_array_equal(cache[slots, :512], lat)
+        assert int((O.bf16_bits_to_float(cache[slots, 512:]) != kr).sum()) <= 1
+    used = np.concatenate([O.paged_slot(dw.block_table_host[b], np.arange(L)) for b, L in enumerate(wl.lens)])
+    unused = np.setdiff1d(np.arange(cache.shape[0]), used)
+    assert len(unused) == 64 * dw.num_pages - sum(wl.lens) and np.all(cache[unused] == 0x7FC1)
+
+
+# ---------------------------------------------------------------------------
+# decode parity
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("chunk", [0, 1024, 256, 64])
+def test_config0_parity_all_heads(chunk):
+    wl = workload(0)
+    dw = DeviceWorkload(wl, kv_chunk=chunk)
+    li = dw.build_layer(0)
+    lse = torch.empty((1, 1, 32), dtype=torch.float32, device=DEV)
+    out, lse = dw.step(li, lse=lse)
+    torch.cuda.synchronize()
+    ref_o, ref_l = expected(wl.seed, 0, 1024, 1, 0)
+    stats = compare(gpu_out(out[0]), lse[0].cpu().numpy(), ref_o, ref_l)
+    print(f"config0 chunk={chunk}: max_abs={stats[0]:.3e} rel_l2={stats[1]:.3e} lse={stats[2]:.3e}")
+
+
+RAGGED = [
+    (1, (1, 2, 63, 64, 65, 700)),
+    (2, (2, 3, 64, 65, 129, 333)),
+    (3, (3, 70, 200)),
+    (5, (5, 130)),
+]
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("sq,lens", RAGGED)
+@pytest.mark.parametrize("chunk", [64, 128, 0])
+def test_ragged_batches(paged, sq, lens, chunk):
+    wl = Workload(91, "ragged", len(lens), sq, 1, lens, True)
+    dw = DeviceWorkload(wl, paged=paged, kv_chunk=chunk, poison=True)
+    li = dw.build_layer(2)
+    lse = torch.empty((len(lens), sq, 32), dtype=torch.float32, device=DEV)
+    out, lse = dw.step(li, lse=lse)
+    torch.cuda.synchronize()
+    go, gl = gpu_out(out), lse.cpu().numpy()
+    for b, L in enumerate(lens):
+        ref_o, ref_l = expected(wl.seed, 2, L, sq, b)
+        compare(go[b], gl[b], ref_o, ref_l)
+
+
+def test_paged_equals_contiguous_bitwise_and_runs_are_deterministic():
+    lens = (1000, 64, 130, 777)
+    wl = Workload(92, "same", len(lens), 2, 1, lens, True, permute_pages=True)
+    outs = []
+    for paged in (False, True):
+        dw = DeviceWorkload(wl, paged=paged, kv_chunk=128)
+        li = dw.build_layer(0)
+        lse = torch.empty((len(lens), 2, 32), dtype=torch.float32, device=DEV)
+        o1, l1 = dw.step(li, lse=lse)
+        o1, l1 = bits(o1), l1.cpu().numpy().copy()
+        o2, l2 = dw.step(li, lse=lse)
+        np.testing.assert_array_equal(bits(o2), o1)
+        np.testing.assert_array_equal(l2.cpu().numpy(), l1)
+        outs.append((o1, l1))
+    np.testing.assert_array_equal(outs[0][0], outs[1][0])
+    np.testing.assert_array_equal(outs[0][1], outs[1][1])
+
+
+def test_chunk_size_changes_only_rounding():
+    wl = Workload(93, "chunks", 2, 1, 1, (3000, 1200), False)
+    dw = DeviceWorkload(wl)
+    li = dw.build_layer(0)
+    res = []
+    for chunk in (64, 512, 4096):
+        out, _ = dw.step(li, kv_chunk=chunk)
+        res.append(gpu_out(out))
+    for r in res[1:]:
+        assert np.abs(r - res[0]).max() < 1e-2
+
+
+def test_empty_batch_is_a_no_op():
+    out = torch.full((0, 1, 32, 128), 1.0, dtype=torch.bfloat16, device=DEV)
+    z = torch.empty((0, 1, 32, 128), dtype=torch.bfloat16, device=DEV)
+    M.mla_decode(z, torch.empty((0, 1, 32, 64), dtype=torch.bfloat16, device=DEV),
+                 torch.zeros((8192, 512), dtype=torch.bfloat16, device=DEV),
+                 torch.zeros((0, 64, 576), dtype=torch.bfloat16, device=DEV),
+                 torch.zeros((0,), dtype=torch.int32, device=DEV), 64, out=out)
+    torch.cuda.synchronize()
+
+
+def test_every_query_row_gets_its_rope_part_with_a_dirty_workspace():
+    # Query rows r = 1, 2, 3 (mod 4) once kept stale workspace bytes in the
+    # rope part of the absorbed query; a NaN-filled workspace exposes that.
+    lens = (5, 9, 17, 33, 65, 100, 7)
+    wl = Workload(94, "rows", len(lens), 2, 1, lens, True)
+    dw = DeviceWorkload(wl, paged=True, kv_chunk=64)
+    dw.workspace.view(torch.int16)[: dw.workspace.numel() // 2].fill_(0x7FC1)
+    li = dw.build_layer(0)
+    lse = torch.empty((len(lens), 2, 32), dtype=torch.float32, device=DEV)
+    out, lse = dw.step(li, lse=lse)
+    torch.cuda.synchronize()
+    go, gl = gpu_out(out), lse.cpu().numpy()
+    for b, L in enumerate(lens):
+        ref_o, ref_l = expected(wl.seed, 0, L, 2, b)
+        compare(go[b], gl[b], ref_o, ref_l)
