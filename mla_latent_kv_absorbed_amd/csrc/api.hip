@@ -4,7 +4,7 @@
 #include <math.h>
 #include <string.h>
 
-#include "../../include/mla.h"
+#include "mla.h"   // include/mla.h (on the include path)
 #include "mla_internal.h"
 
 using namespace mla;
@@ -115,6 +115,7 @@ mla_status decode_common(const mla_shape* shape, const void* q_nope, const void*
   uint16_t* qabs = (uint16_t*)(ws + wl.qabs);
   float* qres = (float*)(ws + wl.qres);
   float* lse2 = (float*)(ws + wl.lse2);
+  uint8_t* zero_row = ws + wl.zero_row;
   float* part_o = (float*)(ws + wl.part_o);
   float* part_lse = (float*)(ws + wl.part_lse);
   float* o_lat = (float*)(ws + wl.o_lat);
@@ -122,7 +123,7 @@ mla_status decode_common(const mla_shape* shape, const void* q_nope, const void*
   const int rows = B * Sq;
 
   if (launch_absorb((const uint16_t*)q_nope, (const uint16_t*)q_pe, (const uint16_t*)w_kv_b, qabs,
-                    qres, rows, s) != hipSuccess)
+                    qres, zero_row, rows, s) != hipSuccess)
     return MLA_ERR_DEVICE;
   DecodeParams p;
   p.qabs = qabs;
@@ -137,6 +138,7 @@ mla_status decode_common(const mla_shape* shape, const void* q_nope, const void*
   p.scale_log2 = shape->softmax_scale * 1.44269504088896340736f;
   p.part_o = part_o;
   p.part_lse = part_lse;
+  p.zero_row = zero_row;
   const bool timed = g_timing.on && g_timing.used < g_timing.capacity;
   if (timed && hipEventRecord(g_timing.ev[2 * g_timing.used], s) != hipSuccess) return MLA_ERR_DEVICE;
   for (int j0 = 0; j0 < Sq; j0 += kMaxQueryGroup) {
@@ -263,7 +265,7 @@ mla_status mla_decode_workspace_size(const mla_shape* shape, int32_t B, int32_t 
   if (B < 0 || Sq < 1 || Sq > kMaxSq || max_ctx_len < Sq) return MLA_ERR_RANGE;
   if (kv_chunk < 0 || kv_chunk % kPage != 0) return MLA_ERR_RANGE;
   const int chunk = kv_chunk ? kv_chunk : auto_chunk(B, max_ctx_len);
-  *bytes = workspace_layout(B, Sq, splits_for(max_ctx_len, chunk)).total;
+  *bytes = (B == 0) ? 0 : workspace_layout(B, Sq, splits_for(max_ctx_len, chunk)).total;
   return MLA_OK;
 }
 

@@ -7,89 +7,94 @@
 // lse = log2 sum_t 2^(s_t log2 e)).  The cache row [c_t | k_pe_t] is what
 // kv_a_proj_with_mqa writes ("mHC+MLA+MTP 是什么", MLA section); scoring
 // against the latent directly is the W_UK absorption, and the LSE combine and
-// W_UV up-projection of the partials follow in combine.hip.
+// W_UV up-projection of the partials follow in kernels.hip.
 //
 // Work decomposition (one workgroup of 4 waves per (sequence, split)):
-//  * A 64-token tile (one page, 72 KiB) is staged in LDS by direct
-//    global->LDS loads, double buffered, so a tile streams in while the
-//    previous one is consumed.  Tile rows are swizzled at 16-byte granularity
-//    (latent chunk c of token t sits at c ^ (t & 15), rope chunk 64+k at
-//    64 + (k ^ ((t >> 1) & 7))) so that both read patterns below are free of
-//    LDS bank conflicts.
+//  * The split streams through LDS in 64-token slots (one page, 72 KiB) of a
+//    two-slot ring, filled by direct global->LDS 16-byte loads: while the
+//    waves consume one slot the next is in flight, and the first slot is
+//    requested before anything else.  Slot rows are swizzled at 16-byte
+//    granularity (latent chunk c of token t sits at c ^ (t & 15), rope chunk
+//    64+k at 64 + (k ^ ((t >> 1) & 7))) so that both read patterns below are
+//    free of LDS bank conflicts.
 //  * The 32*QG query rows (query token, head) are cut into row groups of 16.
-//    Each wave owns one row group and a share of every tile's tokens and
-//    keeps its own running max, sum and 16 x 512 fp32 accumulator: no wave
-//    waits on another inside the tile loop.  With one query token two waves
-//    share a row group (each takes 32 tokens of a tile) and merge at the end.
-//  * Scores: S^T[token][row] = C_tile . Q^T on v_mfma_f32_16x16x32_bf16, the
-//    cache tile as the A operand (ds_read_b128 of 8 latent values per lane)
-//    and the wave's 16 query rows held in registers as the B operand.
+//    Each wave owns one row group and a share of every slot's tokens and
+//    keeps its own running max, sum and 16 x 512 fp32 accumulator (AGPRs); no
+//    wave waits on another inside the loop apart from one barrier per slot.
+//    With one query token two waves share a row group (32 tokens of each slot
+//    apiece) and merge at the end.
+//  * Scores: S^T[token][row] = C_slot . Q^T on v_mfma_f32_16x16x32_bf16, the
+//    cache rows as the A operand (ds_read_b128 of 8 latent values per lane,
+//    eight reads in flight) and the wave's 16 query rows held in registers as
+//    the B operand.
 //  * The S^T accumulator layout (lane = row, 4 tokens per lane) is exactly the
-//    A-operand layout P[row][token] of the value product, with the token order
-//    (4g + e, 16 + 4g + e); the value operand C[token][col] is fetched in that
-//    token order with ds_read_b64_tr_b16 (transposing 4 x 16 blocks), so P
-//    never leaves registers.
-//  * The running max moves only when a row's tile max exceeds it by more
-//    than 8 (log2 units); until then p <= 256 and no rescale is needed.
+//    A-operand layout P[row][token] of the value product; the value operand
+//    C[token][col] is fetched in that token order with ds_read_b64_tr_b16
+//    (transposing 4 x 16 blocks), so P never leaves registers.
+//  * No rescaling inside the loop: a row's reference max is fixed at its
+//    first visible slot, and p = 2^(s - m_ref) may grow to 2^64 (sums stay far
+//    inside fp32).  Each wave also tracks the rows' true maxima; if any score
+//    ever exceeds its reference by more than 64 (log2 units), the workgroup
+//    streams the split a second time with the references set to the true
+//    maxima, where p <= 1.  The accumulators are therefore only ever
+//    accumulated by MFMAs, zeroed, or written to LDS after the loop.
 #include "mla_internal.h"
 
 namespace mla {
 namespace {
 
 constexpr float kNegInf = -__builtin_inff();
-constexpr float kTau = 8.0f;
+constexpr float kTau = 64.0f;          // log2 headroom of p above the reference max
+constexpr int kQkRing = 8;             // score operand reads in flight per wave
+constexpr int kPvRing = 6;             // value operand column blocks in flight per wave
+constexpr int kSlotTok = 64;           // tokens per ring slot (one page)
+constexpr int kSlotBytes = kSlotTok * kRowBytes;   // 73728
+constexpr int kSlots = 2;              // ring slots: kSlots - 1 in flight while one is consumed
+constexpr int kAhead = kSlots - 1;
+constexpr int kLoadsPerLane = kSlotBytes / 16 / 256;   // 18
 
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
-typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-__device__ __forceinline__ void wait_vm_18() { asm volatile("s_waitcnt vmcnt(18)" ::: "memory"); }
-__device__ __forceinline__ void wait_vm_0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most `ahead` slots' worth of direct loads (kLoadsPerLane per
+// lane per slot) are still outstanding.
+template <int PER_SLOT>
+__device__ __forceinline__ void wait_slots_ahead(int ahead) {
+  if (ahead >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * PER_SLOT) : "memory");
+  else if (ahead == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PER_SLOT) : "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
 
-// Chunk <-> slot swizzle of a tile row (an involution within each group).
+// One 16-byte direct global->LDS load: LDS byte lds + 16 * lane receives the
+// 16 bytes at this lane's gaddr (M0 holds the wave-uniform LDS address).
+// Written out so that the compiler does not order later LDS reads of other
+// slots behind it; completion is awaited explicitly with wait_slots_ahead.
+__device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds), "v"(gaddr)
+               : "memory", "m0");
+}
+
+// Chunk <-> slot-row position swizzle (an involution within each group).
 __device__ __forceinline__ int tile_slot(int tok, int c) {
   return c < 64 ? (c ^ (tok & 15)) : (64 + ((c - 64) ^ ((tok >> 1) & 7)));
 }
 
 __device__ __forceinline__ float bcast_row(float v, int src_lane) { return __shfl(v, src_lane, 64); }
 
-// Row scaling of a 16x16 accumulator block on the matrix cores:
-// returns c + diag(f) . x, where f[row] is held by the lanes with n16 == row
-// and x is in the accumulator layout (lane holds rows 4g+i, column n16).
-// Four v_mfma_f32_16x16x4f32 with A[m][k] = f[m] if m == 4k + i, else 0, and
-// B[k][n] = x[4k + i][n]; each output is one exact fp32 product plus zeros.
-// Keeping this off the vector ALU lets the accumulators live in AGPRs.
-struct RowScale {
-  float a[4];
-};
-__device__ __forceinline__ RowScale make_row_scale(float f, int g, int n16) {
-  RowScale r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r.a[i] = (n16 == 4 * g + i) ? f : 0.f;
-  return r;
-}
-__device__ __forceinline__ f32x4 scale_rows(const RowScale& r, f32x4 x, f32x4 c) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) c = __builtin_amdgcn_mfma_f32_16x16x4f32(r.a[i], x[i], c, 0, 0, 0);
-  return c;
-}
-
 template <int QG, bool PAGED>
 __global__ void __launch_bounds__(256, 1) splitkv_decode(DecodeParams p) {
-  constexpr int RG = 2 * QG;        // row groups of 16 rows
-  constexpr int TP = 4 / RG;        // waves per row group
-  constexpr int TOKW = 64 / TP;     // tokens of each tile one wave scores
-  constexpr int NBLK = TOKW / 16;   // 16-token score blocks per tile
-  constexpr int NKV = TOKW / 32;    // 32-token k-steps of the value product
+  constexpr int RG = 2 * QG;          // row groups of 16 rows
+  constexpr int TP = 4 / RG;          // waves per row group
+  constexpr int TOKW = kSlotTok / TP; // tokens of each slot one wave handles
+  constexpr int NBLK = TOKW / 16;     // 16-token score blocks per slot
 
-  // Two tile buffers as separate objects so that reads of one are known not
-  // to alias the direct-to-LDS loads in flight into the other.
-  __shared__ __attribute__((aligned(1024))) uint8_t tile_a[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t tile_b[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kSlots * kSlotBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -111,6 +116,53 @@ __global__ void __launch_bounds__(256, 1) splitkv_decode(DecodeParams p) {
   float* out_o = p.part_o + ((size_t)unit * (2 * p.Sq) + rg_glob) * (32 * 64 * 4);
   float* out_lse = p.part_lse + (size_t)unit * (p.Sq * 32) + rg_glob * 16;
 
+  // Byte offset inside a slot of each 16-byte chunk this lane loads: LDS
+  // position P = (wave*kLoadsPerLane + i)*64 + lane holds chunk (tok = P / 72,
+  // tile_slot(tok, P % 72)) of the slot's token tok.
+  int off[kLoadsPerLane];
+#pragma unroll
+  for (int i = 0; i < kLoadsPerLane; ++i) {
+    const int P = (wave * kLoadsPerLane + i) * 64 + lane;
+    const int tok = P / kChunksPerRow;
+    const int c = tile_slot(tok, P - tok * kChunksPerRow);
+    off[i] = tok * kRowBytes + c * 16;
+  }
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)ring);
+
+  const int s0 = t_begin / kSlotTok;                    // first slot index of the split
+  const int nslot = (t_end - t_begin + kSlotTok - 1) / kSlotTok;
+
+  // Enqueue the split's slot `ts` (absolute slot index) into ring slot
+  // `r`.  Every lane issues exactly kLoadsPerLane loads; rows past the end of
+  // the split come from the zero row, so masked tokens multiply zeros.
+  auto issue = [&](int ts, int r) {
+    const uint8_t* src;
+    if constexpr (PAGED) {
+      constexpr int kSlotsPerPage = kPage / kSlotTok;
+      const int page = p.block_table[(size_t)b * p.max_pages + ts / kSlotsPerPage];
+      src = p.cache + (size_t)page * kTileBytes + (ts % kSlotsPerPage) * kSlotBytes;
+    } else {
+      src = p.cache + ((size_t)b * p.stride_tokens + (size_t)ts * kSlotTok) * kRowBytes;
+    }
+    const int nval = min(kSlotTok, t_end - ts * kSlotTok);
+    const uint32_t dst = ring_lds + r * kSlotBytes + wave * kLoadsPerLane * 1024;
+    if (nval == kSlotTok) {
+#pragma unroll
+      for (int i = 0; i < kLoadsPerLane; ++i) dma16(src + off[i], dst + i * 1024);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kLoadsPerLane; ++i) {
+        const int tok = off[i] / kRowBytes;
+        const uint8_t* a = (tok < nval) ? src + off[i] : p.zero_row + (off[i] - tok * kRowBytes);
+        dma16(a, dst + i * 1024);
+      }
+    }
+  };
+
+  // The first slots are requested before the query rows are read.
+  const int pro = min(kAhead, nslot);
+  for (int k = 0; k < pro; ++k) issue(s0 + k, k);
+
   // The wave's 16 query rows, as MFMA B operands: lane holds row n16, 8 dims.
   bf16x8 q[18];
   {
@@ -119,20 +171,9 @@ __global__ void __launch_bounds__(256, 1) splitkv_decode(DecodeParams p) {
     for (int ks = 0; ks < 18; ++ks) q[ks] = *(const bf16x8*)(qrow + ks * 32);
   }
 
-  // Byte offset inside a tile of each 16-byte chunk this lane loads: LDS slot
-  // P = (wave*18 + i)*64 + lane holds chunk (tok = P / 72, tile_slot(tok, P % 72)).
-  int off[18];
-#pragma unroll
-  for (int i = 0; i < 18; ++i) {
-    const int P = (wave * 18 + i) * 64 + lane;
-    const int tok = P / kChunksPerRow;
-    const int c = tile_slot(tok, P - tok * kChunksPerRow);
-    off[i] = tok * kRowBytes + c * 16;
-  }
-
-  // LDS read offsets.  Score reads: token tok_w + 16*blk + n16, chunk
-  // 4*ks + g, slot (4ks + g) ^ n16 = 16*(ks/4) + ((4*(ks%4)) ^ (g ^ n16)); the
-  // 16*(ks/4) and 16*blk parts become instruction immediates.
+  // LDS read offsets within a slot.  Score reads: token tok_w + 16*blk + n16,
+  // chunk 4*ks + g, position (4ks + g) ^ n16 = 16*(ks/4) + ((4*(ks%4)) ^ (g ^ n16));
+  // the 16*(ks/4) and 16*blk parts become instruction immediates.
   const int tok_w = tp * TOKW;
   const int qk_row = (tok_w + n16) * kRowBytes;
   int qk_off[4];
@@ -141,9 +182,9 @@ __global__ void __launch_bounds__(256, 1) splitkv_decode(DecodeParams p) {
   int rope_off[2];
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) rope_off[kk] = qk_row + ((64 + ((4 * kk + g) ^ (n16 >> 1))) << 4);
-  // Value reads (transposed, 8 bytes): token tok_w + 32*kk + 4g + (n16 >> 2)
-  // (+16 for the upper half), columns 16*cb + 4*(n16 & 3); the chunk
-  // 2cb + ((n16 >> 1) & 1) sits at slot 16*(cb/8) + ((2*(cb%8)) ^ v).
+  // Value reads (transposed, 8 bytes): token tok_w + 4g + (n16 >> 2) (+16 for
+  // the upper half of a 32-token step), columns 16*cb + 4*(n16 & 3); chunk
+  // 2cb + ((n16 >> 1) & 1) sits at position 16*(cb/8) + ((2*(cb%8)) ^ v).
   const int pv_tok = tok_w + 4 * g + (n16 >> 2);
   const int pv_v = ((n16 >> 1) & 1) ^ (pv_tok & 15);
   const int pv_row = pv_tok * kRowBytes + (n16 & 1) * 8;
@@ -151,68 +192,43 @@ __global__ void __launch_bounds__(256, 1) splitkv_decode(DecodeParams p) {
 #pragma unroll
   for (int bb = 0; bb < 8; ++bb) pv_off[bb] = pv_row + (((2 * bb) ^ pv_v) << 4);
 
-  const int tile0 = t_begin >> 6;
-  const int ntiles = (t_end - t_begin + 63) >> 6;
-
-  auto tile_src = [&](int tile) -> const uint8_t* {
-    if constexpr (PAGED) {
-      const int page = p.block_table[(size_t)b * p.max_pages + tile];
-      return p.cache + (size_t)page * kTileBytes;
-    } else {
-      return p.cache + ((size_t)b * p.stride_tokens + (size_t)tile * kPage) * kRowBytes;
-    }
-  };
-
-  // Enqueue tile `tile` into `buf`; returns whether it was a full tile.
-  auto issue_tile = [&](int tile, uint8_t* buf) -> bool {
-    const uint8_t* src = tile_src(tile);
-    const int nval = min(kPage, t_end - tile * kPage);
-    uint8_t* dst = buf + wave * 18 * 1024;
-    if (nval == kPage) {
-#pragma unroll
-      for (int i = 0; i < 18; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(src + off[i]), (lds_void_t*)(dst + i * 1024), 16, 0, 0);
-      return true;
-    }
-    // Ragged last tile: rows past the end are never read from memory; their
-    // LDS slots get zeros so that masked tokens multiply zeros, not garbage.
-#pragma unroll
-    for (int i = 0; i < 18; ++i) {
-      if (off[i] / kRowBytes < nval)
-        __builtin_amdgcn_global_load_lds((const void*)(src + off[i]), (lds_void_t*)(dst + i * 1024), 16, 0, 0);
-      else
-        *(int4*)(dst + i * 1024 + lane * 16) = make_int4(0, 0, 0, 0);
-    }
-    return false;
-  };
-
   f32x4 o[32];
 #pragma unroll
   for (int cb = 0; cb < 32; ++cb) o[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_ref = kNegInf;   // reference max of row n16 (log2 units)
+  float m_ref = kNegInf;   // reference max of row n16 (log2 units), fixed once set
+  float m_true = kNegInf;  // running true max of row n16
   float l_part = 0.f;      // this lane's share of the row sum
+  bool overflow = false;   // some score exceeded m_ref + kTau (wave-uniform)
 
-  auto process = [&](const uint8_t* T, int tile) {
-    const int abs_w = tile * kPage + tok_w;   // absolute position of the wave's first token
+  auto process = [&](const uint8_t* T, int ts) __attribute__((always_inline)) {
+    const int abs_w = ts * kSlotTok + tok_w;   // absolute position of the wave's first token
 
-    // ---- scores S^T = C . Q^T, 16 tokens per block
+    // ---- scores S^T = C . Q^T, 16 tokens per block; reads run kQkRing ahead
+    constexpr int NQK = NBLK * 18;
+    auto qk_src = [&](int i) -> const bf16x8* {
+      const int blk = i % NBLK, ks = i / NBLK;
+      const uint8_t* base = T + blk * 16 * kRowBytes;
+      return (const bf16x8*)(ks < 16 ? base + qk_off[ks & 3] + (ks >> 2) * 256 : base + rope_off[ks - 16]);
+    };
     f32x4 s[NBLK];
 #pragma unroll
-    for (int blk = 0; blk < NBLK; ++blk) {
-      const uint8_t* base = T + blk * 16 * kRowBytes;
-      // all 18 operand reads of the block are issued before the MFMA chain
-      bf16x8 a[18];
+    for (int blk = 0; blk < NBLK; ++blk) s[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 rq[kQkRing];
 #pragma unroll
-      for (int ks = 0; ks < 16; ++ks) a[ks] = *(const bf16x8*)(base + qk_off[ks & 3] + (ks >> 2) * 256);
+    for (int i = 0; i < kQkRing; ++i) rq[i] = *qk_src(i);
+    __builtin_amdgcn_sched_group_barrier(0x100, kQkRing, 0);
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) a[16 + kk] = *(const bf16x8*)(base + rope_off[kk]);
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 18; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], q[ks], acc, 0, 0, 0);
-      s[blk] = acc;
+    for (int i = 0; i < NQK; ++i) {
+      const int blk = i % NBLK, ks = i / NBLK;
+      s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rq[i % kQkRing], q[ks], s[blk], 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i + kQkRing < NQK) {
+        rq[i % kQkRing] = *qk_src(i + kQkRing);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
     }
 
-    // ---- scale, mask, tile max of row n16
+    // ---- scale, mask, slot max of row n16
     float mt = kNegInf;
 #pragma unroll
     for (int blk = 0; blk < NBLK; ++blk)
@@ -226,105 +242,153 @@ __global__ void __launch_bounds__(256, 1) splitkv_decode(DecodeParams p) {
     mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
 
-    // ---- move the reference max only when a row outgrows it by kTau
-    const bool grow = mt > m_ref + kTau;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - mt) : 1.f;
-      m_ref = grow ? mt : m_ref;
-      l_part *= alpha;
-      const RowScale rs = make_row_scale(alpha, g, n16);
-#pragma unroll
-      for (int cb = 0; cb < 32; ++cb) o[cb] = scale_rows(rs, o[cb], f32x4{0.f, 0.f, 0.f, 0.f});
-    }
+    // ---- reference max: set at the row's first visible slot (its
+    // accumulator is still zero then), never moved afterwards
+    m_true = fmaxf(m_true, mt);
+    m_ref = (m_ref == kNegInf) ? mt : m_ref;
+    overflow = overflow || (__builtin_amdgcn_ballot_w64(mt > m_ref + kTau) != 0);
 
-    // ---- P = 2^(s - m_ref) in bf16, as the A operand of the value product
+    // ---- P = 2^(s - m_ref) in bf16, in the A-operand layout of P . C
     const float mref = (m_ref == kNegInf) ? 0.f : m_ref;
-    bf16x8 pa[NKV];
+    __bf16 pe[NBLK][4];
 #pragma unroll
-    for (int kk = 0; kk < NKV; ++kk)
+    for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
-      for (int half = 0; half < 2; ++half)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const __bf16 e = (__bf16)__builtin_amdgcn_exp2f(s[2 * kk + half][i] - mref);
-          l_part += (float)e;
-          pa[kk][half * 4 + i] = e;
-        }
+      for (int i = 0; i < 4; ++i) {
+        pe[blk][i] = (__bf16)__builtin_amdgcn_exp2f(s[blk][i] - mref);
+        l_part += (float)pe[blk][i];
+      }
 
-    // ---- O += P . C[:, 0:512]; B operand by transposed LDS reads
+    // ---- O += P . C[:, 0:512]; value operand by transposed LDS reads
+    auto pv_src = [&](int cb) -> const uint8_t* { return T + pv_off[cb & 7] + (cb >> 3) * 256; };
+    if constexpr (NBLK == 1) {
+      // 16 tokens: v_mfma_f32_16x16x16_bf16, one 4-token transposed read per block
+      s16x4 pa;
 #pragma unroll
-    for (int kk = 0; kk < NKV; ++kk) {
-      const uint8_t* base = T + kk * 32 * kRowBytes;
+      for (int i = 0; i < 4; ++i) pa[i] = __builtin_bit_cast(short, pe[0][i]);
+      s16x4 rv[kPvRing];
+#pragma unroll
+      for (int i = 0; i < kPvRing; ++i) rv[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)pv_src(i));
+      __builtin_amdgcn_sched_group_barrier(0x100, kPvRing, 1);
 #pragma unroll
       for (int cb = 0; cb < 32; ++cb) {
-        const uint8_t* a = base + pv_off[cb & 7] + (cb >> 3) * 256;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(a));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(a + 16 * kRowBytes));
-        const s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, rv[cb % kPvRing], o[cb], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        if (cb + kPvRing < 32) {
+          rv[cb % kPvRing] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)pv_src(cb + kPvRing));
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+        }
+      }
+    } else {
+      // 32-token k-steps: v_mfma_f32_16x16x32_bf16, two transposed reads per
+      // block (tokens 4g+e and 16+4g+e, the order of the score accumulator)
+      constexpr int NKV = NBLK / 2;
+      constexpr int NPV = NKV * 32;
+      bf16x8 pa[NKV];
+#pragma unroll
+      for (int kk = 0; kk < NKV; ++kk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { pa[kk][i] = pe[2 * kk][i]; pa[kk][4 + i] = pe[2 * kk + 1][i]; }
+      auto pv_at = [&](int i) -> const uint8_t* { return pv_src(i % 32) + (i / 32) * 32 * kRowBytes; };
+      s16x4 lo[kPvRing], hi[kPvRing];
+#pragma unroll
+      for (int i = 0; i < kPvRing; ++i) {
+        lo[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)pv_at(i));
+        hi[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(pv_at(i) + 16 * kRowBytes));
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPvRing, 1);
+#pragma unroll
+      for (int i = 0; i < NPV; ++i) {
+        const int kk = i / 32, cb = i % 32, r = i % kPvRing;
+        const s16x8 both = __builtin_shufflevector(lo[r], hi[r], 0, 1, 2, 3, 4, 5, 6, 7);
         o[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[kk], __builtin_bit_cast(bf16x8, both), o[cb], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        if (i + kPvRing < NPV) {
+          lo[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)pv_at(i + kPvRing));
+          hi[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(pv_at(i + kPvRing) + 16 * kRowBytes));
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+        }
       }
     }
   };
 
-  // Double-buffered tile loop, unrolled by two so each buffer is named statically.
-  bool full = issue_tile(tile0, tile_a);
-  (void)full;
-  for (int it = 0; it < ntiles; it += 2) {
-    bool next_full = false;
-    if (it + 1 < ntiles) next_full = issue_tile(tile0 + it + 1, tile_b);
-    if (next_full) wait_vm_18(); else wait_vm_0();
+  // Slot loop.  Iteration it: wait for slot it (its loads and everyone
+  // else's, via the barrier, which also frees the slot consumed at it - 1),
+  // request slot it + kAhead into that freed ring position, consume slot it.
+  // A second pass runs only if some row outgrew its reference by kTau.
+  int pass = 0;
+  for (;;) {
+    for (int it = 0; it < nslot; ++it) {
+      wait_slots_ahead<kLoadsPerLane>(min(nslot, it + kAhead) - (it + 1));
+      lds_barrier();
+      if (it + kAhead < nslot) issue(s0 + it + kAhead, (it + kAhead) % kSlots);
+      process(ring + (it % kSlots) * kSlotBytes, s0 + it);
+    }
+    lds_barrier();   // every wave is done with the last slot
+    int* flag = (int*)ring;
+    if (lane == 0) flag[wave] = overflow ? 1 : 0;
     lds_barrier();
-    process(tile_a, tile0 + it);
+    const bool again = (flag[0] | flag[1] | flag[2] | flag[3]) != 0;
     lds_barrier();
-    if (it + 1 >= ntiles) break;
-    next_full = false;
-    if (it + 2 < ntiles) next_full = issue_tile(tile0 + it + 2, tile_a);
-    if (next_full) wait_vm_18(); else wait_vm_0();
-    lds_barrier();
-    process(tile_b, tile0 + it + 1);
-    lds_barrier();
+    if (!again || pass == 1) break;
+    pass = 1;
+    m_ref = m_true;
+    overflow = false;
+    l_part = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < 32; ++cb) o[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < pro; ++k) issue(s0 + k, k);
   }
 
-  // ---- finalize: row sums, merge the two token halves, normalise, write
+  // ---- finalize.  The accumulators go to LDS straight from AGPRs; each
+  // wave then reads them back four values at a time, merges the two token
+  // halves of its row group (one query token) and normalises.  Keeping every
+  // use of the accumulators out of the vector ALU lets them stay in AGPRs.
   float l_row = l_part;
   l_row += __shfl_xor(l_row, 16, 64);
   l_row += __shfl_xor(l_row, 32, 64);
 
-  if constexpr (TP == 2) {
-    float* xo = (float*)tile_a + rg * (32 * 64 * 4 + 32);
-    float* xm = xo + 32 * 64 * 4;
-    float* xl = xm + 16;
-    if (tp == 1) {
+  constexpr int kRegion = 32 * 64 * 4 + 32;   // floats: accumulators + m + l
+  float* mine = (float*)ring + wave * kRegion;
 #pragma unroll
-      for (int cb = 0; cb < 32; ++cb) *(f32x4*)(xo + (cb * 64 + lane) * 4) = o[cb];
-      if (lane < 16) { xm[lane] = m_ref; xl[lane] = l_row; }
-    }
-    lds_barrier();
-    if (tp == 1) return;
-    const float m1 = xm[n16], l1 = xl[n16];
-    const float mm = fmaxf(m_ref, m1);
-    const float a0 = (m_ref == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_ref - mm);
-    const float a1 = (m1 == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
-    l_row = l_row * a0 + l1 * a1;
-    m_ref = mm;
-    // o = diag(a0/l) o + diag(a1/l) o1, normalised in the same step
-    const float inv = (l_row > 0.f) ? 1.f / l_row : 0.f;
-    const RowScale r0 = make_row_scale(a0 * inv, g, n16);
-    const RowScale r1 = make_row_scale(a1 * inv, g, n16);
-#pragma unroll
-    for (int cb = 0; cb < 32; ++cb) {
-      const f32x4 o1 = *(const f32x4*)(xo + (cb * 64 + lane) * 4);
-      o[cb] = scale_rows(r1, o1, scale_rows(r0, o[cb], f32x4{0.f, 0.f, 0.f, 0.f}));
-    }
-  } else {
-    const float inv = (l_row > 0.f) ? 1.f / l_row : 0.f;
-    const RowScale r0 = make_row_scale(inv, g, n16);
-#pragma unroll
-    for (int cb = 0; cb < 32; ++cb) o[cb] = scale_rows(r0, o[cb], f32x4{0.f, 0.f, 0.f, 0.f});
+  for (int cb = 0; cb < 32; ++cb) *(f32x4*)(mine + (cb * 64 + lane) * 4) = o[cb];
+  if (lane < 16) {
+    mine[32 * 64 * 4 + lane] = m_ref;
+    mine[32 * 64 * 4 + 16 + lane] = l_row;
   }
+  lds_barrier();
 
+  float a_own = 1.f, a_other = 0.f;
+  const float* other = nullptr;
+  if constexpr (TP == 2) {
+    if (tp == 1) return;
+    other = (const float*)ring + (wave + RG) * kRegion;   // the wave sharing these rows
+    const float m1 = other[32 * 64 * 4 + n16], l1 = other[32 * 64 * 4 + 16 + n16];
+    const float mm = fmaxf(m_ref, m1);
+    a_own = (m_ref == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_ref - mm);
+    a_other = (m1 == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
+    l_row = l_row * a_own + l1 * a_other;
+    m_ref = mm;
+  }
+  const float inv = (l_row > 0.f) ? 1.f / l_row : 0.f;
+  float s_own[4], s_other[4];
 #pragma unroll
-  for (int cb = 0; cb < 32; ++cb) *(f32x4*)(out_o + (cb * 64 + lane) * 4) = o[cb];
+  for (int i = 0; i < 4; ++i) {
+    s_own[i] = bcast_row(a_own * inv, 4 * g + i);
+    s_other[i] = bcast_row(a_other * inv, 4 * g + i);
+  }
+#pragma unroll
+  for (int cb = 0; cb < 32; ++cb) {
+    f32x4 v = *(const f32x4*)(mine + (cb * 64 + lane) * 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] *= s_own[i];
+    if constexpr (TP == 2) {
+      const f32x4 w = *(const f32x4*)(other + (cb * 64 + lane) * 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = fmaf(w[i], s_other[i], v[i]);
+    }
+    *(f32x4*)(out_o + (cb * 64 + lane) * 4) = v;
+  }
   if (lane < 16) out_lse[lane] = (l_row > 0.f) ? m_ref + __log2f(l_row) : kNegInf;
 }
 

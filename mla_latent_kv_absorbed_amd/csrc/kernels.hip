@@ -46,9 +46,12 @@ __global__ void __launch_bounds__(256) absorb_query(const uint16_t* __restrict__
                                                      const uint16_t* __restrict__ q_pe,
                                                      const uint16_t* __restrict__ w_kv_b,
                                                      uint16_t* __restrict__ qabs,
-                                                     float* __restrict__ qres, int rows_bs) {
+                                                     float* __restrict__ qres,
+                                                     uint8_t* __restrict__ zero_row, int rows_bs) {
   const int cblk = blockIdx.x;          // 8 blocks of 64 latent columns
   const int h = blockIdx.y;
+  if (cblk == 0 && h == 0 && threadIdx.x < kChunksPerRow)   // the decode kernel's zero row
+    ((uint4*)zero_row)[threadIdx.x] = make_uint4(0, 0, 0, 0);
   const int col = cblk * 64 + (threadIdx.x & 63);
   const int rsub = threadIdx.x >> 6;    // 4 query-row lanes
   float w[kNope];
@@ -282,9 +285,9 @@ __global__ void __launch_bounds__(256) cache_append(uint8_t* __restrict__ cache,
 }  // namespace
 
 hipError_t launch_absorb(const uint16_t* q_nope, const uint16_t* q_pe, const uint16_t* w_kv_b,
-                         uint16_t* qabs, float* qres, int rows, hipStream_t stream) {
+                         uint16_t* qabs, float* qres, uint8_t* zero_row, int rows, hipStream_t stream) {
   hipLaunchKernelGGL(absorb_query, dim3(kLatent / 64, kHeads), dim3(256), 0, stream, q_nope, q_pe,
-                     w_kv_b, qabs, qres, rows);
+                     w_kv_b, qabs, qres, zero_row, rows);
   return hipGetLastError();
 }
 

@@ -35,6 +35,7 @@ struct WorkspaceLayout {
   size_t part_lse;  // fp32 [B][splits][Sq*32], log2 domain
   size_t o_lat;     // fp32 [B][Sq][32][512]
   size_t lse2;      // fp32 [B][Sq][32], combined LSE in log2 units before correction
+  size_t zero_row;  // 1152 zero bytes: stand-in source for cache rows past a split's end
   size_t total;
 };
 
@@ -49,6 +50,7 @@ inline WorkspaceLayout workspace_layout(int B, int Sq, int splits) {
   w.part_lse = off; off = align256(off + size_t(B) * splits * Sq * kHeads * 4);
   w.o_lat = off;    off = align256(off + size_t(B) * Sq * kHeads * kLatent * 4);
   w.lse2 = off;     off = align256(off + size_t(B) * Sq * kHeads * 4);
+  w.zero_row = off; off = align256(off + kRowBytes);
   w.total = off;
   return w;
 }
@@ -67,12 +69,13 @@ struct DecodeParams {
   float scale_log2;             // softmax_scale * log2(e)
   float* part_o;
   float* part_lse;
+  const uint8_t* zero_row;      // kRowBytes zero bytes
 };
 
 // Launchers (each enqueues on `stream`; return hipError_t of the launch).
 hipError_t launch_decode(const DecodeParams& p, int B, int query_group, bool paged, hipStream_t stream);
 hipError_t launch_absorb(const uint16_t* q_nope, const uint16_t* q_pe, const uint16_t* w_kv_b,
-                         uint16_t* qabs, float* qres, int rows, hipStream_t stream);
+                         uint16_t* qabs, float* qres, uint8_t* zero_row, int rows, hipStream_t stream);
 hipError_t launch_combine(const float* part_o, const float* part_lse, const int32_t* ctx_lens,
                           int B, int Sq, int splits, int kv_chunk, float* o_lat, float* lse2,
                           hipStream_t stream);

@@ -216,3 +216,26 @@ def test_every_query_row_gets_its_rope_part_with_a_dirty_workspace():
     for b, L in enumerate(lens):
         ref_o, ref_l = expected(wl.seed, 0, L, 2, b)
         compare(go[b], gl[b], ref_o, ref_l)
+
+
+@pytest.mark.parametrize("sq", [1, 2])
+def test_score_jump_beyond_headroom_takes_the_second_pass(sq):
+    # Token 700's rope key is set to 256 in every dimension: for heads whose
+    # q_pe sums positive its score is hundreds of log2 units above the first
+    # tile's maximum, beyond the kernel's headroom, so the split is streamed a
+    # second time with the true maxima as references.
+    import oracle as O
+    from oracle_inputs import sequence_inputs, weights
+    L = 1500
+    wl = Workload(95, "jump", 1, sq, 1, (L,), False, kv_chunk=1024)
+    dw = DeviceWorkload(wl, kv_chunk=1024)
+    li = dw.build_layer(0)
+    li.cache[0, 700, 512:] = 256.0
+    lse = torch.empty((1, sq, 32), dtype=torch.float32, device=DEV)
+    out, lse = dw.step(li, lse=lse)
+    torch.cuda.synchronize()
+    qn, qp, c, k = sequence_inputs(wl.seed, 0, L, sq, 0)
+    k[700] = 256.0
+    ref_o, ref_l = O.mla_attention_unabsorbed(qn, qp, c, k, weights(wl.seed, 0), O.softmax_scale())
+    assert (ref_l.max() - np.median(ref_l)) * 1.4427 > 64     # the jump really exceeds the headroom
+    compare(gpu_out(out[0]), lse[0].cpu().numpy(), ref_o, ref_l)
