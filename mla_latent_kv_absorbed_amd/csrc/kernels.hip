@@ -7,6 +7,8 @@
 // (rope_scaling fields, attention_bias false).
 #include "mla_internal.h"
 
+#include <algorithm>
+
 namespace mla {
 namespace {
 
@@ -38,144 +40,187 @@ __device__ __forceinline__ uint16_t f64_to_bf16(double d) {
 // Q_abs[r][512:576] = q_pe[r], for rows r = (b, j, h).  The fp32 residual
 // q_lat - bf16(q_lat) is kept for the first-order LSE correction in the
 // up-projection kernel.
-// W_UK[h] = w_kv_b rows [h*256, h*256 + 128).  One workgroup per (head,
-// 64-column block) keeps its 128 x 64 slice of W_UK in registers (each
-// thread one column) and sweeps every query row of that head.
+// W_UK[h] = w_kv_b rows [h*256, h*256 + 128).  A workgroup covers (head,
+// 64-column block, 4 query rows): thread (ng, c8) loads the 4 x 8 weights
+// W_UK[h][4ng .. 4ng+3][c8*8 .. c8*8+7] as four 16-byte loads, forms the
+// partial dot products of its 4 rows over those 4 nope dims, and the 32
+// partials of each output are summed through LDS in a fixed order.
 // ---------------------------------------------------------------------------
+constexpr int kAbsorbRows = 4;
+
 __global__ void __launch_bounds__(256) absorb_query(const uint16_t* __restrict__ q_nope,
                                                      const uint16_t* __restrict__ q_pe,
                                                      const uint16_t* __restrict__ w_kv_b,
                                                      uint16_t* __restrict__ qabs,
                                                      float* __restrict__ qres,
                                                      uint8_t* __restrict__ zero_row, int rows_bs) {
+  __shared__ float red[kAbsorbRows][32][64];
   const int cblk = blockIdx.x;          // 8 blocks of 64 latent columns
   const int h = blockIdx.y;
-  if (cblk == 0 && h == 0 && threadIdx.x < kChunksPerRow)   // the decode kernel's zero row
-    ((uint4*)zero_row)[threadIdx.x] = make_uint4(0, 0, 0, 0);
-  const int col = cblk * 64 + (threadIdx.x & 63);
-  const int rsub = threadIdx.x >> 6;    // 4 query-row lanes
-  float w[kNope];
-  const uint16_t* wk = w_kv_b + (size_t)h * kWRowsPerHead * kLatent + col;
+  const int r0 = blockIdx.z * kAbsorbRows;
+  const int t = threadIdx.x;
+  if (cblk == 0 && h == 0 && r0 == 0 && t < kChunksPerRow)   // the decode kernel's zero row
+    ((uint4*)zero_row)[t] = make_uint4(0, 0, 0, 0);
+  const int c8 = t & 7, ng = t >> 3;
+  const uint16_t* wk = w_kv_b + ((size_t)h * kWRowsPerHead + 4 * ng) * kLatent + cblk * 64 + c8 * 8;
+  uint4 w[4];
 #pragma unroll
-  for (int n = 0; n < kNope; ++n) w[n] = bf16_to_f32(wk[(size_t)n * kLatent]);
-
-  for (int r = rsub; r < rows_bs; r += 4) {
-    const uint16_t* qn = q_nope + ((size_t)r * kHeads + h) * kNope;
-    float acc = 0.f;
+  for (int k = 0; k < 4; ++k) w[k] = *(const uint4*)(wk + (size_t)k * kLatent);
+  uint2 q[kAbsorbRows];
 #pragma unroll
-    for (int n8 = 0; n8 < kNope; n8 += 8) {
-      const uint4 v = *(const uint4*)(qn + n8);   // same address across the wave: one fetch
-      const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+  for (int rr = 0; rr < kAbsorbRows; ++rr) {
+    const int r = min(r0 + rr, rows_bs - 1);
+    q[rr] = *(const uint2*)(q_nope + ((size_t)r * kHeads + h) * kNope + 4 * ng);
+  }
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        acc = fmaf(__uint_as_float(wd[k] << 16), w[n8 + 2 * k], acc);
-        acc = fmaf(__uint_as_float(wd[k] & 0xFFFF0000u), w[n8 + 2 * k + 1], acc);
+  for (int rr = 0; rr < kAbsorbRows; ++rr) {
+    const float qv[4] = {__uint_as_float(q[rr].x << 16), __uint_as_float(q[rr].x & 0xFFFF0000u),
+                         __uint_as_float(q[rr].y << 16), __uint_as_float(q[rr].y & 0xFFFF0000u)};
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t wd[4] = {w[k].x, w[k].y, w[k].z, w[k].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] = fmaf(qv[k], __uint_as_float(wd[e] << 16), acc[2 * e]);
+        acc[2 * e + 1] = fmaf(qv[k], __uint_as_float(wd[e] & 0xFFFF0000u), acc[2 * e + 1]);
       }
     }
-    uint16_t* dst = qabs + ((size_t)r * kHeads + h) * kRow;
-    const uint16_t qb = f32_to_bf16(acc);
-    dst[col] = qb;
-    qres[((size_t)r * kHeads + h) * kLatent + col] = acc - bf16_to_f32(qb);
-    if (cblk == 0) {   // the 64 threads of this row's lane group copy its rope part
-      const int e = threadIdx.x & 63;
-      dst[kLatent + e] = q_pe[((size_t)r * kHeads + h) * kRope + e];
-    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[rr][ng][c8 * 8 + e] = acc[e];
   }
+  __syncthreads();
+  const int rr = t >> 6, col = t & 63;
+  const int r = r0 + rr;
+  if (r >= rows_bs) return;
+  float acc = 0.f;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) acc += red[rr][k][col];
+  const size_t row = (size_t)r * kHeads + h;
+  uint16_t* dst = qabs + row * kRow;
+  const uint16_t qb = f32_to_bf16(acc);
+  dst[cblk * 64 + col] = qb;
+  qres[row * kLatent + cblk * 64 + col] = acc - bf16_to_f32(qb);
+  if (cblk == 0) dst[kLatent + col] = q_pe[row * kRope + col];   // the rope part, copied
 }
 
 // ---------------------------------------------------------------------------
 // LSE combine of the split partials.  One workgroup per (sequence b, row
-// group of 16 rows, 16-column block); each of its 4 waves sums a quarter of
-// the splits, in the partials' own layout (lane holds rows 4g..4g+3 of
-// column n16), and the quarters are added in a fixed order.
+// group of 16 rows, 16-column block); its waves take every W-th split
+// (W = waves in the workgroup), reading the partials in their own layout
+// (lane holds rows 4g..4g+3 of column n16) eight splits at a time, and keep
+// a running max per row.  The waves' results are merged in a fixed order,
+// so the combine is deterministic.
 //   o_lat[row] = sum_i 2^(lse_i - M) O_i / sum_i 2^(lse_i - M)
 //   lse2[row]  = M + log2 sum_i 2^(lse_i - M)   (log2 units)
+// A split whose rows see no token has lse_i = -inf and weight 0.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) lse_combine(const float* __restrict__ part_o,
-                                                   const float* __restrict__ part_lse,
-                                                   const int32_t* __restrict__ ctx_lens, int Sq,
-                                                   int splits, int kv_chunk, float* __restrict__ o_lat,
-                                                   float* __restrict__ lse2_out) {
-  __shared__ float red_m[4][16];
-  __shared__ float red_w[4][16];
-  __shared__ f32x4 red_o[4][64];
+constexpr int kCombineMaxWaves = 16;
+constexpr int kCombineBatch = 8;
+
+__global__ void __launch_bounds__(1024) lse_combine(const float* __restrict__ part_o,
+                                                    const float* __restrict__ part_lse,
+                                                    const int32_t* __restrict__ ctx_lens, int Sq,
+                                                    int splits, int kv_chunk, float* __restrict__ o_lat,
+                                                    float* __restrict__ lse2_out) {
+  __shared__ f32x4 red_o[kCombineMaxWaves][64];
+  __shared__ f32x4 red_m[kCombineMaxWaves][4];
+  __shared__ f32x4 red_w[kCombineMaxWaves][4];
   const int cbm = blockIdx.x;           // 32 column blocks of 16
   const int rgg = blockIdx.y;           // row group in [0, 2*Sq)
   const int b = blockIdx.z;
+  const int nw = blockDim.x >> 6;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4, n16 = lane & 15;
   const int RGT = 2 * Sq;
   const int L = ctx_lens[b];
   const int nsplit = min(splits, (L + kv_chunk - 1) / kv_chunk);
+  const size_t lse_stride = (size_t)Sq * 32;
+  const float* lse_base = part_lse + (size_t)b * splits * lse_stride + rgg * 16 + 4 * g;
+  const float* o_base = part_o + (((size_t)b * splits * RGT + rgg) * 32 + cbm) * 256 + lane * 4;
+  const size_t o_stride = (size_t)RGT * 32 * 256;
 
-  // 1. row maxima of the split LSEs (rows 4g..4g+3 of the group)
-  f32x4 m4 = f32x4{kNegInf, kNegInf, kNegInf, kNegInf};
-  for (int s = wave; s < nsplit; s += 4) {
-    const f32x4 l4 = *(const f32x4*)(part_lse + ((size_t)b * splits + s) * (Sq * 32) + rgg * 16 + 4 * g);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) m4[i] = fmaxf(m4[i], l4[i]);
-  }
-  if (n16 == 0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) red_m[wave][4 * g + i] = m4[i];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 4 * g + i;
-    m4[i] = fmaxf(fmaxf(red_m[0][r], red_m[1][r]), fmaxf(red_m[2][r], red_m[3][r]));
-  }
-
-  // 2. weighted sums
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 m = f32x4{kNegInf, kNegInf, kNegInf, kNegInf};
   f32x4 wsum = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int s = wave; s < nsplit; s += 4) {
-    const size_t unit = (size_t)b * splits + s;
-    const f32x4 l4 = *(const f32x4*)(part_lse + unit * (Sq * 32) + rgg * 16 + 4 * g);
-    const f32x4 o4 = *(const f32x4*)(part_o + ((unit * RGT + rgg) * 32 + cbm) * 256 + lane * 4);
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = wave; s0 < nsplit; s0 += nw * kCombineBatch) {
+    f32x4 l4[kCombineBatch], o4[kCombineBatch];
+#pragma unroll
+    for (int k = 0; k < kCombineBatch; ++k) {
+      const int s = min(s0 + k * nw, nsplit - 1);   // past the end: re-read, weight 0 below
+      l4[k] = *(const f32x4*)(lse_base + s * lse_stride);
+      o4[k] = *(const f32x4*)(o_base + s * o_stride);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // every load of the batch in flight before the first use
+#pragma unroll
+    for (int k = 0; k < kCombineBatch; ++k)
+      if (s0 + k * nw >= nsplit) l4[k] = f32x4{kNegInf, kNegInf, kNegInf, kNegInf};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float wt = (l4[i] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(l4[i] - m4[i]);
-      wsum[i] += wt;
-      acc[i] = fmaf(wt, o4[i], acc[i]);
+      float bm = m[i];
+#pragma unroll
+      for (int k = 0; k < kCombineBatch; ++k) bm = fmaxf(bm, l4[k][i]);
+      const float sc = (m[i] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m[i] - bm);
+      wsum[i] *= sc;
+      acc[i] *= sc;
+      m[i] = bm;
+#pragma unroll
+      for (int k = 0; k < kCombineBatch; ++k) {
+        const float wt = (l4[k][i] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(l4[k][i] - bm);
+        wsum[i] += wt;
+        acc[i] = fmaf(wt, o4[k][i], acc[i]);
+      }
     }
   }
   red_o[wave][lane] = acc;
   if (n16 == 0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) red_w[wave][4 * g + i] = wsum[i];
+    red_m[wave][g] = m;
+    red_w[wave][g] = wsum;
   }
   __syncthreads();
   if (wave != 0) return;
-  f32x4 o = red_o[0][lane];
+  f32x4 M = red_m[0][g];
+  for (int w = 1; w < nw; ++w) {
+    const f32x4 t = red_m[w][g];
 #pragma unroll
-  for (int w = 1; w < 4; ++w) {
-    const f32x4 t = red_o[w][lane];
+    for (int i = 0; i < 4; ++i) M[i] = fmaxf(M[i], t[i]);
+  }
+  f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f}, ws = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int w = 0; w < nw; ++w) {
+    const f32x4 tm = red_m[w][g], tw = red_w[w][g], to = red_o[w][lane];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] += t[i];
+    for (int i = 0; i < 4; ++i) {
+      const float sc = (tm[i] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(tm[i] - M[i]);
+      ws[i] = fmaf(tw[i], sc, ws[i]);
+      o[i] = fmaf(to[i], sc, o[i]);
+    }
   }
   const int j = rgg >> 1;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = 4 * g + i;
-    const float ws = red_w[0][r] + red_w[1][r] + red_w[2][r] + red_w[3][r];
     const int h = (rgg & 1) * 16 + r;
     const size_t row = ((size_t)b * Sq + j) * kHeads + h;
-    o_lat[row * kLatent + cbm * 16 + n16] = (ws > 0.f) ? o[i] / ws : 0.f;
-    if (cbm == 0 && n16 == 0) lse2_out[row] = (ws > 0.f) ? m4[i] + __log2f(ws) : kNegInf;
+    o_lat[row * kLatent + cbm * 16 + n16] = (ws[i] > 0.f) ? o[i] / ws[i] : 0.f;
+    if (cbm == 0 && n16 == 0) lse2_out[row] = (ws[i] > 0.f) ? M[i] + __log2f(ws[i]) : kNegInf;
   }
 }
 
 // ---------------------------------------------------------------------------
 // W_UV up-projection: out[r][v] = bf16(sum_c W_UV[h][v][c] o_lat[r][c]),
-// W_UV[h] = w_kv_b rows [h*256 + 128, h*256 + 256).  One workgroup per
-// (head, 16 output dims); 16 lanes split each 512-long dot product.
+// W_UV[h] = w_kv_b rows [h*256 + 128, h*256 + 256).  A workgroup covers
+// (head, 16 output dims, 4 query rows); 16 lanes split each 512-long dot
+// product, and every load of the workgroup is issued before the first FMA.
 //
 // The workgroup of output block 0 also writes the natural-log LSE.  Scores
 // were taken with the bf16-rounded absorbed query; the exact score differs
 // by scale * (q_lat - bf16(q_lat)) . c_t, so to first order the LSE moves by
 // the softmax mean of that difference, scale * qres . o_lat.
 // ---------------------------------------------------------------------------
+constexpr int kUpRows = 4;
+
 __global__ void __launch_bounds__(256) upproject(const float* __restrict__ o_lat,
                                                  const uint16_t* __restrict__ w_kv_b,
                                                  const float* __restrict__ qres,
@@ -184,53 +229,79 @@ __global__ void __launch_bounds__(256) upproject(const float* __restrict__ o_lat
                                                  int rows_bs) {
   const int vblk = blockIdx.x;          // 8 blocks of 16 output dims
   const int h = blockIdx.y;
+  const int r0 = blockIdx.z * kUpRows;
   const int vl = threadIdx.x >> 4;
   const int v = vblk * 16 + vl;
   const int part = threadIdx.x & 15;    // columns [part*32, part*32 + 32)
   const uint16_t* wrow = w_kv_b + ((size_t)h * kWRowsPerHead + kNope + v) * kLatent + part * 32;
-  const bool lse_lane = (lse != nullptr) && vblk == 0 && vl == 0;
+  // workgroups of output block 0 also finish the LSE: lanes of output dim vl
+  // take row r0 + (vl & 3)
+  const bool lse_wg = (lse != nullptr) && vblk == 0;
+  const int rc = r0 + (vl & (kUpRows - 1));
+  const size_t crow = (size_t)min(rc, rows_bs - 1) * kHeads + h;
+
+  uint4 wu[4];
+  float4 x[kUpRows][8];
+  float4 qr[8];
+  float l2 = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) wu[k] = *(const uint4*)(wrow + 8 * k);
+#pragma unroll
+  for (int rr = 0; rr < kUpRows; ++rr) {
+    const size_t row = (size_t)min(r0 + rr, rows_bs - 1) * kHeads + h;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[rr][k] = *(const float4*)(o_lat + row * kLatent + part * 32 + 4 * k);
+  }
+  if (lse_wg) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) qr[k] = *(const float4*)(qres + crow * kLatent + part * 32 + 4 * k);
+    l2 = lse2[crow];
+  }
+  __builtin_amdgcn_sched_barrier(0);   // every load in flight before the first use
+
   float w[32];
 #pragma unroll
-  for (int k = 0; k < 32; k += 8) {
-    const uint4 u = *(const uint4*)(wrow + k);
-    const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t wd[4] = {wu[k].x, wu[k].y, wu[k].z, wu[k].w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      w[k + 2 * e] = __uint_as_float(wd[e] << 16);
-      w[k + 2 * e + 1] = __uint_as_float(wd[e] & 0xFFFF0000u);
+      w[8 * k + 2 * e] = __uint_as_float(wd[e] << 16);
+      w[8 * k + 2 * e + 1] = __uint_as_float(wd[e] & 0xFFFF0000u);
     }
   }
-  for (int r = 0; r < rows_bs; ++r) {
-    const size_t row = (size_t)r * kHeads + h;
-    const float* ol = o_lat + row * kLatent + part * 32;
-    float acc = 0.f, corr = 0.f;
 #pragma unroll
-    for (int k = 0; k < 32; k += 4) {
-      const float4 x = *(const float4*)(ol + k);
-      acc = fmaf(w[k], x.x, acc);
-      acc = fmaf(w[k + 1], x.y, acc);
-      acc = fmaf(w[k + 2], x.z, acc);
-      acc = fmaf(w[k + 3], x.w, acc);
-      if (lse_lane) {
-        const float4 d = *(const float4*)(qres + row * kLatent + part * 32 + k);
-        corr = fmaf(d.x, x.x, corr);
-        corr = fmaf(d.y, x.y, corr);
-        corr = fmaf(d.z, x.z, corr);
-        corr = fmaf(d.w, x.w, corr);
-      }
+  for (int rr = 0; rr < kUpRows; ++rr) {
+    float acc = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      acc = fmaf(w[4 * k], x[rr][k].x, acc);
+      acc = fmaf(w[4 * k + 1], x[rr][k].y, acc);
+      acc = fmaf(w[4 * k + 2], x[rr][k].z, acc);
+      acc = fmaf(w[4 * k + 3], x[rr][k].w, acc);
     }
 #pragma unroll
-    for (int d = 8; d >= 1; d >>= 1) {
-      acc += __shfl_xor(acc, d, 16);
-      corr += __shfl_xor(corr, d, 16);
-    }
-    if (part == 0) {
-      out[row * kVDim + v] = f32_to_bf16(acc);
-      if (lse_lane) {
-        const float l2 = lse2[row];
-        lse[row] = (l2 == kNegInf) ? kNegInf : (l2 + scale_log2 * corr) * 0.69314718055994530942f;
+    for (int d = 8; d >= 1; d >>= 1) acc += __shfl_xor(acc, d, 16);
+    const int r = r0 + rr;
+    if (part == 0 && r < rows_bs) out[((size_t)r * kHeads + h) * kVDim + v] = f32_to_bf16(acc);
+  }
+  if (lse_wg) {
+    float corr = 0.f;
+#pragma unroll
+    for (int rr = 0; rr < kUpRows; ++rr) {
+      float c = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        c = fmaf(qr[k].x, x[rr][k].x, c);
+        c = fmaf(qr[k].y, x[rr][k].y, c);
+        c = fmaf(qr[k].z, x[rr][k].z, c);
+        c = fmaf(qr[k].w, x[rr][k].w, c);
       }
+      corr = ((vl & (kUpRows - 1)) == rr) ? c : corr;
     }
+#pragma unroll
+    for (int d = 8; d >= 1; d >>= 1) corr += __shfl_xor(corr, d, 16);
+    if (part == 0 && vl < kUpRows && rc < rows_bs)
+      lse[crow] = (l2 == kNegInf) ? kNegInf : (l2 + scale_log2 * corr) * 0.69314718055994530942f;
   }
 }
 
@@ -286,7 +357,8 @@ __global__ void __launch_bounds__(256) cache_append(uint8_t* __restrict__ cache,
 
 hipError_t launch_absorb(const uint16_t* q_nope, const uint16_t* q_pe, const uint16_t* w_kv_b,
                          uint16_t* qabs, float* qres, uint8_t* zero_row, int rows, hipStream_t stream) {
-  hipLaunchKernelGGL(absorb_query, dim3(kLatent / 64, kHeads), dim3(256), 0, stream, q_nope, q_pe,
+  const unsigned rb = (unsigned)((rows + kAbsorbRows - 1) / kAbsorbRows);
+  hipLaunchKernelGGL(absorb_query, dim3(kLatent / 64, kHeads, rb), dim3(256), 0, stream, q_nope, q_pe,
                      w_kv_b, qabs, qres, zero_row, rows);
   return hipGetLastError();
 }
@@ -294,7 +366,9 @@ hipError_t launch_absorb(const uint16_t* q_nope, const uint16_t* q_pe, const uin
 hipError_t launch_combine(const float* part_o, const float* part_lse, const int32_t* ctx_lens,
                           int B, int Sq, int splits, int kv_chunk, float* o_lat, float* lse2,
                           hipStream_t stream) {
-  hipLaunchKernelGGL(lse_combine, dim3(32, 2 * Sq, B), dim3(256), 0, stream, part_o, part_lse,
+  // enough waves that each takes about a batch of splits, at most 16
+  const int waves = std::min(kCombineMaxWaves, std::max(1, (splits + kCombineBatch - 1) / kCombineBatch));
+  hipLaunchKernelGGL(lse_combine, dim3(32, 2 * Sq, B), dim3(64 * waves), 0, stream, part_o, part_lse,
                      ctx_lens, Sq, splits, kv_chunk, o_lat, lse2);
   return hipGetLastError();
 }
@@ -302,7 +376,8 @@ hipError_t launch_combine(const float* part_o, const float* part_lse, const int3
 hipError_t launch_upproj(const float* o_lat, const uint16_t* w_kv_b, const float* qres,
                          const float* lse2, float scale_log2, uint16_t* out, float* lse, int rows,
                          hipStream_t stream) {
-  hipLaunchKernelGGL(upproject, dim3(kVDim / 16, kHeads), dim3(256), 0, stream, o_lat, w_kv_b,
+  const unsigned rb = (unsigned)((rows + kUpRows - 1) / kUpRows);
+  hipLaunchKernelGGL(upproject, dim3(kVDim / 16, kHeads, rb), dim3(256), 0, stream, o_lat, w_kv_b,
                      qres, lse2, scale_log2, out, lse, rows);
   return hipGetLastError();
 }
