@@ -142,7 +142,7 @@ mla_status mla_cache_append(const mla_shape* shape /* host */, void* cache, int6
  *   lse          fp32 [B][Sq][32] natural-log sum of exp(s_t), or NULL
  *   workspace    device scratch of mla_decode_workspace_size() bytes,
  *                256-byte aligned
- * Supports 1 <= Sq <= 16.  B = 0 is a no-op. */
+ * Supports 1 <= Sq <= 16 and B * Sq <= 65535.  B = 0 is a no-op. */
 mla_status mla_decode(const mla_shape* shape /* host */, const void* q_nope, const void* q_pe,
                       const void* w_kv_b, const void* cache, int64_t stride_tokens,
                       const int32_t* ctx_lens, int32_t max_ctx_len, int32_t B, int32_t Sq,
@@ -161,7 +161,42 @@ mla_status mla_decode_paged(const mla_shape* shape /* host */, const void* q_nop
                             int32_t kv_chunk, void* out, float* lse, void* workspace,
                             size_t workspace_bytes, void* stream);
 
-/* Workspace bytes mla_decode / mla_decode_paged need for these sizes (host).
+/* One decode step of a layer for Sq new tokens per sequence, fused: the
+ * whole path of [MLA-arch] from the new tokens' projections to the attention
+ * output.  For token j of sequence b, at position p = L_b - Sq + j
+ * (ctx_lens already count the new tokens):
+ *   1. k_pe_new row (b*Sq + j) is rotated by YaRN RoPE at p and, with
+ *      c_kv_new row (b*Sq + j), written into the cache slot of token p (the
+ *      cache write of mla_cache_append; [MLA-arch], [KV-ledger §二]);
+ *   2. q_pe[b][j] is rotated at p (as mla_rope_yarn);
+ *   3. the decode of mla_decode / mla_decode_paged runs on the result.
+ * The results are bitwise those of mla_rope_yarn + mla_cache_append +
+ * mla_decode with the same arguments; the rotated q_pe is not written back.
+ *   rope          host YaRN parameters (as mla_rope_yarn)
+ *   q_pe          bf16 [B][Sq][32][64], NOT rotated
+ *   c_kv_new      bf16 [B*Sq][ld_c] latent rows of the new tokens (ld_c >= 512)
+ *   k_pe_new      bf16 [B*Sq][ld_k] rope rows, NOT rotated (ld_k >= 64)
+ *   cache         written at the new tokens' slots, read by the decode
+ * Every other argument as in mla_decode.  c_kv_new and k_pe_new must be
+ * 16-byte aligned with ld_c, ld_k multiples of 8. */
+mla_status mla_decode_step(const mla_shape* shape /* host */, const mla_rope_params* rope /* host */,
+                           const void* q_nope, const void* q_pe, const void* c_kv_new, int64_t ld_c,
+                           const void* k_pe_new, int64_t ld_k, const void* w_kv_b, void* cache,
+                           int64_t stride_tokens, const int32_t* ctx_lens, int32_t max_ctx_len,
+                           int32_t B, int32_t Sq, int32_t kv_chunk, void* out, float* lse,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* mla_decode_step against a paged cache (arguments as mla_decode_paged). */
+mla_status mla_decode_step_paged(const mla_shape* shape /* host */, const mla_rope_params* rope /* host */,
+                                 const void* q_nope, const void* q_pe, const void* c_kv_new, int64_t ld_c,
+                                 const void* k_pe_new, int64_t ld_k, const void* w_kv_b, void* cache,
+                                 int64_t num_pages, const int32_t* block_table, int32_t max_pages_per_seq,
+                                 const int32_t* ctx_lens, int32_t max_ctx_len, int32_t B, int32_t Sq,
+                                 int32_t kv_chunk, void* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/* Workspace bytes mla_decode, mla_decode_paged and the mla_decode_step calls
+ * need for these sizes (host).
  * kv_chunk as in mla_decode (0 = the library's choice). */
 mla_status mla_decode_workspace_size(const mla_shape* shape /* host */, int32_t B, int32_t Sq,
                                      int32_t max_ctx_len, int32_t kv_chunk,

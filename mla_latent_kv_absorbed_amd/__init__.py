@@ -17,7 +17,7 @@ from .build import lib_path
 
 __all__ = [
     "MlaError", "MlaShape", "MlaRopeParams", "default_shape", "default_rope", "library",
-    "mla_rope_yarn", "mla_cache_append", "mla_decode", "mla_decode_paged",
+    "mla_rope_yarn", "mla_cache_append", "mla_decode", "mla_decode_paged", "mla_decode_step",
     "mla_decode_workspace_size", "mla_decode_auto_chunk", "mla_status_string",
     "mla_timing_enable", "mla_timing_collect", "mla_timing_disable",
 ]
@@ -64,6 +64,11 @@ def library() -> ctypes.CDLL:
                            _P, _P, _P, ctypes.c_size_t, _P],
             "mla_decode_paged": [ctypes.POINTER(MlaShape), _P, _P, _P, _P, _I64, _P, _I32, _P, _I32,
                                  _I32, _I32, _I32, _P, _P, _P, ctypes.c_size_t, _P],
+            "mla_decode_step": [ctypes.POINTER(MlaShape), ctypes.POINTER(MlaRopeParams), _P, _P, _P, _I64, _P,
+                                _I64, _P, _P, _I64, _P, _I32, _I32, _I32, _I32, _P, _P, _P, ctypes.c_size_t, _P],
+            "mla_decode_step_paged": [ctypes.POINTER(MlaShape), ctypes.POINTER(MlaRopeParams), _P, _P, _P, _I64,
+                                      _P, _I64, _P, _P, _I64, _P, _I32, _P, _I32, _I32, _I32, _I32, _P, _P, _P,
+                                      ctypes.c_size_t, _P],
             "mla_decode_workspace_size": [ctypes.POINTER(MlaShape), _I32, _I32, _I32, _I32,
                                           ctypes.POINTER(ctypes.c_size_t)],
             "mla_decode_auto_chunk": [_I32, _I32, _I32, ctypes.POINTER(_I32)],
@@ -244,6 +249,48 @@ def mla_decode_paged(q_nope, q_pe, w_kv_b, cache, block_table, ctx_lens, max_ctx
                                       _ptr(ctx_lens), max_ctx_len, B, Sq, kv_chunk, _ptr(out), _ptr(lse),
                                       _ptr(workspace), workspace.numel(), _stream(stream)),
            "mla_decode_paged")
+    return out, lse
+
+
+def mla_decode_step(q_nope, q_pe, c_kv_new, k_pe_new, w_kv_b, cache, ctx_lens, max_ctx_len: int,
+                    kv_chunk: int = 0, block_table=None, out=None, lse=None, workspace=None,
+                    rope: MlaRopeParams | None = None, shape: MlaShape | None = None, stream=None):
+    """One fused decode step: rotate q_pe and the new rope rows at p = L_b - Sq + j, write the new
+    tokens' rows [c_kv_new | rot(k_pe_new)] into the cache, then decode.  q_pe and k_pe_new are
+    NOT rotated.  ``block_table`` selects the paged layout [num_pages, 64, 576]; otherwise the
+    cache is contiguous [B, stride, 576].  Returns (out, lse)."""
+    _need(cache, torch.bfloat16, "cache")
+    B, Sq = q_nope.shape[0], q_nope.shape[1]
+    for t, name, width in ((c_kv_new, "c_kv_new", 512), (k_pe_new, "k_pe_new", 64)):
+        if t.dtype != torch.bfloat16 or t.device.type != "cuda" or t.dim() != 2 or t.stride(1) != 1:
+            raise MlaError(f"{name} must be a 2-D bf16 GPU tensor with unit column stride")
+        if t.shape[0] != B * Sq or t.shape[1] < width:
+            raise MlaError(f"{name} must have B*Sq rows of at least {width} values")
+    out, lse, workspace, s = _decode_io(q_nope, q_pe, w_kv_b, ctx_lens, out, lse, workspace, B, Sq,
+                                        max_ctx_len, kv_chunk, shape)
+    r = rope if rope is not None else default_rope()
+    lib = library()
+    if block_table is None:
+        if cache.dim() != 3 or cache.shape[0] != B or cache.shape[2] != 576:
+            raise MlaError("cache must be [B, stride, 576]")
+        code = lib.mla_decode_step(ctypes.byref(s), ctypes.byref(r), _ptr(q_nope), _ptr(q_pe), _ptr(c_kv_new),
+                                   c_kv_new.stride(0), _ptr(k_pe_new), k_pe_new.stride(0), _ptr(w_kv_b),
+                                   _ptr(cache), cache.shape[1], _ptr(ctx_lens), max_ctx_len, B, Sq, kv_chunk,
+                                   _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream))
+        _check(code, "mla_decode_step")
+    else:
+        _need(block_table, torch.int32, "block_table")
+        if cache.dim() != 3 or cache.shape[1] != 64 or cache.shape[2] != 576:
+            raise MlaError("cache must be [num_pages, 64, 576]")
+        if block_table.dim() != 2 or block_table.shape[0] != B:
+            raise MlaError("block_table must be [B, max_pages_per_seq]")
+        code = lib.mla_decode_step_paged(ctypes.byref(s), ctypes.byref(r), _ptr(q_nope), _ptr(q_pe),
+                                         _ptr(c_kv_new), c_kv_new.stride(0), _ptr(k_pe_new), k_pe_new.stride(0),
+                                         _ptr(w_kv_b), _ptr(cache), cache.shape[0], _ptr(block_table),
+                                         block_table.shape[1], _ptr(ctx_lens), max_ctx_len, B, Sq, kv_chunk,
+                                         _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+                                         _stream(stream))
+        _check(code, "mla_decode_step_paged")
     return out, lse
 
 

@@ -2,6 +2,7 @@
 // include/mla.h).  Host side only: argument checks, split selection,
 // workspace carving and kernel launches on the caller's stream.
 #include <math.h>
+#include <algorithm>
 #include <string.h>
 
 #include "mla.h"   // include/mla.h (on the include path)
@@ -12,6 +13,7 @@ using namespace mla;
 namespace {
 
 constexpr int kMaxSq = 16;
+constexpr int64_t kMaxRows = 65535;   // B * Sq: one grid dimension of the combine
 
 // Opt-in kernel timing (mla_timing_*): event pairs around split-KV launches.
 struct Timing {
@@ -40,21 +42,38 @@ mla_status check_shape(const mla_shape* s) {
   return MLA_OK;
 }
 
-// Tokens per split when the caller passes 0: aim at one workgroup per compute
-// unit for a single sequence and about four per unit for batches (sequences
-// of a batch may be shorter than max_ctx_len), never below two tiles.
-int auto_chunk(int B, int max_ctx) {
-  if (B < 1) B = 1;
-  const int tiles = (max_ctx + kPage - 1) / kPage;
-  const int target_units = (B <= 1) ? 256 : 1024;
-  int splits = (target_units + B - 1) / B;
-  if (splits < 1) splits = 1;
-  int tiles_per_split = (tiles + splits - 1) / splits;
-  if (tiles_per_split < 2) tiles_per_split = 2;
-  return tiles_per_split * kPage;
+// Compute units of the current device (the balanced schedule aims at one
+// split-KV workgroup per unit).
+int compute_units() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    return 256;
+  return n;
 }
 
-int splits_for(int max_ctx, int chunk) { return (max_ctx + chunk - 1) / chunk; }
+// Upper bound of the number of segments (splits) of a call: with a fixed
+// kv_chunk every sequence has at most ceil(max_ctx_len / kv_chunk); the
+// balanced schedule (kv_chunk = 0) chooses c >= ceil(T / target) tiles, so
+// sum_b ceil(tiles_b / c) <= T / c + B <= target + B.
+int64_t max_segments(int B, int max_ctx, int kv_chunk, int target) {
+  if (kv_chunk > 0) return (int64_t)B * ((max_ctx + kv_chunk - 1) / kv_chunk);
+  return (int64_t)target + B;
+}
+
+// Tokens per split the balanced schedule picks when all B sequences hold
+// max_ctx tokens (the device decides from the actual lengths).
+int balanced_chunk(int B, int max_ctx, int target) {
+  const int64_t tiles = (max_ctx + kPage - 1) / kPage;
+  const int64_t T = tiles * B;
+  int64_t c = std::max<int64_t>(kMinTilesPerSplit, (T + target - 1) / target);
+  for (int it = 0; it < 8; ++it) {
+    const int64_t n = B * ((tiles + c - 1) / c);
+    if (n <= target) break;
+    c = std::max<int64_t>(c + 1, (c * n + target - 1) / target);
+  }
+  return (int)(c * kPage);
+}
 
 // YaRN NTK-by-parts frequencies (Peng et al., 2023): pairs turning more than
 // beta_fast times over the original context keep base^(-2i/d); pairs turning
@@ -83,15 +102,36 @@ void yarn_frequencies(const mla_rope_params& p, double* out) {
   }
 }
 
-mla_status decode_common(const mla_shape* shape, const void* q_nope, const void* q_pe,
-                         const void* w_kv_b, const void* cache, int64_t stride_tokens,
+// Optional fused front end of a decode call: rotate q_pe (and the new
+// tokens' rope rows) at p = L_b - Sq + j and write the new tokens' cache rows.
+struct StepInputs {
+  const mla_rope_params* rope;  // null: q_pe is already rotated, nothing appended
+  const void* c_new;
+  int64_t ld_c;
+  const void* k_new;
+  int64_t ld_k;
+};
+
+mla_status check_rope(const mla_rope_params* params) {
+  if (params == nullptr) return MLA_ERR_NULL;
+  if (params->rope_dim != kRope || !(params->base > 1.0) || !(params->factor >= 1.0) ||
+      !(params->original_max_position > 0) || !(params->beta_fast > params->beta_slow) ||
+      !(params->beta_slow > 0))
+    return MLA_ERR_SHAPE;
+  return MLA_OK;
+}
+
+mla_status decode_common(const mla_shape* shape, const StepInputs& step, const void* q_nope,
+                         const void* q_pe, const void* w_kv_b, const void* cache, int64_t stride_tokens,
                          int64_t num_pages, const int32_t* block_table, int32_t max_pages,
                          const int32_t* ctx_lens, int32_t max_ctx_len, int32_t B, int32_t Sq,
                          int32_t kv_chunk, void* out, float* lse, void* workspace,
                          size_t workspace_bytes, void* stream, bool paged) {
   mla_status st = check_shape(shape);
   if (st != MLA_OK) return st;
+  if (step.rope != nullptr && (st = check_rope(step.rope)) != MLA_OK) return st;
   if (B < 0 || Sq < 1 || Sq > kMaxSq || max_ctx_len < Sq) return MLA_ERR_RANGE;
+  if ((int64_t)B * Sq > kMaxRows) return MLA_ERR_RANGE;
   if (B == 0) return MLA_OK;
   if (!q_nope || !q_pe || !w_kv_b || !cache || !ctx_lens || !out || !workspace) return MLA_ERR_NULL;
   if (paged) {
@@ -105,56 +145,93 @@ mla_status decode_common(const mla_shape* shape, const void* q_nope, const void*
       !aligned16(out) || ((uintptr_t)workspace & 255u) != 0)
     return MLA_ERR_ALIGN;
   if (lse != nullptr && ((uintptr_t)lse & 3u) != 0) return MLA_ERR_ALIGN;
-  const int chunk = kv_chunk ? kv_chunk : auto_chunk(B, max_ctx_len);
-  const int splits = splits_for(max_ctx_len, chunk);
-  if ((int64_t)B * splits > 0x7FFFFFFF) return MLA_ERR_RANGE;
-  const WorkspaceLayout wl = workspace_layout(B, Sq, splits);
+  if (step.rope != nullptr) {
+    if (!step.c_new || !step.k_new) return MLA_ERR_NULL;
+    if (step.ld_c < kLatent || step.ld_k < kRope) return MLA_ERR_RANGE;
+    if (!aligned16(step.c_new) || !aligned16(step.k_new) || step.ld_c % 8 != 0 || step.ld_k % 8 != 0)
+      return MLA_ERR_ALIGN;
+  }
+  const int target = compute_units();
+  const int64_t segs = max_segments(B, max_ctx_len, kv_chunk, target);
+  if (segs > 0x7FFFFFFF) return MLA_ERR_RANGE;
+  const WorkspaceLayout wl = workspace_layout(B, Sq, (int)segs);
   if (workspace_bytes < wl.total) return MLA_ERR_WORKSPACE;
 
   uint8_t* ws = (uint8_t*)workspace;
   uint16_t* qabs = (uint16_t*)(ws + wl.qabs);
   float* qres = (float*)(ws + wl.qres);
-  float* lse2 = (float*)(ws + wl.lse2);
   uint8_t* zero_row = ws + wl.zero_row;
-  float* part_o = (float*)(ws + wl.part_o);
-  float* part_lse = (float*)(ws + wl.part_lse);
-  float* o_lat = (float*)(ws + wl.o_lat);
   hipStream_t s = (hipStream_t)stream;
   const int rows = B * Sq;
+  const float scale_log2 = shape->softmax_scale * 1.44269504088896340736f;
 
-  if (launch_absorb((const uint16_t*)q_nope, (const uint16_t*)q_pe, (const uint16_t*)w_kv_b, qabs,
-                    qres, zero_row, rows, s) != hipSuccess)
-    return MLA_ERR_DEVICE;
+  PrepParams pp;
+  pp.q_nope = (const uint16_t*)q_nope;
+  pp.q_pe = (const uint16_t*)q_pe;
+  pp.w_kv_b = (const uint16_t*)w_kv_b;
+  pp.qabs = qabs;
+  pp.qres = qres;
+  pp.zero_row = zero_row;
+  pp.rows = rows;
+  pp.Sq = Sq;
+  pp.ctx_lens = ctx_lens;
+  pp.rotate = step.rope != nullptr;
+  memset(&pp.inv, 0, sizeof(pp.inv));
+  if (step.rope != nullptr) yarn_frequencies(*step.rope, pp.inv.v);
+  pp.c_new = (const uint16_t*)step.c_new;
+  pp.ld_c = step.ld_c;
+  pp.k_new = (const uint16_t*)step.k_new;
+  pp.ld_k = step.ld_k;
+  pp.cache = (uint8_t*)cache;
+  pp.stride_tokens = stride_tokens;
+  pp.block_table = block_table;
+  pp.max_pages = max_pages;
+  pp.paged = paged ? 1 : 0;
+  pp.B = B;
+  pp.fixed_tiles = kv_chunk / kPage;
+  pp.target_segs = target;
+  pp.max_segs = (int)segs;
+  pp.seg_desc = (int4*)(ws + wl.seg_desc);
+  pp.seg_start = (int32_t*)(ws + wl.seg_start);
+  if (launch_prep(pp, s) != hipSuccess) return MLA_ERR_DEVICE;
+
   DecodeParams p;
   p.qabs = qabs;
   p.cache = (const uint8_t*)cache;
   p.stride_tokens = stride_tokens;
   p.block_table = block_table;
   p.max_pages = max_pages;
-  p.ctx_lens = ctx_lens;
+  p.seg_desc = pp.seg_desc;
   p.Sq = Sq;
-  p.kv_chunk = chunk;
-  p.splits = splits;
-  p.scale_log2 = shape->softmax_scale * 1.44269504088896340736f;
-  p.part_o = part_o;
-  p.part_lse = part_lse;
+  p.scale_log2 = scale_log2;
+  p.part_o = (float*)(ws + wl.part_o);
+  p.part_lse = (float*)(ws + wl.part_lse);
   p.zero_row = zero_row;
   const bool timed = g_timing.on && g_timing.used < g_timing.capacity;
   if (timed && hipEventRecord(g_timing.ev[2 * g_timing.used], s) != hipSuccess) return MLA_ERR_DEVICE;
   for (int j0 = 0; j0 < Sq; j0 += kMaxQueryGroup) {
     const int qg = (Sq - j0 >= 2) ? 2 : 1;
     p.j0 = j0;
-    if (launch_decode(p, B, qg, paged, s) != hipSuccess) return MLA_ERR_DEVICE;
+    if (launch_decode(p, (int)segs, qg, paged, s) != hipSuccess) return MLA_ERR_DEVICE;
   }
   if (timed) {
     if (hipEventRecord(g_timing.ev[2 * g_timing.used + 1], s) != hipSuccess) return MLA_ERR_DEVICE;
     ++g_timing.used;
   }
-  if (launch_combine(part_o, part_lse, ctx_lens, B, Sq, splits, chunk, o_lat, lse2, s) != hipSuccess)
-    return MLA_ERR_DEVICE;
-  if (launch_upproj(o_lat, (const uint16_t*)w_kv_b, qres, lse2, p.scale_log2, (uint16_t*)out, lse, rows,
-                    s) != hipSuccess)
-    return MLA_ERR_DEVICE;
+
+  CombineParams cp;
+  cp.part_o = p.part_o;
+  cp.part_lse = p.part_lse;
+  cp.seg_start = pp.seg_start;
+  cp.max_segs = (int)segs;
+  cp.Sq = Sq;
+  cp.hrows = rows * kHeads;
+  cp.w_kv_b = (const uint16_t*)w_kv_b;
+  cp.qres = qres;
+  cp.scale_log2 = scale_log2;
+  cp.out = (uint16_t*)out;
+  cp.lse = lse;
+  if (launch_combine_upproject(cp, s) != hipSuccess) return MLA_ERR_DEVICE;
   return MLA_OK;
 }
 
@@ -202,11 +279,8 @@ const char* mla_status_string(mla_status s) {
 
 mla_status mla_rope_yarn(const mla_rope_params* params, const void* src, int64_t ld_src, void* dst,
                          int64_t ld_dst, const int32_t* positions, int64_t n, void* stream) {
-  if (params == nullptr) return MLA_ERR_NULL;
-  if (params->rope_dim != kRope || !(params->base > 1.0) || !(params->factor >= 1.0) ||
-      !(params->original_max_position > 0) || !(params->beta_fast > params->beta_slow) ||
-      !(params->beta_slow > 0))
-    return MLA_ERR_SHAPE;
+  const mla_status st = check_rope(params);
+  if (st != MLA_OK) return st;
   if (n < 0 || ld_src < params->rope_dim || ld_dst < params->rope_dim) return MLA_ERR_RANGE;
   if (n == 0) return MLA_OK;
   if (!src || !dst || !positions) return MLA_ERR_NULL;
@@ -242,8 +316,9 @@ mla_status mla_decode(const mla_shape* shape, const void* q_nope, const void* q_
                       const void* cache, int64_t stride_tokens, const int32_t* ctx_lens,
                       int32_t max_ctx_len, int32_t B, int32_t Sq, int32_t kv_chunk, void* out,
                       float* lse, void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_common(shape, q_nope, q_pe, w_kv_b, cache, stride_tokens, 0, nullptr, 0, ctx_lens,
-                       max_ctx_len, B, Sq, kv_chunk, out, lse, workspace, workspace_bytes, stream, false);
+  return decode_common(shape, StepInputs{}, q_nope, q_pe, w_kv_b, cache, stride_tokens, 0, nullptr, 0,
+                       ctx_lens, max_ctx_len, B, Sq, kv_chunk, out, lse, workspace, workspace_bytes, stream,
+                       false);
 }
 
 mla_status mla_decode_paged(const mla_shape* shape, const void* q_nope, const void* q_pe,
@@ -252,9 +327,34 @@ mla_status mla_decode_paged(const mla_shape* shape, const void* q_nope, const vo
                             const int32_t* ctx_lens, int32_t max_ctx_len, int32_t B, int32_t Sq,
                             int32_t kv_chunk, void* out, float* lse, void* workspace,
                             size_t workspace_bytes, void* stream) {
-  return decode_common(shape, q_nope, q_pe, w_kv_b, cache, 0, num_pages, block_table, max_pages_per_seq,
-                       ctx_lens, max_ctx_len, B, Sq, kv_chunk, out, lse, workspace, workspace_bytes,
-                       stream, true);
+  return decode_common(shape, StepInputs{}, q_nope, q_pe, w_kv_b, cache, 0, num_pages, block_table,
+                       max_pages_per_seq, ctx_lens, max_ctx_len, B, Sq, kv_chunk, out, lse, workspace,
+                       workspace_bytes, stream, true);
+}
+
+mla_status mla_decode_step(const mla_shape* shape, const mla_rope_params* rope, const void* q_nope,
+                           const void* q_pe, const void* c_kv_new, int64_t ld_c, const void* k_pe_new,
+                           int64_t ld_k, const void* w_kv_b, void* cache, int64_t stride_tokens,
+                           const int32_t* ctx_lens, int32_t max_ctx_len, int32_t B, int32_t Sq,
+                           int32_t kv_chunk, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  if (rope == nullptr) return MLA_ERR_NULL;
+  return decode_common(shape, StepInputs{rope, c_kv_new, ld_c, k_pe_new, ld_k}, q_nope, q_pe, w_kv_b, cache,
+                       stride_tokens, 0, nullptr, 0, ctx_lens, max_ctx_len, B, Sq, kv_chunk, out, lse,
+                       workspace, workspace_bytes, stream, false);
+}
+
+mla_status mla_decode_step_paged(const mla_shape* shape, const mla_rope_params* rope, const void* q_nope,
+                                 const void* q_pe, const void* c_kv_new, int64_t ld_c, const void* k_pe_new,
+                                 int64_t ld_k, const void* w_kv_b, void* cache, int64_t num_pages,
+                                 const int32_t* block_table, int32_t max_pages_per_seq,
+                                 const int32_t* ctx_lens, int32_t max_ctx_len, int32_t B, int32_t Sq,
+                                 int32_t kv_chunk, void* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  if (rope == nullptr) return MLA_ERR_NULL;
+  return decode_common(shape, StepInputs{rope, c_kv_new, ld_c, k_pe_new, ld_k}, q_nope, q_pe, w_kv_b, cache,
+                       0, num_pages, block_table, max_pages_per_seq, ctx_lens, max_ctx_len, B, Sq, kv_chunk,
+                       out, lse, workspace, workspace_bytes, stream, true);
 }
 
 mla_status mla_decode_workspace_size(const mla_shape* shape, int32_t B, int32_t Sq, int32_t max_ctx_len,
@@ -263,9 +363,15 @@ mla_status mla_decode_workspace_size(const mla_shape* shape, int32_t B, int32_t 
   if (st != MLA_OK) return st;
   if (bytes == nullptr) return MLA_ERR_NULL;
   if (B < 0 || Sq < 1 || Sq > kMaxSq || max_ctx_len < Sq) return MLA_ERR_RANGE;
+  if ((int64_t)B * Sq > kMaxRows) return MLA_ERR_RANGE;
   if (kv_chunk < 0 || kv_chunk % kPage != 0) return MLA_ERR_RANGE;
-  const int chunk = kv_chunk ? kv_chunk : auto_chunk(B, max_ctx_len);
-  *bytes = (B == 0) ? 0 : workspace_layout(B, Sq, splits_for(max_ctx_len, chunk)).total;
+  if (B == 0) {
+    *bytes = 0;
+    return MLA_OK;
+  }
+  const int64_t segs = max_segments(B, max_ctx_len, kv_chunk, compute_units());
+  if (segs > 0x7FFFFFFF) return MLA_ERR_RANGE;
+  *bytes = workspace_layout(B, Sq, (int)segs).total;
   return MLA_OK;
 }
 
@@ -310,7 +416,7 @@ mla_status mla_timing_disable(void) {
 mla_status mla_decode_auto_chunk(int32_t B, int32_t Sq, int32_t max_ctx_len, int32_t* kv_chunk) {
   if (kv_chunk == nullptr) return MLA_ERR_NULL;
   if (B < 0 || Sq < 1 || Sq > kMaxSq || max_ctx_len < Sq) return MLA_ERR_RANGE;
-  *kv_chunk = auto_chunk(B, max_ctx_len);
+  *kv_chunk = balanced_chunk(B < 1 ? 1 : B, max_ctx_len, compute_units());
   return MLA_OK;
 }
 

@@ -1,6 +1,6 @@
 // Split-KV flash decoding over the latent cache on gfx950 (bf16 MFMA).
 //
-// What is computed (per sequence b, split of kv_chunk tokens, query token j,
+// What is computed (per sequence b, split of its tokens, query token j,
 // head h): the online-softmax partial of
 //     s_t = scale * ([q_lat | q_pe] . [c_t | k_pe_t])
 // over the split's visible tokens, i.e. (O = sum_t p_t c_t / sum_t p_t,
@@ -9,7 +9,8 @@
 // against the latent directly is the W_UK absorption, and the LSE combine and
 // W_UV up-projection of the partials follow in kernels.hip.
 //
-// Work decomposition (one workgroup of 4 waves per (sequence, split)):
+// Work decomposition (one workgroup of 4 waves per split, described by a
+// segment record {b, first token, end token, L_b} of the call's schedule):
 //  * The split streams through LDS in 64-token slots (one page, 72 KiB) of a
 //    two-slot ring, filled by direct global->LDS 16-byte loads: while the
 //    waves consume one slot the next is in flight, and the first slot is
@@ -28,9 +29,12 @@
 //    eight reads in flight) and the wave's 16 query rows held in registers as
 //    the B operand.
 //  * The S^T accumulator layout (lane = row, 4 tokens per lane) is exactly the
-//    A-operand layout P[row][token] of the value product; the value operand
-//    C[token][col] is fetched in that token order with ds_read_b64_tr_b16
-//    (transposing 4 x 16 blocks), so P never leaves registers.
+//    operand layout of P[row][token] in the value product; the latent values
+//    C[token][col] are fetched in that token order with ds_read_b64_tr_b16
+//    (transposing 4 x 16 blocks), so P never leaves registers.  The product
+//    is taken as O^T = C^T . P^T (latent values as the A operand), so that a
+//    lane's accumulator holds 4 consecutive latent columns of one row and the
+//    partials leave the kernel as plain row-major fp32 rows.
 //  * No rescaling inside the loop: a row's reference max is fixed at its
 //    first visible slot, and p = 2^(s - m_ref) may grow to 2^64 (sums stay far
 //    inside fp32).  Each wave also tracks the rows' true maxima; if any score
@@ -76,7 +80,7 @@ __device__ __forceinline__ void wait_slots_ahead(int ahead) {
 __device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                :
-               : "s"(lds), "v"(gaddr)
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(gaddr)
                : "memory", "m0");
 }
 
@@ -84,8 +88,6 @@ __device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds) {
 __device__ __forceinline__ int tile_slot(int tok, int c) {
   return c < 64 ? (c ^ (tok & 15)) : (64 + ((c - 64) ^ ((tok >> 1) & 7)));
 }
-
-__device__ __forceinline__ float bcast_row(float v, int src_lane) { return __shfl(v, src_lane, 64); }
 
 template <int QG, bool PAGED>
 __global__ void __launch_bounds__(256, 1) splitkv_decode(DecodeParams p) {
@@ -102,18 +104,16 @@ __global__ void __launch_bounds__(256, 1) splitkv_decode(DecodeParams p) {
   const int g = lane >> 4, n16 = lane & 15;
   const int rg = wave % RG, tp = wave / RG;
 
-  const int unit = blockIdx.x;
-  const int b = unit / p.splits;
-  const int split = unit - b * p.splits;
-  const int L = p.ctx_lens[b];
-  const int t_begin = split * p.kv_chunk;
-  const int t_end = min(L, t_begin + p.kv_chunk);
-  if (t_begin >= t_end) return;     // split past the end: the combine never reads it
+  const int unit = blockIdx.x;   // segment: tokens [t_begin, t_end) of sequence b
+  const int4 seg = p.seg_desc[unit];
+  const int b = seg.x, t_begin = seg.y, t_end = seg.z, L = seg.w;
+  if (b < 0 || t_begin >= t_end) return;   // no segment: the combine never reads it
 
   const int j = p.j0 + (rg >> 1);
   const int limit = min(t_end, L - p.Sq + j + 1);   // rows of this wave see tokens < limit
   const int rg_glob = 2 * p.j0 + rg;
-  float* out_o = p.part_o + ((size_t)unit * (2 * p.Sq) + rg_glob) * (32 * 64 * 4);
+  // partial rows of this wave's row group: [unit][j*32 + h][512] fp32
+  float* out_o = p.part_o + ((size_t)unit * (2 * p.Sq) + rg_glob) * (16 * kLatent);
   float* out_lse = p.part_lse + (size_t)unit * (p.Sq * 32) + rg_glob * 16;
 
   // Byte offset inside a slot of each 16-byte chunk this lane loads: LDS
@@ -272,7 +272,7 @@ __global__ void __launch_bounds__(256, 1) splitkv_decode(DecodeParams p) {
       __builtin_amdgcn_sched_group_barrier(0x100, kPvRing, 1);
 #pragma unroll
       for (int cb = 0; cb < 32; ++cb) {
-        o[cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, rv[cb % kPvRing], o[cb], 0, 0, 0);
+        o[cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(rv[cb % kPvRing], pa, o[cb], 0, 0, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
         if (cb + kPvRing < 32) {
           rv[cb % kPvRing] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)pv_src(cb + kPvRing));
@@ -301,7 +301,7 @@ __global__ void __launch_bounds__(256, 1) splitkv_decode(DecodeParams p) {
       for (int i = 0; i < NPV; ++i) {
         const int kk = i / 32, cb = i % 32, r = i % kPvRing;
         const s16x8 both = __builtin_shufflevector(lo[r], hi[r], 0, 1, 2, 3, 4, 5, 6, 7);
-        o[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[kk], __builtin_bit_cast(bf16x8, both), o[cb], 0, 0, 0);
+        o[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, both), pa[kk], o[cb], 0, 0, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
         if (i + kPvRing < NPV) {
           lo[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)pv_at(i + kPvRing));
@@ -370,32 +370,29 @@ __global__ void __launch_bounds__(256, 1) splitkv_decode(DecodeParams p) {
     l_row = l_row * a_own + l1 * a_other;
     m_ref = mm;
   }
+  // lane (g, n16) holds row n16, columns 16*cb + 4g .. 16*cb + 4g + 3
   const float inv = (l_row > 0.f) ? 1.f / l_row : 0.f;
-  float s_own[4], s_other[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    s_own[i] = bcast_row(a_own * inv, 4 * g + i);
-    s_other[i] = bcast_row(a_other * inv, 4 * g + i);
-  }
+  const float s_own = a_own * inv, s_other = a_other * inv;
+  float* orow = out_o + n16 * kLatent + 4 * g;
 #pragma unroll
   for (int cb = 0; cb < 32; ++cb) {
     f32x4 v = *(const f32x4*)(mine + (cb * 64 + lane) * 4);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] *= s_own[i];
+    for (int i = 0; i < 4; ++i) v[i] *= s_own;
     if constexpr (TP == 2) {
       const f32x4 w = *(const f32x4*)(other + (cb * 64 + lane) * 4);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = fmaf(w[i], s_other[i], v[i]);
+      for (int i = 0; i < 4; ++i) v[i] = fmaf(w[i], s_other, v[i]);
     }
-    *(f32x4*)(out_o + (cb * 64 + lane) * 4) = v;
+    *(f32x4*)(orow + cb * 16) = v;
   }
   if (lane < 16) out_lse[lane] = (l_row > 0.f) ? m_ref + __log2f(l_row) : kNegInf;
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeParams& p, int B, int query_group, bool paged, hipStream_t stream) {
-  const dim3 grid((unsigned)B * (unsigned)p.splits), block(256);
+hipError_t launch_decode(const DecodeParams& p, int segments, int query_group, bool paged, hipStream_t stream) {
+  const dim3 grid((unsigned)segments), block(256);
   if (query_group == 1) {
     if (paged) hipLaunchKernelGGL((splitkv_decode<1, true>), grid, block, 0, stream, p);
     else hipLaunchKernelGGL((splitkv_decode<1, false>), grid, block, 0, stream, p);

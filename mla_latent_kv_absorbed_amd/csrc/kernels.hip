@@ -1,13 +1,13 @@
-// The small kernels around the split-KV decode: query absorption, LSE
-// combine, W_UV up-projection, YaRN RoPE and the cache append.
+// The kernels around the split-KV decode: the per-call preparation (query
+// absorption, query RoPE, cache rows of the new tokens), the fused LSE
+// combine + W_UV up-projection, and the stand-alone YaRN RoPE and cache
+// append.
 //
 // Pages cited: "mHC+MLA+MTP 是什么？拆开给 Agent 用的百亿 MoE", MLA section
 // (kv_b_proj: latent -> per-head [k_nope | v]; kv_a_proj_with_mqa output
 // cached as latent + rope; YaRN rope) and "256K 长上下文真能本地用", §一
 // (rope_scaling fields, attention_bias false).
 #include "mla_internal.h"
-
-#include <algorithm>
 
 namespace mla {
 namespace {
@@ -35,45 +35,163 @@ __device__ __forceinline__ uint16_t f64_to_bf16(double d) {
   return (uint16_t)(__float_as_uint(f) >> 16);
 }
 
-// ---------------------------------------------------------------------------
-// Query absorption: Q_abs[r][0:512] = bf16(W_UK[h]^T q_nope[r]),
-// Q_abs[r][512:576] = q_pe[r], for rows r = (b, j, h).  The fp32 residual
-// q_lat - bf16(q_lat) is kept for the first-order LSE correction in the
-// up-projection kernel.
-// W_UK[h] = w_kv_b rows [h*256, h*256 + 128).  A workgroup covers (head,
-// 64-column block, 4 query rows): thread (ng, c8) loads the 4 x 8 weights
-// W_UK[h][4ng .. 4ng+3][c8*8 .. c8*8+7] as four 16-byte loads, forms the
-// partial dot products of its 4 rows over those 4 nope dims, and the 32
-// partials of each output are summed through LDS in a fixed order.
-// ---------------------------------------------------------------------------
-constexpr int kAbsorbRows = 4;
+// YaRN RoPE of one rotation pair (x_i, x_{i+half}) at angle pos * inv_freq_i:
+// cos/sin and the rotation in fp64, each result rounded once to bf16.
+__device__ __forceinline__ void rope_pair(uint16_t lo, uint16_t hi, double ang, uint16_t* out_lo,
+                                          uint16_t* out_hi) {
+#pragma clang fp contract(off)   // products and differences rounded separately, as written
+  double s, c;
+  sincos(ang, &s, &c);
+  const double a = (double)bf16_to_f32(lo), b = (double)bf16_to_f32(hi);
+  *out_lo = f64_to_bf16(a * c - b * s);
+  *out_hi = f64_to_bf16(b * c + a * s);
+}
 
-__global__ void __launch_bounds__(256) absorb_query(const uint16_t* __restrict__ q_nope,
-                                                     const uint16_t* __restrict__ q_pe,
-                                                     const uint16_t* __restrict__ w_kv_b,
-                                                     uint16_t* __restrict__ qabs,
-                                                     float* __restrict__ qres,
-                                                     uint8_t* __restrict__ zero_row, int rows_bs) {
-  __shared__ float red[kAbsorbRows][32][64];
-  const int cblk = blockIdx.x;          // 8 blocks of 64 latent columns
-  const int h = blockIdx.y;
-  const int r0 = blockIdx.z * kAbsorbRows;
+// Sum over a 256-thread workgroup (every thread gets the total).
+__device__ __forceinline__ int block_sum256(int v, int* red4) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+  if (lane == 0) red4[wv] = v;
+  __syncthreads();
+  const int r = red4[0] + red4[1] + red4[2] + red4[3];
+  __syncthreads();
+  return r;
+}
+
+// Inclusive prefix sum over a 256-thread workgroup; *total gets the sum.
+__device__ __forceinline__ int block_scan256(int v, int* red4, int* total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(v, d, 64);
+    if (lane >= d) v += y;
+  }
+  if (lane == 63) red4[wv] = v;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wv; ++w) before += red4[w];
+  *total = red4[0] + red4[1] + red4[2] + red4[3];
+  __syncthreads();
+  return v + before;
+}
+
+// The split schedule of one call, built by one 256-thread workgroup: splits
+// of c tiles, c fixed or chosen here so that the segments of all sequences
+// number at most target_segs where the lengths allow; then the first
+// segment of every sequence and the segment descriptors {b, first token, end
+// token, L_b} in sequence order.  Up to kSchedLds sequences, the lengths and
+// segment starts stay in LDS (`lds`, 2 * kSchedLds + 1 ints) and each
+// descriptor is found by binary search; larger batches take a serial path.
+constexpr int kSchedLds = 2048;
+
+__device__ void build_schedule(const PrepParams& p, int* lds) {
+  __shared__ int red4[4];
   const int t = threadIdx.x;
-  if (cblk == 0 && h == 0 && r0 == 0 && t < kChunksPerRow)   // the decode kernel's zero row
-    ((uint4*)zero_row)[t] = make_uint4(0, 0, 0, 0);
+  const bool in_lds = p.B <= kSchedLds;
+  int* lens = lds;                    // [kSchedLds]
+  int* starts = lds + kSchedLds;      // [kSchedLds + 1]
+  auto len_of = [&](int b) { return in_lds ? lens[b] : p.ctx_lens[b]; };
+  if (in_lds) {
+    for (int b = t; b < p.B; b += 256) lens[b] = p.ctx_lens[b];
+    __syncthreads();
+  }
+  int c = p.fixed_tiles;
+  if (c <= 0) {
+    int tsum = 0;
+    for (int b = t; b < p.B; b += 256) tsum += (len_of(b) + kPage - 1) / kPage;
+    const int T = block_sum256(tsum, red4);
+    c = max(kMinTilesPerSplit, (T + p.target_segs - 1) / p.target_segs);
+    for (int it = 0; it < 8; ++it) {   // the last split of each sequence is short: grow c until it fits
+      int n = 0;
+      for (int b = t; b < p.B; b += 256) n += ((len_of(b) + kPage - 1) / kPage + c - 1) / c;
+      n = block_sum256(n, red4);
+      if (n <= p.target_segs) break;
+      c = max(c + 1, (int)(((long long)c * n + p.target_segs - 1) / p.target_segs));
+    }
+  }
+  const int chunk = c * kPage;
+  int carry = 0;
+  for (int base = 0; base < p.B; base += 256) {
+    const int b = base + t;
+    const int L = (b < p.B) ? len_of(b) : 0;
+    const int n = (b < p.B) ? ((L + kPage - 1) / kPage + c - 1) / c : 0;
+    int total;
+    const int first = carry + block_scan256(n, red4, &total) - n;
+    if (b < p.B) {
+      p.seg_start[b] = min(first, p.max_segs);
+      if (in_lds) {
+        starts[b] = first;
+      } else {
+        for (int k = 0; k < n && first + k < p.max_segs; ++k)
+          p.seg_desc[first + k] = make_int4(b, k * chunk, min(L, (k + 1) * chunk), L);
+      }
+    }
+    carry += total;
+  }
+  if (t == 0) p.seg_start[p.B] = min(carry, p.max_segs);
+  if (in_lds) {
+    __syncthreads();
+    for (int w = t; w < min(carry, p.max_segs); w += 256) {
+      int lo = 0, hi = p.B - 1;          // last b with starts[b] <= w
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (starts[mid] <= w) lo = mid;
+        else hi = mid - 1;
+      }
+      const int k = w - starts[lo], L = lens[lo];
+      p.seg_desc[w] = make_int4(lo, k * chunk, min(L, (k + 1) * chunk), L);
+    }
+  }
+  for (int w = carry + t; w < p.max_segs; w += 256) p.seg_desc[w] = make_int4(-1, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Preparation of one decode call.  Grid (8 latent blocks of 64 + 1, 32
+// heads, query-row blocks of 4); row r = b*Sq + j.
+//  * Absorption: Q_abs[r][h][0:512] = bf16(W_UK[h]^T q_nope[r][h]) and the
+//    fp32 residual q_lat - bf16(q_lat) (for the first-order LSE correction).
+//    W_UK[h] = w_kv_b rows [h*256, h*256 + 128).  Thread (ng, c8) loads
+//    W_UK[h][4ng .. 4ng+3][c8*8 .. c8*8+7] as four 16-byte loads, forms the
+//    partial dot products of the block's 4 rows over those 4 nope dims, and
+//    the 32 partials of each output are summed through LDS in a fixed order.
+//  * Rope part: Q_abs[r][h][512:576] = q_pe[r][h], rotated at the query's
+//    position p = L_b - Sq + j when `rotate` is set (latent block 0).
+//  * New tokens (when c_new is given): cache row of token p of sequence b =
+//    [c_new[r] | rot(k_new[r], p)] (head 0 writes the latent, head 1 of
+//    latent block 0 the rope part).
+//  * Workgroup (8, 0, 0) zeroes the decode kernel's zero row and builds the
+//    split schedule (the other workgroups of that column exit at once).
+// ---------------------------------------------------------------------------
+constexpr int kPrepRows = 4;
+
+__global__ void __launch_bounds__(256) prep_query(PrepParams p) {
+  __shared__ float red[kPrepRows][32][64];
+  static_assert(sizeof(red) >= (2 * kSchedLds + 1) * sizeof(int), "schedule scratch");
+  const int cblk = blockIdx.x;
+  const int h = blockIdx.y;
+  const int r0 = blockIdx.z * kPrepRows;
+  const int t = threadIdx.x;
+  if (cblk == kLatent / 64) {           // the extra column: schedule and zero row
+    if (h == 0 && r0 == 0) {
+      if (t < kChunksPerRow) ((uint4*)p.zero_row)[t] = make_uint4(0, 0, 0, 0);
+      build_schedule(p, (int*)&red[0][0][0]);
+    }
+    return;
+  }
   const int c8 = t & 7, ng = t >> 3;
-  const uint16_t* wk = w_kv_b + ((size_t)h * kWRowsPerHead + 4 * ng) * kLatent + cblk * 64 + c8 * 8;
+  const uint16_t* wk = p.w_kv_b + ((size_t)h * kWRowsPerHead + 4 * ng) * kLatent + cblk * 64 + c8 * 8;
   uint4 w[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) w[k] = *(const uint4*)(wk + (size_t)k * kLatent);
-  uint2 q[kAbsorbRows];
+  uint2 q[kPrepRows];
 #pragma unroll
-  for (int rr = 0; rr < kAbsorbRows; ++rr) {
-    const int r = min(r0 + rr, rows_bs - 1);
-    q[rr] = *(const uint2*)(q_nope + ((size_t)r * kHeads + h) * kNope + 4 * ng);
+  for (int rr = 0; rr < kPrepRows; ++rr) {
+    const int r = min(r0 + rr, p.rows - 1);
+    q[rr] = *(const uint2*)(p.q_nope + ((size_t)r * kHeads + h) * kNope + 4 * ng);
   }
 #pragma unroll
-  for (int rr = 0; rr < kAbsorbRows; ++rr) {
+  for (int rr = 0; rr < kPrepRows; ++rr) {
     const float qv[4] = {__uint_as_float(q[rr].x << 16), __uint_as_float(q[rr].x & 0xFFFF0000u),
                          __uint_as_float(q[rr].y << 16), __uint_as_float(q[rr].y & 0xFFFF0000u)};
     float acc[8];
@@ -94,226 +212,195 @@ __global__ void __launch_bounds__(256) absorb_query(const uint16_t* __restrict__
   __syncthreads();
   const int rr = t >> 6, col = t & 63;
   const int r = r0 + rr;
-  if (r >= rows_bs) return;
+  if (r >= p.rows) return;
   float acc = 0.f;
 #pragma unroll
   for (int k = 0; k < 32; ++k) acc += red[rr][k][col];
-  const size_t row = (size_t)r * kHeads + h;
-  uint16_t* dst = qabs + row * kRow;
+  const size_t hrow = (size_t)r * kHeads + h;
+  uint16_t* dst = p.qabs + hrow * kRow;
   const uint16_t qb = f32_to_bf16(acc);
   dst[cblk * 64 + col] = qb;
-  qres[row * kLatent + cblk * 64 + col] = acc - bf16_to_f32(qb);
-  if (cblk == 0) dst[kLatent + col] = q_pe[row * kRope + col];   // the rope part, copied
+  p.qres[hrow * kLatent + cblk * 64 + col] = acc - bf16_to_f32(qb);
+
+  const int b = r / p.Sq;
+  const int pos = p.ctx_lens[b] - p.Sq + (r - b * p.Sq);
+  const int half = kRope / 2;
+  if (cblk == 0) {
+    const uint16_t* src = p.q_pe + hrow * kRope;
+    if (!p.rotate) {
+      dst[kLatent + col] = src[col];
+    } else if (col < half) {
+      uint16_t lo, hi;
+      rope_pair(src[col], src[col + half], (double)pos * p.inv.v[col], &lo, &hi);
+      dst[kLatent + col] = lo;
+      dst[kLatent + col + half] = hi;
+    }
+  }
+  if (p.c_new != nullptr && pos >= 0 && (h == 0 || (h == 1 && cblk == 0))) {
+    int64_t slot;
+    if (p.paged) slot = (int64_t)p.block_table[(size_t)b * p.max_pages + pos / kPage] * kPage + pos % kPage;
+    else slot = (int64_t)b * p.stride_tokens + pos;
+    uint16_t* crow = (uint16_t*)(p.cache + slot * kRowBytes);
+    if (h == 0) {
+      crow[cblk * 64 + col] = p.c_new[r * p.ld_c + cblk * 64 + col];
+    } else {
+      const uint16_t* src = p.k_new + r * p.ld_k;
+      if (!p.rotate) {
+        crow[kLatent + col] = src[col];
+      } else if (col < half) {
+        uint16_t lo, hi;
+        rope_pair(src[col], src[col + half], (double)pos * p.inv.v[col], &lo, &hi);
+        crow[kLatent + col] = lo;
+        crow[kLatent + col + half] = hi;
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
-// LSE combine of the split partials.  One workgroup per (sequence b, row
-// group of 16 rows, 16-column block); its waves take every W-th split
-// (W = waves in the workgroup), reading the partials in their own layout
-// (lane holds rows 4g..4g+3 of column n16) eight splits at a time, and keep
-// a running max per row.  The waves' results are merged in a fixed order,
-// so the combine is deterministic.
-//   o_lat[row] = sum_i 2^(lse_i - M) O_i / sum_i 2^(lse_i - M)
-//   lse2[row]  = M + log2 sum_i 2^(lse_i - M)   (log2 units)
-// A split whose rows see no token has lse_i = -inf and weight 0.
+// LSE combine of the split partials fused with the W_UV up-projection.
+// One workgroup of 1024 threads per head row (query row r, head h):
+//  1. its 8 groups of 128 lanes take every 8th of the sequence's segments
+//     (splits), 16 per batch
+//     with every load in flight, each lane 4 latent columns, and keep a
+//     running max; the groups are merged in a fixed order:
+//       o_lat = sum_i 2^(lse_i - M) O_i / sum_i 2^(lse_i - M)
+//     (a split whose row saw no token has lse_i = -inf and weight 0);
+//  2. out[v] = bf16(sum_c W_UV[h][v][c] o_lat[c]), W_UV[h] = w_kv_b rows
+//     [h*256 + 128, h*256 + 256): thread (v, e8) takes 64 columns and 8 lanes
+//     add their products;
+//  3. lse = ln 2 * (M + log2 sum_i 2^(lse_i - M) + scale_log2 * qres . o_lat).
+// Scores were taken with the bf16-rounded absorbed query; the exact score
+// differs by scale * (q_lat - bf16(q_lat)) . c_t, so to first order the LSE
+// moves by the softmax mean of that difference, scale * qres . o_lat.
 // ---------------------------------------------------------------------------
-constexpr int kCombineMaxWaves = 16;
-constexpr int kCombineBatch = 8;
+constexpr int kCombThreads = 1024;
+constexpr int kCombGroups = kCombThreads / 128;   // 8 split groups
+constexpr int kCombBatch = 16;
 
-__global__ void __launch_bounds__(1024) lse_combine(const float* __restrict__ part_o,
-                                                    const float* __restrict__ part_lse,
-                                                    const int32_t* __restrict__ ctx_lens, int Sq,
-                                                    int splits, int kv_chunk, float* __restrict__ o_lat,
-                                                    float* __restrict__ lse2_out) {
-  __shared__ f32x4 red_o[kCombineMaxWaves][64];
-  __shared__ f32x4 red_m[kCombineMaxWaves][4];
-  __shared__ f32x4 red_w[kCombineMaxWaves][4];
-  const int cbm = blockIdx.x;           // 32 column blocks of 16
-  const int rgg = blockIdx.y;           // row group in [0, 2*Sq)
-  const int b = blockIdx.z;
-  const int nw = blockDim.x >> 6;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int g = lane >> 4, n16 = lane & 15;
-  const int RGT = 2 * Sq;
-  const int L = ctx_lens[b];
-  const int nsplit = min(splits, (L + kv_chunk - 1) / kv_chunk);
-  const size_t lse_stride = (size_t)Sq * 32;
-  const float* lse_base = part_lse + (size_t)b * splits * lse_stride + rgg * 16 + 4 * g;
-  const float* o_base = part_o + (((size_t)b * splits * RGT + rgg) * 32 + cbm) * 256 + lane * 4;
-  const size_t o_stride = (size_t)RGT * 32 * 256;
+__global__ void __launch_bounds__(kCombThreads) combine_upproject(CombineParams p) {
+  __shared__ f32x4 red_acc[kCombGroups][128];
+  __shared__ float red_m[kCombGroups], red_w[kCombGroups];
+  __shared__ float olat[kLatent];
+  __shared__ float red_c[2];
+  const int h = blockIdx.x;
+  const int r = blockIdx.y;
+  const int b = r / p.Sq;
+  const int j = r - b * p.Sq;
+  const size_t hrow = (size_t)r * kHeads + h;
+  const int t = threadIdx.x;
+  const int grp = t >> 7, c4 = t & 127;
 
-  f32x4 m = f32x4{kNegInf, kNegInf, kNegInf, kNegInf};
-  f32x4 wsum = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int seg0 = p.seg_start[b];
+  const int nsplit = min(p.seg_start[b + 1], p.max_segs) - seg0;
+  const size_t unit_rows = (size_t)p.Sq * kHeads;
+  const float* obase = p.part_o + ((size_t)seg0 * unit_rows + j * kHeads + h) * kLatent + 4 * c4;
+  const float* lbase = p.part_lse + (size_t)seg0 * unit_rows + j * kHeads + h;
+  const size_t ostride = unit_rows * kLatent;
+  float4 qr = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (t < 128) qr = *(const float4*)(p.qres + hrow * kLatent + 4 * t);
+
+  float m = kNegInf, wsum = 0.f;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int s0 = wave; s0 < nsplit; s0 += nw * kCombineBatch) {
-    f32x4 l4[kCombineBatch], o4[kCombineBatch];
+  for (int s0 = grp; s0 < nsplit; s0 += kCombGroups * kCombBatch) {
+    float l[kCombBatch];
+    f32x4 o4[kCombBatch];
 #pragma unroll
-    for (int k = 0; k < kCombineBatch; ++k) {
-      const int s = min(s0 + k * nw, nsplit - 1);   // past the end: re-read, weight 0 below
-      l4[k] = *(const f32x4*)(lse_base + s * lse_stride);
-      o4[k] = *(const f32x4*)(o_base + s * o_stride);
+    for (int k = 0; k < kCombBatch; ++k) {
+      const int s = min(s0 + k * kCombGroups, nsplit - 1);   // past the end: re-read, weight 0 below
+      l[k] = lbase[s * unit_rows];
+      o4[k] = *(const f32x4*)(obase + s * ostride);
     }
     __builtin_amdgcn_sched_barrier(0);   // every load of the batch in flight before the first use
 #pragma unroll
-    for (int k = 0; k < kCombineBatch; ++k)
-      if (s0 + k * nw >= nsplit) l4[k] = f32x4{kNegInf, kNegInf, kNegInf, kNegInf};
+    for (int k = 0; k < kCombBatch; ++k)
+      if (s0 + k * kCombGroups >= nsplit) l[k] = kNegInf;
+    float bm = m;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float bm = m[i];
+    for (int k = 0; k < kCombBatch; ++k) bm = fmaxf(bm, l[k]);
+    const float sc = (m == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m - bm);
+    wsum *= sc;
 #pragma unroll
-      for (int k = 0; k < kCombineBatch; ++k) bm = fmaxf(bm, l4[k][i]);
-      const float sc = (m[i] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m[i] - bm);
-      wsum[i] *= sc;
-      acc[i] *= sc;
-      m[i] = bm;
+    for (int i = 0; i < 4; ++i) acc[i] *= sc;
+    m = bm;
 #pragma unroll
-      for (int k = 0; k < kCombineBatch; ++k) {
-        const float wt = (l4[k][i] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(l4[k][i] - bm);
-        wsum[i] += wt;
-        acc[i] = fmaf(wt, o4[k][i], acc[i]);
-      }
+    for (int k = 0; k < kCombBatch; ++k) {
+      const float wt = (l[k] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(l[k] - bm);
+      wsum += wt;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = fmaf(wt, o4[k][i], acc[i]);
     }
   }
-  red_o[wave][lane] = acc;
-  if (n16 == 0) {
-    red_m[wave][g] = m;
-    red_w[wave][g] = wsum;
+  // W_UV[h][v][64*e8 .. 64*e8 + 64): thread (v, e8), requested before the merge
+  const int v = t >> 3, e8 = t & 7;
+  const uint16_t* wrow = p.w_kv_b + ((size_t)h * kWRowsPerHead + kNope + v) * kLatent + 64 * e8;
+  uint4 wu[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) wu[k] = *(const uint4*)(wrow + 8 * k);
+
+  red_acc[grp][c4] = acc;
+  if (c4 == 0) {
+    red_m[grp] = m;
+    red_w[grp] = wsum;
   }
   __syncthreads();
-  if (wave != 0) return;
-  f32x4 M = red_m[0][g];
-  for (int w = 1; w < nw; ++w) {
-    const f32x4 t = red_m[w][g];
+  float M = red_m[0];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) M[i] = fmaxf(M[i], t[i]);
-  }
-  f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f}, ws = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int w = 0; w < nw; ++w) {
-    const f32x4 tm = red_m[w][g], tw = red_w[w][g], to = red_o[w][lane];
+  for (int g2 = 1; g2 < kCombGroups; ++g2) M = fmaxf(M, red_m[g2]);
+  float W = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float sc = (tm[i] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(tm[i] - M[i]);
-      ws[i] = fmaf(tw[i], sc, ws[i]);
-      o[i] = fmaf(to[i], sc, o[i]);
+  for (int g2 = 0; g2 < kCombGroups; ++g2)
+    W = fmaf(red_w[g2], (red_m[g2] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(red_m[g2] - M), W);
+  if (t < 128) {
+    f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int g2 = 0; g2 < kCombGroups; ++g2) {
+      const float sc = (red_m[g2] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(red_m[g2] - M);
+      const f32x4 a = red_acc[g2][t];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = fmaf(a[i], sc, o[i]);
     }
+    const float inv = (W > 0.f) ? 1.f / W : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] *= inv;
+    *(f32x4*)(olat + 4 * t) = o;
+    // qres . o_lat: waves 0 and 1, one partial each
+    float c = qr.x * o[0];
+    c = fmaf(qr.y, o[1], c);
+    c = fmaf(qr.z, o[2], c);
+    c = fmaf(qr.w, o[3], c);
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) c += __shfl_xor(c, d, 64);
+    if ((t & 63) == 0) red_c[t >> 6] = c;
   }
-  const int j = rgg >> 1;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 4 * g + i;
-    const int h = (rgg & 1) * 16 + r;
-    const size_t row = ((size_t)b * Sq + j) * kHeads + h;
-    o_lat[row * kLatent + cbm * 16 + n16] = (ws[i] > 0.f) ? o[i] / ws[i] : 0.f;
-    if (cbm == 0 && n16 == 0) lse2_out[row] = (ws[i] > 0.f) ? M[i] + __log2f(ws[i]) : kNegInf;
-  }
-}
+  __syncthreads();
 
-// ---------------------------------------------------------------------------
-// W_UV up-projection: out[r][v] = bf16(sum_c W_UV[h][v][c] o_lat[r][c]),
-// W_UV[h] = w_kv_b rows [h*256 + 128, h*256 + 256).  A workgroup covers
-// (head, 16 output dims, 4 query rows); 16 lanes split each 512-long dot
-// product, and every load of the workgroup is issued before the first FMA.
-//
-// The workgroup of output block 0 also writes the natural-log LSE.  Scores
-// were taken with the bf16-rounded absorbed query; the exact score differs
-// by scale * (q_lat - bf16(q_lat)) . c_t, so to first order the LSE moves by
-// the softmax mean of that difference, scale * qres . o_lat.
-// ---------------------------------------------------------------------------
-constexpr int kUpRows = 4;
-
-__global__ void __launch_bounds__(256) upproject(const float* __restrict__ o_lat,
-                                                 const uint16_t* __restrict__ w_kv_b,
-                                                 const float* __restrict__ qres,
-                                                 const float* __restrict__ lse2, float scale_log2,
-                                                 uint16_t* __restrict__ out, float* __restrict__ lse,
-                                                 int rows_bs) {
-  const int vblk = blockIdx.x;          // 8 blocks of 16 output dims
-  const int h = blockIdx.y;
-  const int r0 = blockIdx.z * kUpRows;
-  const int vl = threadIdx.x >> 4;
-  const int v = vblk * 16 + vl;
-  const int part = threadIdx.x & 15;    // columns [part*32, part*32 + 32)
-  const uint16_t* wrow = w_kv_b + ((size_t)h * kWRowsPerHead + kNope + v) * kLatent + part * 32;
-  // workgroups of output block 0 also finish the LSE: lanes of output dim vl
-  // take row r0 + (vl & 3)
-  const bool lse_wg = (lse != nullptr) && vblk == 0;
-  const int rc = r0 + (vl & (kUpRows - 1));
-  const size_t crow = (size_t)min(rc, rows_bs - 1) * kHeads + h;
-
-  uint4 wu[4];
-  float4 x[kUpRows][8];
-  float4 qr[8];
-  float l2 = 0.f;
+  float up = 0.f;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) wu[k] = *(const uint4*)(wrow + 8 * k);
-#pragma unroll
-  for (int rr = 0; rr < kUpRows; ++rr) {
-    const size_t row = (size_t)min(r0 + rr, rows_bs - 1) * kHeads + h;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) x[rr][k] = *(const float4*)(o_lat + row * kLatent + part * 32 + 4 * k);
-  }
-  if (lse_wg) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) qr[k] = *(const float4*)(qres + crow * kLatent + part * 32 + 4 * k);
-    l2 = lse2[crow];
-  }
-  __builtin_amdgcn_sched_barrier(0);   // every load in flight before the first use
-
-  float w[32];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < 8; ++k) {
     const uint32_t wd[4] = {wu[k].x, wu[k].y, wu[k].z, wu[k].w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      w[8 * k + 2 * e] = __uint_as_float(wd[e] << 16);
-      w[8 * k + 2 * e + 1] = __uint_as_float(wd[e] & 0xFFFF0000u);
+      const int c = 64 * e8 + 8 * k + 2 * e;
+      up = fmaf(__uint_as_float(wd[e] << 16), olat[c], up);
+      up = fmaf(__uint_as_float(wd[e] & 0xFFFF0000u), olat[c + 1], up);
     }
   }
-#pragma unroll
-  for (int rr = 0; rr < kUpRows; ++rr) {
-    float acc = 0.f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      acc = fmaf(w[4 * k], x[rr][k].x, acc);
-      acc = fmaf(w[4 * k + 1], x[rr][k].y, acc);
-      acc = fmaf(w[4 * k + 2], x[rr][k].z, acc);
-      acc = fmaf(w[4 * k + 3], x[rr][k].w, acc);
-    }
-#pragma unroll
-    for (int d = 8; d >= 1; d >>= 1) acc += __shfl_xor(acc, d, 16);
-    const int r = r0 + rr;
-    if (part == 0 && r < rows_bs) out[((size_t)r * kHeads + h) * kVDim + v] = f32_to_bf16(acc);
-  }
-  if (lse_wg) {
-    float corr = 0.f;
-#pragma unroll
-    for (int rr = 0; rr < kUpRows; ++rr) {
-      float c = 0.f;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        c = fmaf(qr[k].x, x[rr][k].x, c);
-        c = fmaf(qr[k].y, x[rr][k].y, c);
-        c = fmaf(qr[k].z, x[rr][k].z, c);
-        c = fmaf(qr[k].w, x[rr][k].w, c);
-      }
-      corr = ((vl & (kUpRows - 1)) == rr) ? c : corr;
-    }
-#pragma unroll
-    for (int d = 8; d >= 1; d >>= 1) corr += __shfl_xor(corr, d, 16);
-    if (part == 0 && vl < kUpRows && rc < rows_bs)
-      lse[crow] = (l2 == kNegInf) ? kNegInf : (l2 + scale_log2 * corr) * 0.69314718055994530942f;
+  up += __shfl_xor(up, 1, 8);
+  up += __shfl_xor(up, 2, 8);
+  up += __shfl_xor(up, 4, 8);
+  if (e8 == 0) p.out[hrow * kVDim + v] = f32_to_bf16(up);
+  if (t == 0 && p.lse != nullptr) {
+    const float corr = red_c[0] + red_c[1];
+    p.lse[hrow] = (W > 0.f) ? (M + __log2f(W) + p.scale_log2 * corr) * 0.69314718055994530942f : kNegInf;
   }
 }
 
 // ---------------------------------------------------------------------------
 // YaRN RoPE: pair (i, i + rope_dim/2) of row r rotated by
-// positions[r] * inv_freq[i], in fp64, rounded once to bf16.  Each thread
-// reads and writes only its own pair, so dst may equal src.
+// positions[r] * inv_freq[i].  Each thread reads and writes only its own
+// pair, so dst may equal src.
 // ---------------------------------------------------------------------------
-struct InvFreq {
-  double v[32];
-};
-
 __global__ void __launch_bounds__(256) rope_rotate(const uint16_t* src, int64_t ld_src,
                                                    uint16_t* dst, int64_t ld_dst,
                                                    const int32_t* __restrict__ positions, int64_t n,
@@ -324,15 +411,10 @@ __global__ void __launch_bounds__(256) rope_rotate(const uint16_t* src, int64_t 
   const int i = (int)(idx - r * half);
   const uint16_t* in = src + r * ld_src;
   uint16_t* o = dst + r * ld_dst;
-  const double ang = (double)positions[r] * inv.v[i];
-  double s, c;
-  sincos(ang, &s, &c);
-  const double lo = (double)bf16_to_f32(in[i]);
-  const double hi = (double)bf16_to_f32(in[i + half]);
-  const uint16_t out_lo = f64_to_bf16(lo * c - hi * s);
-  const uint16_t out_hi = f64_to_bf16(hi * c + lo * s);
-  o[i] = out_lo;
-  o[i + half] = out_hi;
+  uint16_t lo, hi;
+  rope_pair(in[i], in[i + half], (double)positions[r] * inv.v[i], &lo, &hi);
+  o[i] = lo;
+  o[i + half] = hi;
 }
 
 // ---------------------------------------------------------------------------
@@ -355,30 +437,15 @@ __global__ void __launch_bounds__(256) cache_append(uint8_t* __restrict__ cache,
 
 }  // namespace
 
-hipError_t launch_absorb(const uint16_t* q_nope, const uint16_t* q_pe, const uint16_t* w_kv_b,
-                         uint16_t* qabs, float* qres, uint8_t* zero_row, int rows, hipStream_t stream) {
-  const unsigned rb = (unsigned)((rows + kAbsorbRows - 1) / kAbsorbRows);
-  hipLaunchKernelGGL(absorb_query, dim3(kLatent / 64, kHeads, rb), dim3(256), 0, stream, q_nope, q_pe,
-                     w_kv_b, qabs, qres, zero_row, rows);
+hipError_t launch_prep(const PrepParams& p, hipStream_t stream) {
+  const unsigned rb = (unsigned)((p.rows + kPrepRows - 1) / kPrepRows);
+  hipLaunchKernelGGL(prep_query, dim3(kLatent / 64 + 1, kHeads, rb), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const float* part_o, const float* part_lse, const int32_t* ctx_lens,
-                          int B, int Sq, int splits, int kv_chunk, float* o_lat, float* lse2,
-                          hipStream_t stream) {
-  // enough waves that each takes about a batch of splits, at most 16
-  const int waves = std::min(kCombineMaxWaves, std::max(1, (splits + kCombineBatch - 1) / kCombineBatch));
-  hipLaunchKernelGGL(lse_combine, dim3(32, 2 * Sq, B), dim3(64 * waves), 0, stream, part_o, part_lse,
-                     ctx_lens, Sq, splits, kv_chunk, o_lat, lse2);
-  return hipGetLastError();
-}
-
-hipError_t launch_upproj(const float* o_lat, const uint16_t* w_kv_b, const float* qres,
-                         const float* lse2, float scale_log2, uint16_t* out, float* lse, int rows,
-                         hipStream_t stream) {
-  const unsigned rb = (unsigned)((rows + kUpRows - 1) / kUpRows);
-  hipLaunchKernelGGL(upproject, dim3(kVDim / 16, kHeads, rb), dim3(256), 0, stream, o_lat, w_kv_b,
-                     qres, lse2, scale_log2, out, lse, rows);
+hipError_t launch_combine_upproject(const CombineParams& p, hipStream_t stream) {
+  const unsigned rows = (unsigned)(p.hrows / kHeads);
+  hipLaunchKernelGGL(combine_upproject, dim3(kHeads, rows), dim3(kCombThreads), 0, stream, p);
   return hipGetLastError();
 }
 

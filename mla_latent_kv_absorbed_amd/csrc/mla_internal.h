@@ -27,33 +27,51 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
+// Split schedule.  A sequence's cached tokens are cut into splits of `c`
+// tiles (64 tokens each); every split is one segment, processed by one
+// workgroup of the split-KV kernel.  Segments are numbered sequence by
+// sequence; seg_start[b] is the first segment of sequence b and
+// seg_start[B] the count.  With a fixed kv_chunk, c = kv_chunk / 64; with
+// kv_chunk = 0 the preparation kernel chooses c on the device from the
+// actual context lengths so that all sequences together give about one
+// segment per compute unit (never below kMinTilesPerSplit tiles).
+constexpr int kMinTilesPerSplit = 4;
+
 // Workspace layout of one decode call (byte offsets, each 256-aligned).
+// rows = B * Sq query tokens; a "head row" is one (query token, head).
 struct WorkspaceLayout {
-  size_t qabs;      // bf16 [B][Sq][32][576]: [W_UK^T q_nope | q_pe]
-  size_t qres;      // fp32 [B][Sq][32][512]: W_UK^T q_nope - bf16(W_UK^T q_nope)
-  size_t part_o;    // fp32 [B][splits][2*Sq][32 col blocks][64 lanes][4]
-  size_t part_lse;  // fp32 [B][splits][Sq*32], log2 domain
-  size_t o_lat;     // fp32 [B][Sq][32][512]
-  size_t lse2;      // fp32 [B][Sq][32], combined LSE in log2 units before correction
+  size_t qabs;      // bf16 [rows][32][576]: [W_UK^T q_nope | rotated q_pe]
+  size_t qres;      // fp32 [rows][32][512]: W_UK^T q_nope - bf16(W_UK^T q_nope)
+  size_t part_o;    // fp32 [max_segs][Sq*32][512]: normalised segment partials
+  size_t part_lse;  // fp32 [max_segs][Sq*32], log2 domain
+  size_t seg_desc;  // int4 [max_segs]: {b, first token, end token, L_b}; b = -1: none
+  size_t seg_start; // int32 [B + 1]
   size_t zero_row;  // 1152 zero bytes: stand-in source for cache rows past a split's end
   size_t total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-inline WorkspaceLayout workspace_layout(int B, int Sq, int splits) {
+inline WorkspaceLayout workspace_layout(int B, int Sq, int max_segs) {
   WorkspaceLayout w;
+  const size_t seq_rows = size_t(Sq) * kHeads;
+  const size_t hrows = size_t(B) * seq_rows;
   size_t off = 0;
-  w.qabs = off;     off = align256(off + size_t(B) * Sq * kHeads * kRow * 2);
-  w.qres = off;     off = align256(off + size_t(B) * Sq * kHeads * kLatent * 4);
-  w.part_o = off;   off = align256(off + size_t(B) * splits * Sq * kHeads * kLatent * 4);
-  w.part_lse = off; off = align256(off + size_t(B) * splits * Sq * kHeads * 4);
-  w.o_lat = off;    off = align256(off + size_t(B) * Sq * kHeads * kLatent * 4);
-  w.lse2 = off;     off = align256(off + size_t(B) * Sq * kHeads * 4);
-  w.zero_row = off; off = align256(off + kRowBytes);
+  w.qabs = off;      off = align256(off + hrows * kRow * 2);
+  w.qres = off;      off = align256(off + hrows * kLatent * 4);
+  w.part_o = off;    off = align256(off + size_t(max_segs) * seq_rows * kLatent * 4);
+  w.part_lse = off;  off = align256(off + size_t(max_segs) * seq_rows * 4);
+  w.seg_desc = off;  off = align256(off + size_t(max_segs) * 16);
+  w.seg_start = off; off = align256(off + (size_t(B) + 1) * 4);
+  w.zero_row = off;  off = align256(off + kRowBytes);
   w.total = off;
   return w;
 }
+
+// YaRN inverse frequencies of the 32 rotation pairs, passed by value.
+struct InvFreq {
+  double v[32];
+};
 
 struct DecodeParams {
   const uint16_t* qabs;         // bf16 [B][Sq][32][576]
@@ -61,27 +79,67 @@ struct DecodeParams {
   int64_t stride_tokens;        // contiguous layout: tokens per sequence block
   const int32_t* block_table;   // paged layout: [B][max_pages]
   int32_t max_pages;
-  const int32_t* ctx_lens;      // [B]
+  const int4* seg_desc;         // one per workgroup
   int32_t Sq;                   // query tokens per sequence
   int32_t j0;                   // first query token of this pass
-  int32_t kv_chunk;             // tokens per split (multiple of 64)
-  int32_t splits;               // splits per sequence (grid.x / B)
   float scale_log2;             // softmax_scale * log2(e)
   float* part_o;
   float* part_lse;
   const uint8_t* zero_row;      // kRowBytes zero bytes
 };
 
+// Everything that precedes the split-KV pass: the absorbed query rows, the
+// rope part of the query (copied, or rotated at p = L_b - Sq + j), the cache
+// rows of the new tokens (optional), the split schedule and the decode
+// kernel's zero row.
+struct PrepParams {
+  const uint16_t* q_nope;       // bf16 [rows][32][128]
+  const uint16_t* q_pe;         // bf16 [rows][32][64]
+  const uint16_t* w_kv_b;       // bf16 [8192][512]
+  uint16_t* qabs;
+  float* qres;
+  uint8_t* zero_row;
+  int32_t rows;                 // B * Sq
+  int32_t B;
+  int32_t Sq;
+  const int32_t* ctx_lens;
+  int32_t rotate;               // q_pe and k_new are rotated here when non-zero
+  InvFreq inv;
+  const uint16_t* c_new;        // bf16 [rows][ld_c] latent rows of the new tokens, or null
+  int64_t ld_c;
+  const uint16_t* k_new;        // bf16 [rows][ld_k] rope rows of the new tokens
+  int64_t ld_k;
+  uint8_t* cache;
+  int64_t stride_tokens;
+  const int32_t* block_table;
+  int32_t max_pages;
+  int32_t paged;
+  // split schedule
+  int32_t fixed_tiles;          // tiles per split, or 0: balance on the device
+  int32_t target_segs;          // balanced: aim at no more segments than this
+  int32_t max_segs;             // capacity of seg_desc / part_o
+  int4* seg_desc;
+  int32_t* seg_start;
+};
+
+struct CombineParams {
+  const float* part_o;
+  const float* part_lse;
+  const int32_t* seg_start;
+  int32_t max_segs;
+  int32_t Sq;
+  int32_t hrows;                // rows * 32
+  const uint16_t* w_kv_b;
+  const float* qres;
+  float scale_log2;
+  uint16_t* out;                // bf16 [rows][32][128]
+  float* lse;                   // fp32 [rows][32] or null
+};
+
 // Launchers (each enqueues on `stream`; return hipError_t of the launch).
-hipError_t launch_decode(const DecodeParams& p, int B, int query_group, bool paged, hipStream_t stream);
-hipError_t launch_absorb(const uint16_t* q_nope, const uint16_t* q_pe, const uint16_t* w_kv_b,
-                         uint16_t* qabs, float* qres, uint8_t* zero_row, int rows, hipStream_t stream);
-hipError_t launch_combine(const float* part_o, const float* part_lse, const int32_t* ctx_lens,
-                          int B, int Sq, int splits, int kv_chunk, float* o_lat, float* lse2,
-                          hipStream_t stream);
-hipError_t launch_upproj(const float* o_lat, const uint16_t* w_kv_b, const float* qres,
-                         const float* lse2, float scale_log2, uint16_t* out, float* lse, int rows,
-                         hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, int segments, int query_group, bool paged, hipStream_t stream);
+hipError_t launch_prep(const PrepParams& p, hipStream_t stream);
+hipError_t launch_combine_upproject(const CombineParams& p, hipStream_t stream);
 hipError_t launch_rope(const uint16_t* src, int64_t ld_src, uint16_t* dst, int64_t ld_dst,
                        const int32_t* positions, int64_t n, const double* inv_freq, int rope_dim,
                        hipStream_t stream);

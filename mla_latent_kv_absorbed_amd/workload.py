@@ -6,7 +6,9 @@ device memory, the rope keys of all cached tokens are rotated by
 (contiguous [B, stride, 576] or paged [pages, 64, 576]) by
 ``mla_cache_append``.  A decode step of one layer then runs the whole path on
 the Sq new tokens of every sequence: RoPE of their query and key rope parts,
-append of their cache rows, and ``mla_decode`` / ``mla_decode_paged``.
+append of their cache rows and the decode, either fused in one
+``mla_decode_step`` call (``step``) or as ``mla_rope_yarn``,
+``mla_cache_append`` and ``mla_decode`` / ``mla_decode_paged`` (``step_unfused``).
 """
 from __future__ import annotations
 
@@ -18,7 +20,7 @@ import synth
 import synth.gpu as sgpu
 from synth.configs import Workload
 
-from . import (mla_cache_append, mla_decode, mla_decode_paged, mla_decode_workspace_size,
+from . import (mla_cache_append, mla_decode, mla_decode_paged, mla_decode_step, mla_decode_workspace_size,
                mla_decode_auto_chunk, mla_rope_yarn)
 
 BF16_NAN = 0x7FC1   # bit pattern written into unused cache slots when poisoning
@@ -126,17 +128,30 @@ class DeviceWorkload:
     # ---- one decode step of one layer (the whole hot path)
     def step(self, li: LayerInputs, out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
              kv_chunk: int | None = None):
+        """The fused step: one library call rotates, appends and decodes."""
+        chunk = self.kv_chunk if kv_chunk is None else kv_chunk
+        ws = self._workspace(chunk)
+        return mla_decode_step(li.q_nope, li.q_pe_raw, li.new_c, li.new_kpe_raw, li.w_kv_b, li.cache,
+                               self.ctx_lens, self.max_ctx, chunk, block_table=self.block_table,
+                               out=out, lse=lse, workspace=ws)
+
+    def step_unfused(self, li: LayerInputs, out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                     kv_chunk: int | None = None):
+        """The same step as separate calls: RoPE of q and of the new keys, append, decode."""
         mla_rope_yarn(li.q_pe_raw, self.q_pos, dst=li.q_pe)
         mla_rope_yarn(li.new_kpe_raw, self.new_pos, dst=li.new_kpe)
         mla_cache_append(li.cache, li.new_c, li.new_kpe, self.new_slots)
         return self.decode(li, out, lse, kv_chunk)
 
+    def _workspace(self, chunk: int) -> torch.Tensor:
+        need = mla_decode_workspace_size(self.B, self.Sq, self.max_ctx, chunk)
+        if need > self.workspace.numel():
+            self.workspace = torch.empty(need, dtype=torch.uint8, device=self.dev)
+        return self.workspace
+
     def decode(self, li: LayerInputs, out=None, lse=None, kv_chunk: int | None = None):
         chunk = self.kv_chunk if kv_chunk is None else kv_chunk
-        ws = self.workspace
-        need = mla_decode_workspace_size(self.B, self.Sq, self.max_ctx, chunk)
-        if need > ws.numel():
-            ws = torch.empty(need, dtype=torch.uint8, device=self.dev)
+        ws = self._workspace(chunk)
         if self.paged:
             return mla_decode_paged(li.q_nope, li.q_pe, li.w_kv_b, li.cache, self.block_table, self.ctx_lens,
                                     self.max_ctx, chunk, out=out, lse=lse, workspace=ws)

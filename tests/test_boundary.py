@@ -104,13 +104,20 @@ def test_append_and_rope_argument_errors():
 
 
 def test_workspace_size_and_auto_chunk():
-    assert M.mla_decode_auto_chunk(1, 1, 32768) % 64 == 0
+    # Without a GPU the library assumes 256 compute units: the balanced
+    # schedule aims at one split per unit and never below 4 tiles (256 tokens).
+    assert M.mla_decode_auto_chunk(1, 1, 32768) == 256
+    assert M.mla_decode_auto_chunk(1, 1, 262144) == 1024
+    assert M.mla_decode_auto_chunk(16, 1, 65536) == 4096
     for B, Sq, L in [(1, 1, 1024), (1, 1, 32768), (16, 1, 65536), (1, 1, 262144), (32, 2, 131072), (3, 5, 100)]:
         chunk = M.mla_decode_auto_chunk(B, Sq, L)
-        assert chunk % 64 == 0 and chunk >= 128
-        splits = -(-L // chunk)
+        assert chunk % 64 == 0 and chunk >= 256
+        assert B * -(-L // chunk) <= 256 or chunk == 256
+        # partials for up to 256 + B segments, plus the query rows
         need = M.mla_decode_workspace_size(B, Sq, L)
-        assert need >= B * Sq * 32 * (576 * 2 + 512 * 4) + B * splits * Sq * 32 * 513 * 4
+        assert need >= B * Sq * 32 * (576 * 2 + 512 * 4) + (256 + B) * Sq * 32 * 513 * 4
+        fixed = M.mla_decode_workspace_size(B, Sq, L, kv_chunk=128)
+        assert fixed >= B * Sq * 32 * (576 * 2 + 512 * 4) + B * -(-L // 128) * Sq * 32 * 513 * 4
     with pytest.raises(M.MlaError):
         M.mla_decode_workspace_size(1, 1, 100, kv_chunk=65)
     # an empty batch needs no workspace and must not trip the split heuristic

@@ -239,3 +239,55 @@ def test_score_jump_beyond_headroom_takes_the_second_pass(sq):
     ref_o, ref_l = O.mla_attention_unabsorbed(qn, qp, c, k, weights(wl.seed, 0), O.softmax_scale())
     assert (ref_l.max() - np.median(ref_l)) * 1.4427 > 64     # the jump really exceeds the headroom
     compare(gpu_out(out[0]), lse[0].cpu().numpy(), ref_o, ref_l)
+
+
+FUSED = [
+    (1, (1, 65, 700)),
+    (2, (2, 130, 64)),
+    (3, (3, 200)),
+]
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("sq,lens", FUSED)
+def test_fused_step_equals_separate_calls_bitwise(paged, sq, lens):
+    # mla_decode_step (RoPE + append + decode in one call) against
+    # mla_rope_yarn + mla_cache_append + mla_decode.  The new tokens' cache
+    # rows are poisoned first, so only the step's own append can fill them.
+    wl = Workload(96, "fused", len(lens), sq, 1, lens, True)
+    res = []
+    for fused in (True, False):
+        dw = DeviceWorkload(wl, paged=paged, kv_chunk=64)
+        li = dw.build_layer(1)
+        li.cache.view(torch.int16).view(-1, 576)[dw.new_slots] = 0x7FC1
+        lse = torch.empty((len(lens), sq, 32), dtype=torch.float32, device=DEV)
+        out, lse = (dw.step if fused else dw.step_unfused)(li, lse=lse)
+        torch.cuda.synchronize()
+        valid = torch.cat([dw.slots_of(torch.full((L,), b, dtype=torch.int64, device=DEV),
+                                       torch.arange(L, dtype=torch.int64, device=DEV))
+                           for b, L in enumerate(lens)])
+        res.append((bits(out), lse.cpu().numpy().copy(), bits(li.cache.view(-1, 576)[valid])))
+    np.testing.assert_array_equal(res[0][2], res[1][2])   # every cached row of every sequence
+    np.testing.assert_array_equal(res[0][0], res[1][0])
+    np.testing.assert_array_equal(res[0][1], res[1][1])
+    go = O.bf16_bits_to_float(res[0][0]).reshape(len(lens), sq, 32, 128)
+    for b, L in enumerate(lens):
+        ref_o, ref_l = expected(wl.seed, 1, L, sq, b)
+        compare(go[b], res[0][1][b], ref_o, ref_l)
+
+
+def test_balanced_schedule_over_many_short_sequences():
+    # 300 sequences: the device-side schedule scans the lengths in two
+    # 256-wide passes; every tenth sequence is checked against the oracle.
+    rng = np.random.default_rng(7)
+    lens = tuple(int(x) for x in rng.integers(1, 200, 300))
+    wl = Workload(97, "many", len(lens), 1, 1, lens, True)
+    dw = DeviceWorkload(wl, paged=True, kv_chunk=0)
+    li = dw.build_layer(0)
+    lse = torch.empty((len(lens), 1, 32), dtype=torch.float32, device=DEV)
+    out, lse = dw.step(li, lse=lse)
+    torch.cuda.synchronize()
+    go, gl = gpu_out(out), lse.cpu().numpy()
+    for b in range(0, len(lens), 10):
+        ref_o, ref_l = expected(wl.seed, 0, lens[b], 1, b)
+        compare(go[b], gl[b], ref_o, ref_l)
