@@ -16,7 +16,10 @@ Output: one JSON line.  "value" is decode tokens/s (batch * query tokens per
 step / step time, timed over --steps replays of a HIP graph of the step).
 "roofline" covers the split-KV kernel: algorithmic latent bytes per launch
 (1152 B per visible cached token) over its average duration, measured with
-HIP events recorded by the library on the launch stream.
+HIP events that the kernel dispatches record themselves (hipExtLaunchKernel)
+on the stream they run on; "traffic" is the HBM bytes per launch from the
+committed rocprofv3 FETCH_SIZE / WRITE_SIZE counters of the same kernel
+source on the same workload, scaled by a calibration copy (else null).
 """
 from __future__ import annotations
 
@@ -132,7 +135,13 @@ def run_workload(k: int, steps: int, warmup: int, use_graph: bool, kv_chunk=None
 
 
 def cpu_baseline(k: int, budget_s: float = 15.0):
-    """The un-absorbed oracle on the host: layer 0 of workload k, a head subset."""
+    """The un-absorbed fp64 oracle on the host cores, on a bounded sample of workload k.
+
+    Sample: sequence 0, all 32 heads over its full context, layer after layer
+    (each layer with its own inputs and kv_b_proj) until about budget_s of
+    oracle time; the time per layer scales to one step (all layers, all
+    sequences of the same length).  Input generation is not timed.
+    """
     import numpy as np
     import threadpoolctl
     import oracle as O
@@ -143,36 +152,95 @@ def cpu_baseline(k: int, budget_s: float = 15.0):
     L, Sq, seed = wl.lens[0], wl.sq, wl.seed
     f = O.bf16_bits_to_float
     inv = O.yarn_inv_freq()
-    c = f(synth.latent_bits(seed, 0, 0, 0, L))
-    kk = O.round_to_bf16(O.rope_rotate(f(synth.kpe_bits(seed, 0, 0, 0, L)), np.arange(L), inv))
-    qn = f(synth.qnope_bits(seed, 0, 0, Sq))
-    qp = O.round_to_bf16(O.rope_rotate(f(synth.qpe_bits(seed, 0, 0, Sq)), (L - Sq + np.arange(Sq))[:, None], inv))
-    w = f(synth.wkvb_bits(seed, 0))
     scale = O.softmax_scale()
-    t0 = time.perf_counter()
-    O.mla_attention_unabsorbed(qn, qp, c, kk, w, scale, heads=[0])
-    one = time.perf_counter() - t0
-    nheads = int(max(1, min(32, budget_s // max(one, 1e-3))))
-    t0 = time.perf_counter()
-    O.mla_attention_unabsorbed(qn, qp, c, kk, w, scale, heads=list(range(nheads)))
-    dt = time.perf_counter() - t0
-    step_s = dt * (32 / nheads) * wl.layers
+    layers, spent = 0, 0.0
+    while layers < wl.layers and spent < budget_s:
+        c = f(synth.latent_bits(seed, layers, 0, 0, L))
+        kk = O.round_to_bf16(O.rope_rotate(f(synth.kpe_bits(seed, layers, 0, 0, L)), np.arange(L), inv))
+        qn = f(synth.qnope_bits(seed, layers, 0, Sq))
+        qp = O.round_to_bf16(O.rope_rotate(f(synth.qpe_bits(seed, layers, 0, Sq)),
+                                           (L - Sq + np.arange(Sq))[:, None], inv))
+        w = f(synth.wkvb_bits(seed, layers))
+        t0 = time.perf_counter()
+        O.mla_attention_unabsorbed(qn, qp, c, kk, w, scale)
+        spent += time.perf_counter() - t0
+        layers += 1
+    per_layer = spent / layers
+    step_s = per_layer * wl.layers * wl.batch
     threads = sum(p.get("num_threads", 0) for p in threadpoolctl.threadpool_info() if p.get("user_api") == "blas")
     return {"value": wl.batch * Sq / step_s, "unit": "tokens/s", "cores": threads or os.cpu_count(),
             "kind": "oracle",
-            "sample": (f"un-absorbed fp64 oracle, layer 0, heads 0..{nheads - 1} of 32, full {L}-token "
-                       f"context, {dt:.1f}s; scaled x{32 / nheads:g} (heads) x{wl.layers} (layers) to one step")}
+            "sample": (f"un-absorbed fp64 oracle, sequence 0 of {wl.name}, all 32 heads over the full {L}-token "
+                       f"context, layers 0..{layers - 1}: {spent:.1f} s; {per_layer:.2f} s per layer scaled by "
+                       f"{wl.layers} layers x {wl.batch} sequence(s) to one step")}
 
 
-def traffic_from_counters(bytes_per_launch):
-    """HBM bytes per launch from committed rocprofv3 counters, if they match this kernel source."""
+def traffic_from_counters(workload_name: str):
+    """HBM bytes per split-KV launch from committed rocprofv3 counters, if they were taken on
+    this workload with this kernel source (else None)."""
     if not os.path.exists(COUNTERS):
         return None
     with open(COUNTERS) as fh:
         c = json.load(fh)
-    if c.get("source_hash") != source_hash():
+    if c.get("source_hash") != source_hash() or c.get("workload") != workload_name:
         return None
-    return c.get("bytes_per_launch")
+    return c.get("kernels", {}).get("splitkv_decode", {}).get("hbm_bytes_per_launch")
+
+
+def _counter_rows(path):
+    import csv
+    out = {}
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            name = r.get("Kernel_Name", "")
+            out.setdefault((r["Counter_Name"], name), []).append(float(r["Counter_Value"]))
+    return out
+
+
+def summarize_counters(fetch_csv: str, write_csv: str, copy_bytes: int, workload_name: str, command: str):
+    """Writes profiles/splitkv_decode_counters.json from two rocprofv3 --pmc runs (FETCH_SIZE, then
+    WRITE_SIZE, KiB per dispatch).  Each counter is scaled by what it reads for the calibration copy
+    of copy_bytes bytes (the runtime's buffer-copy kernel) in the same run."""
+    import statistics
+    res = {"workload": workload_name, "source_hash": source_hash(), "command": command,
+           "copy_bytes": copy_bytes, "kernels": {}}
+    per = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _counter_rows(path)
+        copy = [v for (cn, kn), vals in rows.items() if cn == counter and "copyBuffer" in kn for v in vals]
+        copy_kib = max(copy) if copy else None      # the calibration copy is the largest buffer copy
+        scale = (copy_bytes / 1024.0) / copy_kib if copy_kib else None
+        res[f"{counter}_copy_kib"] = copy_kib
+        res[f"{counter}_scale"] = scale
+        for short, key in (("splitkv_decode", "splitkv_decode"), ("combine_upproject", "combine_upproject"),
+                           ("prep_query", "prep_query")):
+            vals = [v for (cn, kn), vs in rows.items() if cn == counter and key in kn for v in vs]
+            if vals:
+                kib = statistics.mean(vals)
+                per.setdefault(short, {})[counter] = {"kib_per_dispatch": kib, "dispatches": len(vals),
+                                                       "bytes_scaled": kib * 1024.0 * scale if scale else None}
+    for short, d in per.items():
+        f, w = d.get("FETCH_SIZE", {}), d.get("WRITE_SIZE", {})
+        tot = None
+        if f.get("bytes_scaled") is not None and w.get("bytes_scaled") is not None:
+            tot = f["bytes_scaled"] + w["bytes_scaled"]
+        res["kernels"][short] = {"fetch": f, "write": w, "hbm_bytes_per_launch": tot}
+    with open(COUNTERS, "w") as fh:
+        json.dump(res, fh, indent=1)
+    print(json.dumps(res, indent=1))
+
+
+def copy_calibration(nbytes: int):
+    """A plain device-to-device copy of nbytes, three times (a known-size reference for counters)."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+    torch.cuda.empty_cache()
 
 
 def main():
@@ -184,7 +252,17 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-256k", action="store_true", help="skip the 256K report")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="first copy this many MiB device-to-device 3 times (reference for rocprofv3 counters)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/splitkv_decode_counters.json from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--counters-command", default="", help="command line recorded with --summarize-counters")
     args = ap.parse_args()
+    if args.summarize_counters:
+        from synth.configs import workload
+        summarize_counters(args.summarize_counters[0], args.summarize_counters[1],
+                           args.copy_calibration_mb << 20, workload(args.config).name, args.counters_command)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path",
               file=sys.stderr)
@@ -192,6 +270,8 @@ def main():
 
     import torch
     torch.cuda.init()
+    if args.copy_calibration_mb:
+        copy_calibration(args.copy_calibration_mb << 20)
     main_res = run_workload(args.config, args.steps, args.warmup, not args.no_graph, label=f"config{args.config}")
     log(f"[config{args.config}] {json.dumps(main_res)}")
     extra = None
@@ -225,7 +305,7 @@ def main():
         "latent_gbps_step": main_res["step_latent_gbps"],
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic_from_counters(bpl),
+            "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic_from_counters(main_res["workload"]),
             "kernel": "splitkv_decode", "bytes_per_launch": bpl, "avg_launch_us": main_res["kernel_avg_us"],
         },
         "cpu_baseline": cpu,

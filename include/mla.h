@@ -206,9 +206,10 @@ mla_status mla_decode_workspace_size(const mla_shape* shape /* host */, int32_t 
 mla_status mla_decode_auto_chunk(int32_t B, int32_t Sq, int32_t max_ctx_len, int32_t* kv_chunk /* host */);
 
 /* Kernel timing, a profiling aid (not needed to compute anything).
- * After mla_timing_enable(n), each of the next n decode calls records a HIP
- * event pair on its stream around its split-KV attention kernel(s); calls
- * beyond n are not timed.  mla_timing_collect() waits for the recorded
+ * After mla_timing_enable(n), each of the next n decode calls has its
+ * split-KV attention kernel(s) record a HIP event pair themselves, at the
+ * start of the first and the end of the last launch; calls beyond n are not
+ * timed.  mla_timing_collect() waits for the recorded
  * events and returns the summed kernel time in milliseconds and the number
  * of timed kernel launches; mla_timing_disable() releases the events.  This
  * is the library's only global state: enable it outside HIP graph capture,

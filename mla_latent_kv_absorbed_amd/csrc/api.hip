@@ -208,16 +208,15 @@ mla_status decode_common(const mla_shape* shape, const StepInputs& step, const v
   p.part_lse = (float*)(ws + wl.part_lse);
   p.zero_row = zero_row;
   const bool timed = g_timing.on && g_timing.used < g_timing.capacity;
-  if (timed && hipEventRecord(g_timing.ev[2 * g_timing.used], s) != hipSuccess) return MLA_ERR_DEVICE;
   for (int j0 = 0; j0 < Sq; j0 += kMaxQueryGroup) {
     const int qg = (Sq - j0 >= 2) ? 2 : 1;
+    const bool first = j0 == 0, last = j0 + qg >= Sq;
+    hipEvent_t ev0 = (timed && first) ? g_timing.ev[2 * g_timing.used] : nullptr;
+    hipEvent_t ev1 = (timed && last) ? g_timing.ev[2 * g_timing.used + 1] : nullptr;
     p.j0 = j0;
-    if (launch_decode(p, (int)segs, qg, paged, s) != hipSuccess) return MLA_ERR_DEVICE;
+    if (launch_decode(p, (int)segs, qg, paged, s, ev0, ev1) != hipSuccess) return MLA_ERR_DEVICE;
   }
-  if (timed) {
-    if (hipEventRecord(g_timing.ev[2 * g_timing.used + 1], s) != hipSuccess) return MLA_ERR_DEVICE;
-    ++g_timing.used;
-  }
+  if (timed) ++g_timing.used;
 
   CombineParams cp;
   cp.part_o = p.part_o;

@@ -44,6 +44,8 @@
 //    accumulated by MFMAs, zeroed, or written to LDS after the loop.
 #include "mla_internal.h"
 
+#include <hip/hip_ext.h>
+
 namespace mla {
 namespace {
 
@@ -391,14 +393,16 @@ __global__ void __launch_bounds__(256, 1) splitkv_decode(DecodeParams p) {
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeParams& p, int segments, int query_group, bool paged, hipStream_t stream) {
+hipError_t launch_decode(const DecodeParams& p, int segments, int query_group, bool paged, hipStream_t stream,
+                         hipEvent_t ev_start, hipEvent_t ev_stop) {
   const dim3 grid((unsigned)segments), block(256);
+  // with events, the dispatch itself records them at kernel start and end
   if (query_group == 1) {
-    if (paged) hipLaunchKernelGGL((splitkv_decode<1, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((splitkv_decode<1, false>), grid, block, 0, stream, p);
+    if (paged) hipExtLaunchKernelGGL((splitkv_decode<1, true>), grid, block, 0, stream, ev_start, ev_stop, 0, p);
+    else hipExtLaunchKernelGGL((splitkv_decode<1, false>), grid, block, 0, stream, ev_start, ev_stop, 0, p);
   } else {
-    if (paged) hipLaunchKernelGGL((splitkv_decode<2, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((splitkv_decode<2, false>), grid, block, 0, stream, p);
+    if (paged) hipExtLaunchKernelGGL((splitkv_decode<2, true>), grid, block, 0, stream, ev_start, ev_stop, 0, p);
+    else hipExtLaunchKernelGGL((splitkv_decode<2, false>), grid, block, 0, stream, ev_start, ev_stop, 0, p);
   }
   return hipGetLastError();
 }

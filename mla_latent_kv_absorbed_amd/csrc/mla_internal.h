@@ -137,7 +137,10 @@ struct CombineParams {
 };
 
 // Launchers (each enqueues on `stream`; return hipError_t of the launch).
-hipError_t launch_decode(const DecodeParams& p, int segments, int query_group, bool paged, hipStream_t stream);
+// ev_start / ev_stop (may be null): recorded by the dispatches themselves at
+// the start of the first and the end of the last split-KV launch.
+hipError_t launch_decode(const DecodeParams& p, int segments, int query_group, bool paged, hipStream_t stream,
+                         hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_prep(const PrepParams& p, hipStream_t stream);
 hipError_t launch_combine_upproject(const CombineParams& p, hipStream_t stream);
 hipError_t launch_rope(const uint16_t* src, int64_t ld_src, uint16_t* dst, int64_t ld_dst,
