@@ -230,6 +230,9 @@ mla_status decode_common(const mla_shape* shape, const StepInputs& step, const v
   cp.scale_log2 = scale_log2;
   cp.out = (uint16_t*)out;
   cp.lse = lse;
+  cp.up_part = (float*)(ws + wl.up_part);
+  cp.corr_part = (float*)(ws + wl.corr_part);
+  cp.stat = (float*)(ws + wl.stat);
   if (launch_combine_upproject(cp, s) != hipSuccess) return MLA_ERR_DEVICE;
   return MLA_OK;
 }

@@ -13,8 +13,8 @@
 // segment record {b, first token, end token, L_b} of the call's schedule):
 //  * The split streams through LDS in 64-token slots (one page, 72 KiB) of a
 //    two-slot ring, filled by direct global->LDS 16-byte loads: while the
-//    waves consume one slot the next is in flight, and the first slot is
-//    requested before anything else.  Slot rows are swizzled at 16-byte
+//    waves consume one slot the next is in flight, and the first two slots
+//    are requested before anything else.  Slot rows are swizzled at 16-byte
 //    granularity (latent chunk c of token t sits at c ^ (t & 15), rope chunk
 //    64+k at 64 + (k ^ ((t >> 1) & 7))) so that both read patterns below are
 //    free of LDS bank conflicts.
@@ -56,7 +56,6 @@ constexpr int kPvRing = 6;             // value operand column blocks in flight 
 constexpr int kSlotTok = 64;           // tokens per ring slot (one page)
 constexpr int kSlotBytes = kSlotTok * kRowBytes;   // 73728
 constexpr int kSlots = 2;              // ring slots: kSlots - 1 in flight while one is consumed
-constexpr int kAhead = kSlots - 1;
 constexpr int kLoadsPerLane = kSlotBytes / 16 / 256;   // 18
 
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
@@ -161,8 +160,9 @@ __global__ void __launch_bounds__(256, 1) splitkv_decode(DecodeParams p) {
     }
   };
 
-  // The first slots are requested before the query rows are read.
-  const int pro = min(kAhead, nslot);
+  // The first two slots (both ring positions) are requested before the query
+  // rows are read.
+  const int pro = min(kSlots, nslot);
   for (int k = 0; k < pro; ++k) issue(s0 + k, k);
 
   // The wave's 16 query rows, as MFMA B operands: lane holds row n16, 8 dims.
@@ -316,14 +316,16 @@ __global__ void __launch_bounds__(256, 1) splitkv_decode(DecodeParams p) {
 
   // Slot loop.  Iteration it: wait for slot it (its loads and everyone
   // else's, via the barrier, which also frees the slot consumed at it - 1),
-  // request slot it + kAhead into that freed ring position, consume slot it.
+  // request slot it + 1 into that freed ring position (slot 1 came with the
+  // prologue), consume slot it.  Only while slot 0 is awaited can a later
+  // slot's loads be outstanding.
   // A second pass runs only if some row outgrew its reference by kTau.
   int pass = 0;
   for (;;) {
     for (int it = 0; it < nslot; ++it) {
-      wait_slots_ahead<kLoadsPerLane>(min(nslot, it + kAhead) - (it + 1));
+      wait_slots_ahead<kLoadsPerLane>((it == 0 && nslot > 1) ? 1 : 0);
       lds_barrier();
-      if (it + kAhead < nslot) issue(s0 + it + kAhead, (it + kAhead) % kSlots);
+      if (it >= 1 && it + 1 < nslot) issue(s0 + it + 1, (it + 1) % kSlots);
       process(ring + (it % kSlots) * kSlotBytes, s0 + it);
     }
     lds_barrier();   // every wave is done with the last slot

@@ -258,63 +258,67 @@ __global__ void __launch_bounds__(256) prep_query(PrepParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// LSE combine of the split partials fused with the W_UV up-projection.
-// One workgroup of 1024 threads per head row (query row r, head h):
-//  1. its 8 groups of 128 lanes take every 8th of the sequence's segments
-//     (splits), 16 per batch
-//     with every load in flight, each lane 4 latent columns, and keep a
-//     running max; the groups are merged in a fixed order:
-//       o_lat = sum_i 2^(lse_i - M) O_i / sum_i 2^(lse_i - M)
-//     (a split whose row saw no token has lse_i = -inf and weight 0);
-//  2. out[v] = bf16(sum_c W_UV[h][v][c] o_lat[c]), W_UV[h] = w_kv_b rows
-//     [h*256 + 128, h*256 + 256): thread (v, e8) takes 64 columns and 8 lanes
-//     add their products;
-//  3. lse = ln 2 * (M + log2 sum_i 2^(lse_i - M) + scale_log2 * qres . o_lat).
-// Scores were taken with the bf16-rounded absorbed query; the exact score
-// differs by scale * (q_lat - bf16(q_lat)) . c_t, so to first order the LSE
-// moves by the softmax mean of that difference, scale * qres . o_lat.
+// LSE combine of the segment partials with this column block's share of the
+// W_UV up-projection.  Grid (8 latent blocks of 64 columns, 32 heads, rows);
+// a workgroup of 256 threads handles head row (r, h) on columns
+// [64 cb, 64 cb + 64):
+//  1. its 16 groups of 16 lanes take every 16th of the sequence's segments,
+//     16 per batch with every load in flight, each lane 4 columns, and keep
+//     a running max; the groups are merged in a fixed order:
+//       o_lat = sum_i 2^(lse_i - M) O_i / W,   W = sum_i 2^(lse_i - M)
+//     (a segment whose row saw no token has lse_i = -inf and weight 0);
+//  2. share[v] = sum over the block's columns of W_UV[h][v][c] o_lat[c]
+//     (W_UV[h] = w_kv_b rows [h*256 + 128, h*256 + 256)) and the block's share
+//     of qres . o_lat go to the workspace; block 0 also stores (M, W).
+// finalize_out then adds the 8 shares in block order.
 // ---------------------------------------------------------------------------
-constexpr int kCombThreads = 1024;
-constexpr int kCombGroups = kCombThreads / 128;   // 8 split groups
+constexpr int kCombGroups = 16;
 constexpr int kCombBatch = 16;
 
-__global__ void __launch_bounds__(kCombThreads) combine_upproject(CombineParams p) {
-  __shared__ f32x4 red_acc[kCombGroups][128];
+__global__ void __launch_bounds__(256) combine_blocks(CombineParams p) {
+  __shared__ f32x4 red_acc[kCombGroups][16];
   __shared__ float red_m[kCombGroups], red_w[kCombGroups];
-  __shared__ float olat[kLatent];
-  __shared__ float red_c[2];
-  const int h = blockIdx.x;
-  const int r = blockIdx.y;
+  __shared__ float olat[64];
+  const int cb = blockIdx.x;
+  const int h = blockIdx.y;
+  const int r = blockIdx.z;
   const int b = r / p.Sq;
   const int j = r - b * p.Sq;
   const size_t hrow = (size_t)r * kHeads + h;
   const int t = threadIdx.x;
-  const int grp = t >> 7, c4 = t & 127;
+  const int grp = t >> 4, c4 = t & 15;
+
+  // W_UV[h][v][64 cb + 32 half .. + 32): thread (v, half), requested first
+  const int v = t >> 1, half = t & 1;
+  const uint16_t* wrow = p.w_kv_b + ((size_t)h * kWRowsPerHead + kNope + v) * kLatent + cb * 64 + 32 * half;
+  uint4 wu[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) wu[k] = *(const uint4*)(wrow + 8 * k);
+  float4 qr = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (t < 16) qr = *(const float4*)(p.qres + hrow * kLatent + cb * 64 + 4 * t);
 
   const int seg0 = p.seg_start[b];
-  const int nsplit = min(p.seg_start[b + 1], p.max_segs) - seg0;
+  const int nseg = min(p.seg_start[b + 1], p.max_segs) - seg0;
   const size_t unit_rows = (size_t)p.Sq * kHeads;
-  const float* obase = p.part_o + ((size_t)seg0 * unit_rows + j * kHeads + h) * kLatent + 4 * c4;
+  const float* obase = p.part_o + ((size_t)seg0 * unit_rows + j * kHeads + h) * kLatent + cb * 64 + 4 * c4;
   const float* lbase = p.part_lse + (size_t)seg0 * unit_rows + j * kHeads + h;
   const size_t ostride = unit_rows * kLatent;
-  float4 qr = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (t < 128) qr = *(const float4*)(p.qres + hrow * kLatent + 4 * t);
 
   float m = kNegInf, wsum = 0.f;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int s0 = grp; s0 < nsplit; s0 += kCombGroups * kCombBatch) {
+  for (int s0 = grp; s0 < nseg; s0 += kCombGroups * kCombBatch) {
     float l[kCombBatch];
     f32x4 o4[kCombBatch];
 #pragma unroll
     for (int k = 0; k < kCombBatch; ++k) {
-      const int s = min(s0 + k * kCombGroups, nsplit - 1);   // past the end: re-read, weight 0 below
+      const int s = min(s0 + k * kCombGroups, nseg - 1);   // past the end: re-read, weight 0 below
       l[k] = lbase[s * unit_rows];
       o4[k] = *(const f32x4*)(obase + s * ostride);
     }
     __builtin_amdgcn_sched_barrier(0);   // every load of the batch in flight before the first use
 #pragma unroll
     for (int k = 0; k < kCombBatch; ++k)
-      if (s0 + k * kCombGroups >= nsplit) l[k] = kNegInf;
+      if (s0 + k * kCombGroups >= nseg) l[k] = kNegInf;
     float bm = m;
 #pragma unroll
     for (int k = 0; k < kCombBatch; ++k) bm = fmaxf(bm, l[k]);
@@ -331,67 +335,86 @@ __global__ void __launch_bounds__(kCombThreads) combine_upproject(CombineParams 
       for (int i = 0; i < 4; ++i) acc[i] = fmaf(wt, o4[k][i], acc[i]);
     }
   }
-  // W_UV[h][v][64*e8 .. 64*e8 + 64): thread (v, e8), requested before the merge
-  const int v = t >> 3, e8 = t & 7;
-  const uint16_t* wrow = p.w_kv_b + ((size_t)h * kWRowsPerHead + kNope + v) * kLatent + 64 * e8;
-  uint4 wu[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) wu[k] = *(const uint4*)(wrow + 8 * k);
-
   red_acc[grp][c4] = acc;
   if (c4 == 0) {
     red_m[grp] = m;
     red_w[grp] = wsum;
   }
   __syncthreads();
-  float M = red_m[0];
+  if (t < 64) {   // wave 0: merge the groups, this block's o_lat and share of qres . o_lat
+    float M = red_m[0];
 #pragma unroll
-  for (int g2 = 1; g2 < kCombGroups; ++g2) M = fmaxf(M, red_m[g2]);
-  float W = 0.f;
-#pragma unroll
-  for (int g2 = 0; g2 < kCombGroups; ++g2)
-    W = fmaf(red_w[g2], (red_m[g2] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(red_m[g2] - M), W);
-  if (t < 128) {
+    for (int g2 = 1; g2 < kCombGroups; ++g2) M = fmaxf(M, red_m[g2]);
+    float W = 0.f;
     f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int g2 = 0; g2 < kCombGroups; ++g2) {
       const float sc = (red_m[g2] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(red_m[g2] - M);
-      const f32x4 a = red_acc[g2][t];
+      W = fmaf(red_w[g2], sc, W);
+      const f32x4 a = red_acc[g2][t & 15];
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[i] = fmaf(a[i], sc, o[i]);
     }
     const float inv = (W > 0.f) ? 1.f / W : 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] *= inv;
-    *(f32x4*)(olat + 4 * t) = o;
-    // qres . o_lat: waves 0 and 1, one partial each
-    float c = qr.x * o[0];
-    c = fmaf(qr.y, o[1], c);
-    c = fmaf(qr.z, o[2], c);
-    c = fmaf(qr.w, o[3], c);
+    float c = 0.f;
+    if (t < 16) {
+      *(f32x4*)(olat + 4 * t) = o;
+      c = qr.x * o[0];
+      c = fmaf(qr.y, o[1], c);
+      c = fmaf(qr.z, o[2], c);
+      c = fmaf(qr.w, o[3], c);
+    }
 #pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) c += __shfl_xor(c, d, 64);
-    if ((t & 63) == 0) red_c[t >> 6] = c;
+    for (int d = 8; d >= 1; d >>= 1) c += __shfl_xor(c, d, 16);
+    if (t == 0) {
+      p.corr_part[hrow * 8 + cb] = c;
+      if (cb == 0) {
+        p.stat[2 * hrow] = M;
+        p.stat[2 * hrow + 1] = W;
+      }
+    }
   }
   __syncthreads();
 
   float up = 0.f;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
+  for (int k = 0; k < 4; ++k) {
     const uint32_t wd[4] = {wu[k].x, wu[k].y, wu[k].z, wu[k].w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int c = 64 * e8 + 8 * k + 2 * e;
+      const int c = 32 * half + 8 * k + 2 * e;
       up = fmaf(__uint_as_float(wd[e] << 16), olat[c], up);
       up = fmaf(__uint_as_float(wd[e] & 0xFFFF0000u), olat[c + 1], up);
     }
   }
-  up += __shfl_xor(up, 1, 8);
-  up += __shfl_xor(up, 2, 8);
-  up += __shfl_xor(up, 4, 8);
-  if (e8 == 0) p.out[hrow * kVDim + v] = f32_to_bf16(up);
-  if (t == 0 && p.lse != nullptr) {
-    const float corr = red_c[0] + red_c[1];
+  up += __shfl_xor(up, 1, 2);
+  if (half == 0) p.up_part[(hrow * 8 + cb) * kVDim + v] = up;
+}
+
+// ---------------------------------------------------------------------------
+// out[r][h][v] = bf16(sum over the 8 latent blocks of their W_UV shares), in
+// block order; lse = ln 2 * (M + log2 W + scale_log2 * sum of the blocks'
+// qres . o_lat).  Scores were taken with the bf16-rounded absorbed query; the
+// exact score differs by scale * (q_lat - bf16(q_lat)) . c_t, so to first
+// order the LSE moves by the softmax mean of that difference,
+// scale * qres . o_lat.  Two head rows per 256-thread workgroup.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) finalize_out(CombineParams p) {
+  const size_t hrow = (size_t)blockIdx.x * 2 + (threadIdx.x >> 7);
+  const int v = threadIdx.x & 127;
+  if (hrow >= (size_t)p.hrows) return;
+  const float* u = p.up_part + hrow * 8 * kVDim + v;
+  float sum = 0.f;
+#pragma unroll
+  for (int cb = 0; cb < 8; ++cb) sum += u[cb * kVDim];
+  p.out[hrow * kVDim + v] = f32_to_bf16(sum);
+  if (v == 0 && p.lse != nullptr) {
+    float corr = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) corr += p.corr_part[hrow * 8 + cb];
+    const float M = p.stat[2 * hrow], W = p.stat[2 * hrow + 1];
     p.lse[hrow] = (W > 0.f) ? (M + __log2f(W) + p.scale_log2 * corr) * 0.69314718055994530942f : kNegInf;
   }
 }
@@ -445,7 +468,9 @@ hipError_t launch_prep(const PrepParams& p, hipStream_t stream) {
 
 hipError_t launch_combine_upproject(const CombineParams& p, hipStream_t stream) {
   const unsigned rows = (unsigned)(p.hrows / kHeads);
-  hipLaunchKernelGGL(combine_upproject, dim3(kHeads, rows), dim3(kCombThreads), 0, stream, p);
+  hipLaunchKernelGGL(combine_blocks, dim3(kLatent / 64, kHeads, rows), dim3(256), 0, stream, p);
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  hipLaunchKernelGGL(finalize_out, dim3((unsigned)((p.hrows + 1) / 2)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

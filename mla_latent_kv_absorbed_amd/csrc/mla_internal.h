@@ -35,7 +35,7 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 // kv_chunk = 0 the preparation kernel chooses c on the device from the
 // actual context lengths so that all sequences together give about one
 // segment per compute unit (never below kMinTilesPerSplit tiles).
-constexpr int kMinTilesPerSplit = 4;
+constexpr int kMinTilesPerSplit = 2;
 
 // Workspace layout of one decode call (byte offsets, each 256-aligned).
 // rows = B * Sq query tokens; a "head row" is one (query token, head).
@@ -46,6 +46,9 @@ struct WorkspaceLayout {
   size_t part_lse;  // fp32 [max_segs][Sq*32], log2 domain
   size_t seg_desc;  // int4 [max_segs]: {b, first token, end token, L_b}; b = -1: none
   size_t seg_start; // int32 [B + 1]
+  size_t up_part;   // fp32 [rows*32][8][128]: W_UV shares of the 8 latent blocks
+  size_t corr_part; // fp32 [rows*32][8]
+  size_t stat;      // fp32 [rows*32][2]
   size_t zero_row;  // 1152 zero bytes: stand-in source for cache rows past a split's end
   size_t total;
 };
@@ -63,6 +66,9 @@ inline WorkspaceLayout workspace_layout(int B, int Sq, int max_segs) {
   w.part_lse = off;  off = align256(off + size_t(max_segs) * seq_rows * 4);
   w.seg_desc = off;  off = align256(off + size_t(max_segs) * 16);
   w.seg_start = off; off = align256(off + (size_t(B) + 1) * 4);
+  w.up_part = off;   off = align256(off + hrows * 8 * kVDim * 4);
+  w.corr_part = off; off = align256(off + hrows * 8 * 4);
+  w.stat = off;      off = align256(off + hrows * 2 * 4);
   w.zero_row = off;  off = align256(off + kRowBytes);
   w.total = off;
   return w;
@@ -134,6 +140,9 @@ struct CombineParams {
   float scale_log2;
   uint16_t* out;                // bf16 [rows][32][128]
   float* lse;                   // fp32 [rows][32] or null
+  float* up_part;               // fp32 [rows*32][8][128]: W_UV shares of the 8 latent blocks
+  float* corr_part;             // fp32 [rows*32][8]: qres . o_lat shares
+  float* stat;                  // fp32 [rows*32][2]: combined (M, W), log2 domain
 };
 
 // Launchers (each enqueues on `stream`; return hipError_t of the launch).

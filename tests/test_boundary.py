@@ -105,14 +105,14 @@ def test_append_and_rope_argument_errors():
 
 def test_workspace_size_and_auto_chunk():
     # Without a GPU the library assumes 256 compute units: the balanced
-    # schedule aims at one split per unit and never below 4 tiles (256 tokens).
-    assert M.mla_decode_auto_chunk(1, 1, 32768) == 256
+    # schedule aims at one split per unit and never below 2 tiles (128 tokens).
+    assert M.mla_decode_auto_chunk(1, 1, 32768) == 128
     assert M.mla_decode_auto_chunk(1, 1, 262144) == 1024
     assert M.mla_decode_auto_chunk(16, 1, 65536) == 4096
     for B, Sq, L in [(1, 1, 1024), (1, 1, 32768), (16, 1, 65536), (1, 1, 262144), (32, 2, 131072), (3, 5, 100)]:
         chunk = M.mla_decode_auto_chunk(B, Sq, L)
-        assert chunk % 64 == 0 and chunk >= 256
-        assert B * -(-L // chunk) <= 256 or chunk == 256
+        assert chunk % 64 == 0 and chunk >= 128
+        assert B * -(-L // chunk) <= 256 or chunk == 128
         # partials for up to 256 + B segments, plus the query rows
         need = M.mla_decode_workspace_size(B, Sq, L)
         assert need >= B * Sq * 32 * (576 * 2 + 512 * 4) + (256 + B) * Sq * 32 * 513 * 4
