@@ -178,6 +178,85 @@ def paged_slot(block_table_row: np.ndarray, t: np.ndarray, page_size: int = PAGE
 
 
 # ---------------------------------------------------------------------------
+# 8-bit latent cache.  [KV-ledger §三] (plan A) keeps the KV cache in 8 bits
+# (llama.cpp's q8_0), which halves its bytes against bf16 at a small cost in
+# long-context accuracy.  The pages fix neither the number format nor the
+# scale granularity; readings: OCP FP8 E4M3 codes (sign, 4 exponent bits with
+# bias 7, 3 mantissa bits, no infinities, code 0x7F / 0xFF = NaN, largest
+# finite value 448), one fp32 scale per group of 128 latent values of a token
+# (scale = group max |x| / 448, computed in fp32), and the rope key kept in
+# bf16.  A token's fp8 row is [512 codes | 4 fp32 scales | 64 bf16 rope key]
+# = 656 bytes.
+# ---------------------------------------------------------------------------
+E4M3_MAX = 448.0
+FP8_GROUP = 128
+FP8_ROW_BYTES = KV_LORA_RANK + 4 * (KV_LORA_RANK // FP8_GROUP) + 2 * QK_ROPE_HEAD_DIM   # 656
+
+
+def e4m3_value(code: np.ndarray) -> np.ndarray:
+    """fp64 value of E4M3 codes: (-1)^s * 2^(e-7) * (1 + m/8) for e > 0,
+    (-1)^s * 2^-6 * m/8 for e = 0; NaN for exponent and mantissa all ones."""
+    c = np.asarray(code, dtype=np.int64)
+    s = (c >> 7) & 1
+    e = (c >> 3) & 15
+    m = c & 7
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(s == 1, -mag, mag)
+
+
+def round_to_e4m3(x: np.ndarray) -> np.ndarray:
+    """E4M3 code of the representable value nearest to each x (|x| <= 448),
+    ties to the code with an even mantissa; the sign bit follows x's sign."""
+    x = np.asarray(x, dtype=np.float64)
+    if np.any(np.abs(x) > E4M3_MAX):
+        raise ValueError("round_to_e4m3 takes |x| <= 448")
+    grid = e4m3_value(np.arange(0, 0x7F))            # codes 0x00..0x7E, increasing
+    a = np.abs(x)
+    hi = np.clip(np.searchsorted(grid, a, side="left"), 0, len(grid) - 1)
+    lo = np.clip(hi - 1, 0, len(grid) - 1)
+    d_lo, d_hi = a - grid[lo], grid[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.int64)
+    return (code | (np.signbit(x).astype(np.int64) << 7)).astype(np.uint8)
+
+
+def quantize_latent_fp8(c_kv: np.ndarray):
+    """codes uint8 [..., 512] and fp32 scales [..., 4] of latent rows.
+
+    Per group of 128 values, in fp32 as the cache writer does it: amax = max |x|,
+    scale = amax / 448, code = e4m3(clamp(x / scale, -448, 448)); a group of
+    zeros gets scale 0 and codes 0.
+    """
+    x = np.asarray(c_kv, dtype=np.float32)
+    g = x.reshape(x.shape[:-1] + (-1, FP8_GROUP))
+    amax = np.abs(g).max(axis=-1)
+    scale = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1.0))
+    y = (g / safe[..., None]).astype(np.float32)
+    y = np.clip(y, -np.float32(E4M3_MAX), np.float32(E4M3_MAX))
+    y = np.where(scale[..., None] > 0, y, np.float32(0.0))
+    codes = round_to_e4m3(y.astype(np.float64)).reshape(x.shape)
+    return codes, scale
+
+
+def dequantize_latent_fp8(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """fp64 latent values code * scale (exact in fp64)."""
+    v = e4m3_value(codes).reshape(np.shape(codes)[:-1] + (-1, FP8_GROUP))
+    return (v * np.asarray(scales, dtype=np.float64)[..., None]).reshape(np.shape(codes))
+
+
+def fp8_cache_row_bytes(codes: np.ndarray, scales: np.ndarray, k_pe_bits: np.ndarray) -> np.ndarray:
+    """Bytes of fp8 cache rows [512 codes | 4 fp32 scales | 64 bf16 rope key] (656 per token)."""
+    n = np.shape(codes)[0]
+    out = np.empty((n, FP8_ROW_BYTES), dtype=np.uint8)
+    out[:, :KV_LORA_RANK] = codes
+    out[:, KV_LORA_RANK:KV_LORA_RANK + 16] = np.asarray(scales, dtype="<f4").view(np.uint8).reshape(n, 16)
+    out[:, KV_LORA_RANK + 16:] = np.asarray(k_pe_bits, dtype="<u2").view(np.uint8).reshape(n, 128)
+    return out
+
+
+# ---------------------------------------------------------------------------
 # Attention
 # ---------------------------------------------------------------------------
 
