@@ -10,7 +10,10 @@ cache and kv_b_proj weights, all resident in HBM before timing starts.
 
 Default workload: batch 1, one query token, context 32768, contiguous cache
 (the 32K configuration of the headline metric).  The 256K configuration
-(context 262144, KV chunks of 4096) is reported alongside under "ctx256k".
+(context 262144, KV chunks of 4096 and the device-balanced split) is
+reported alongside under "ctx256k", and the 32K and 256K workloads over the
+8-bit latent cache (E4M3 codes with per-128 fp32 scales, 656 bytes per token
+and layer) under "fp8_cache".
 
 Output: one JSON line.  "value" is decode tokens/s (batch * query tokens per
 step / step time, timed over --steps replays of a HIP graph of the step).
@@ -36,6 +39,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MLA decode tokens/s + latent-KV GB/s (% HBM peak) at 32K and 256K ctx, 1 GPU"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
 BYTES_PER_TOKEN_LAYER = 1152    # 576 bf16 cached values per token per layer
+BYTES_PER_TOKEN_LAYER_FP8 = 656  # 512 E4M3 codes + 4 fp32 scales + 64 bf16 rope values
 COUNTERS = os.path.join(ROOT, "profiles", "splitkv_decode_counters.json")
 DECODE_SRC = os.path.join(ROOT, "mla_latent_kv_absorbed_amd", "csrc", "decode.hip")
 
@@ -49,14 +53,14 @@ def source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def run_workload(k: int, steps: int, warmup: int, use_graph: bool, kv_chunk=None, label=""):
+def run_workload(k: int, steps: int, warmup: int, use_graph: bool, kv_chunk=None, label="", cache_dtype="bf16"):
     import torch
     import mla_latent_kv_absorbed_amd as M
     from mla_latent_kv_absorbed_amd.workload import DeviceWorkload
     from synth.configs import workload
 
     wl = workload(k)
-    dw = DeviceWorkload(wl, kv_chunk=kv_chunk)
+    dw = DeviceWorkload(wl, kv_chunk=kv_chunk, cache_dtype=cache_dtype)
     t0 = time.perf_counter()
     layers = [dw.build_layer(l) for l in range(wl.layers)]
     torch.cuda.synchronize()
@@ -118,12 +122,13 @@ def run_workload(k: int, steps: int, warmup: int, use_graph: bool, kv_chunk=None
     M.mla_timing_disable()
 
     tokens_ctx = sum(dw.lens)
-    bytes_per_launch = tokens_ctx * BYTES_PER_TOKEN_LAYER
+    bytes_per_launch = tokens_ctx * (BYTES_PER_TOKEN_LAYER_FP8 if cache_dtype == "fp8" else BYTES_PER_TOKEN_LAYER)
     avg_kernel_s = kern_ms / 1e3 / launches
     step_bytes = bytes_per_launch * len(layers)
     res = dict(
         workload=wl.name, batch=B, query_tokens=Sq, context=list(dw.lens) if B <= 4 else f"{B} seqs, sum {tokens_ctx}",
         layers=len(layers), layout="paged" if dw.paged else "contiguous", kv_chunk=dw.chunk_used,
+        cache_dtype=cache_dtype,
         graph=graph is not None, ms_per_step=ms_per_step, tokens_per_s=B * Sq / (ms_per_step / 1e3),
         step_latent_gbps=step_bytes / (ms_per_step / 1e3) / 1e9,
         kernel_avg_us=avg_kernel_s * 1e6, kernel_bytes_per_launch=bytes_per_launch,
@@ -252,6 +257,7 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-256k", action="store_true", help="skip the 256K report")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the 8-bit cache report")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="first copy this many MiB device-to-device 3 times (reference for rocprofv3 counters)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -283,6 +289,18 @@ def main():
             extra[name] = {k: r[k] for k in ("tokens_per_s", "ms_per_step", "step_latent_gbps", "kernel_avg_us",
                                             "kernel_latent_gbps", "kv_chunk")}
             extra[name]["kernel_hbm_frac"] = r["kernel_latent_gbps"] / HBM_PEAK_GBPS
+    fp8 = None
+    if not args.no_fp8:
+        fp8 = {}
+        for name, k in (("ctx32k", 1), ("ctx256k", 3)):
+            if args.no_256k and k == 3:
+                continue
+            r = run_workload(k, max(3, min(args.steps, 10)), 2, not args.no_graph, kv_chunk=0, label=f"fp8-{name}",
+                             cache_dtype="fp8")
+            log(f"[fp8 {name}] {json.dumps(r)}")
+            fp8[name] = {key: r[key] for key in ("workload", "tokens_per_s", "ms_per_step", "step_latent_gbps",
+                                               "kernel_avg_us", "kernel_latent_gbps", "kv_chunk")}
+            fp8[name]["kernel_hbm_frac"] = r["kernel_latent_gbps"] / HBM_PEAK_GBPS
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.config)
 
     bpl = main_res["kernel_bytes_per_launch"]
@@ -310,6 +328,7 @@ def main():
         },
         "cpu_baseline": cpu,
         "ctx256k": extra,
+        "fp8_cache": fp8,
     }
     print(json.dumps(line), flush=True)
 

@@ -51,13 +51,26 @@ typedef int32_t mla_status;
 #define MLA_ERR_DEVICE       6   /* a HIP runtime call failed                        */
 #define MLA_ERR_UNSUPPORTED  7   /* a valid request this build does not implement    */
 
+/* Cache row formats (mla_shape.kv_cache_dtype).
+ *  MLA_CACHE_BF16      576 bf16 = 1152 bytes: [latent (512) | rope key (64)]
+ *  MLA_CACHE_FP8_E4M3  656 bytes: [512 OCP FP8 E4M3 codes | 4 fp32 scales |
+ *                      64 bf16 rope key]; latent value = code * scale of its
+ *                      group of 128 (scale = group max |x| / 448, fp32; codes
+ *                      round to nearest, ties to even; a group of zeros has
+ *                      scale 0).  The 8-bit cache of [KV-ledger §三] (plan A),
+ *                      which halves the cache bytes of bf16.
+ * A page holds 64 rows of the chosen format. */
+#define MLA_CACHE_BF16      0
+#define MLA_CACHE_FP8_E4M3  1
+
 /* Attention shape.  The library implements exactly num_heads 32,
  * kv_lora_rank 512, qk_nope_head_dim 128, qk_rope_head_dim 64, v_head_dim 128
  * and page_size 64 ([KV-ledger §一]; [MLA-arch]); anything else returns
  * MLA_ERR_SHAPE.  softmax_scale multiplies q.k; for this model it is
  * (qk_nope + qk_rope)^-1/2 * mscale^2 with mscale = 0.1 ln(64) + 1
  * (YaRN's attention-logit correction named by [MLA-arch]); see
- * mla_default_softmax_scale(). */
+ * mla_default_shape().  kv_cache_dtype selects the cache row format of every
+ * call that takes a cache (MLA_CACHE_BF16 or MLA_CACHE_FP8_E4M3). */
 typedef struct {
     int32_t num_heads;
     int32_t kv_lora_rank;
@@ -66,6 +79,7 @@ typedef struct {
     int32_t v_head_dim;
     int32_t page_size;
     float   softmax_scale;
+    int32_t kv_cache_dtype;
 } mla_shape;
 
 /* YaRN rope parameters ([KV-ledger §一] rope_scaling; base not printed for
@@ -80,7 +94,8 @@ typedef struct {
     int32_t rope_dim;             /* 64                                */
 } mla_rope_params;
 
-/* Fills *shape with the model's shape and its softmax scale (host). */
+/* Fills *shape with the model's shape, its softmax scale and the bf16 cache
+ * format (host). */
 mla_status mla_default_shape(mla_shape* shape /* host */);
 
 /* Fills *params with the model's YaRN parameters, base 10000 (host). */
@@ -106,10 +121,12 @@ const char* mla_status_string(mla_status status);
 mla_status mla_rope_yarn(const mla_rope_params* params /* host */, const void* src, int64_t ld_src,
                          void* dst, int64_t ld_dst, const int32_t* positions, int64_t n, void* stream);
 
-/* Write cache rows: cache[slot] = [c_kv row (512) | k_pe row (64)], a bit copy.
+/* Write cache rows: cache[slot] = [c_kv row (512) | k_pe row (64)], a bit
+ * copy for the bf16 format; for the fp8 format the latent row is quantised
+ * (see the cache row formats above) and the rope key copied.
  * [MLA-arch]: only the compressed latent and the rope component are cached
  * per token, no per-head K or V.
- *   cache         bf16 [num_slots][576]; for the paged layout slot =
+ *   cache         [num_slots] rows of the shape's format; for the paged layout slot =
  *                 page * page_size + offset, for the contiguous layout slot =
  *                 b * stride + t
  *   c_kv, ld_c    bf16 latent rows [n][ld_c] (ld_c >= 512)
@@ -133,7 +150,7 @@ mla_status mla_cache_append(const mla_shape* shape /* host */, void* cache, int6
  *   q_nope       bf16 [B][Sq][32][128]
  *   q_pe         bf16 [B][Sq][32][64], already rotated
  *   w_kv_b       bf16 [8192][512] (nn.Linear storage: out x in)
- *   cache        bf16 [B][stride_tokens][576]
+ *   cache        [B][stride_tokens] rows of the shape's format
  *   ctx_lens     int32 [B], Sq <= L_b <= min(max_ctx_len, stride_tokens)
  *   max_ctx_len  host upper bound of ctx_lens
  *   kv_chunk     tokens per split, a multiple of 64, or 0 to let the
@@ -151,7 +168,7 @@ mla_status mla_decode(const mla_shape* shape /* host */, const void* q_nope, con
 
 /* Decode attention against a paged cache: as mla_decode, but token t of
  * sequence b lives in slot block_table[b][t / 64] * 64 + t % 64 of
- *   cache        bf16 [num_pages][64][576]
+ *   cache        [num_pages][64] rows of the shape's format
  *   block_table  int32 [B][max_pages_per_seq]
  * Every page a sequence uses must be in [0, num_pages). */
 mla_status mla_decode_paged(const mla_shape* shape /* host */, const void* q_nope, const void* q_pe,

@@ -17,6 +17,7 @@ from .build import lib_path
 
 __all__ = [
     "MlaError", "MlaShape", "MlaRopeParams", "default_shape", "default_rope", "library",
+    "CACHE_BF16", "CACHE_FP8_E4M3", "cache_row_width",
     "mla_rope_yarn", "mla_cache_append", "mla_decode", "mla_decode_paged", "mla_decode_step",
     "mla_decode_workspace_size", "mla_decode_auto_chunk", "mla_status_string",
     "mla_timing_enable", "mla_timing_collect", "mla_timing_disable",
@@ -31,7 +32,11 @@ class MlaShape(ctypes.Structure):
     _fields_ = [("num_heads", ctypes.c_int32), ("kv_lora_rank", ctypes.c_int32),
                 ("qk_nope_head_dim", ctypes.c_int32), ("qk_rope_head_dim", ctypes.c_int32),
                 ("v_head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
-                ("softmax_scale", ctypes.c_float)]
+                ("softmax_scale", ctypes.c_float), ("kv_cache_dtype", ctypes.c_int32)]
+
+
+CACHE_BF16 = 0          # rows of 576 bf16: [latent | rope key]
+CACHE_FP8_E4M3 = 1      # rows of 656 bytes: [512 E4M3 codes | 4 fp32 scales | 64 bf16 rope key]
 
 
 class MlaRopeParams(ctypes.Structure):
@@ -95,10 +100,26 @@ def _check(code: int, what: str):
         raise MlaError(f"{what}: {mla_status_string(code)} ({code})")
 
 
-def default_shape() -> MlaShape:
+def default_shape(kv_cache_dtype: int = CACHE_BF16) -> MlaShape:
     s = MlaShape()
     _check(library().mla_default_shape(ctypes.byref(s)), "mla_default_shape")
+    s.kv_cache_dtype = kv_cache_dtype
     return s
+
+
+def cache_row_width(shape: MlaShape) -> tuple:
+    """(torch dtype, elements per cache row) of the shape's cache format."""
+    if shape.kv_cache_dtype == CACHE_FP8_E4M3:
+        return torch.uint8, 656
+    return torch.bfloat16, 576
+
+
+def _check_cache(cache, shape, name="cache"):
+    dtype, width = cache_row_width(shape)
+    _need(cache, dtype, name)
+    if cache.shape[-1] != width:
+        raise MlaError(f"{name} rows must hold {width} {dtype} values for this cache format")
+    return width
 
 
 def default_rope() -> MlaRopeParams:
@@ -159,8 +180,10 @@ def mla_rope_yarn(src: torch.Tensor, positions: torch.Tensor, dst: torch.Tensor 
 
 def mla_cache_append(cache: torch.Tensor, c_kv: torch.Tensor, k_pe: torch.Tensor,
                      slot_mapping: torch.Tensor, shape: MlaShape | None = None, stream=None):
-    """cache.view(-1, 576)[slot] = [c_kv row | k_pe row] (bit copy); slot < 0 skips."""
-    _need(cache, torch.bfloat16, "cache")
+    """cache row[slot] = [c_kv row | k_pe row] (a bit copy for bf16 rows, quantised latent for
+    fp8 rows); slot < 0 skips."""
+    s = shape if shape is not None else default_shape()
+    width = _check_cache(cache, s)
     _need(slot_mapping, torch.int64, "slot_mapping")
     for t, name in ((c_kv, "c_kv"), (k_pe, "k_pe")):
         if t.dtype != torch.bfloat16 or t.device.type != "cuda" or t.dim() != 2 or t.stride(1) != 1:
@@ -168,8 +191,7 @@ def mla_cache_append(cache: torch.Tensor, c_kv: torch.Tensor, k_pe: torch.Tensor
     n = c_kv.shape[0]
     if k_pe.shape[0] != n or slot_mapping.numel() != n:
         raise MlaError("c_kv, k_pe and slot_mapping need the same number of rows")
-    num_slots = cache.numel() // 576
-    s = shape if shape is not None else default_shape()
+    num_slots = cache.numel() // width
     _check(library().mla_cache_append(ctypes.byref(s), _ptr(cache), num_slots, _ptr(c_kv), c_kv.stride(0),
                                       _ptr(k_pe), k_pe.stride(0), _ptr(slot_mapping), n, _stream(stream)),
            "mla_cache_append")
@@ -217,11 +239,11 @@ def _decode_io(q_nope, q_pe, w_kv_b, ctx_lens, out, lse, workspace, B, Sq, max_c
 
 def mla_decode(q_nope, q_pe, w_kv_b, cache, ctx_lens, max_ctx_len: int, kv_chunk: int = 0,
                out=None, lse=None, workspace=None, shape: MlaShape | None = None, stream=None):
-    """Decode against a contiguous cache [B, stride, 576]; returns (out, lse)."""
-    _need(cache, torch.bfloat16, "cache")
+    """Decode against a contiguous cache [B, stride, row]; returns (out, lse)."""
     B, Sq = q_nope.shape[0], q_nope.shape[1]
-    if cache.dim() != 3 or cache.shape[0] != B or cache.shape[2] != 576:
-        raise MlaError("cache must be [B, stride, 576]")
+    width = _check_cache(cache, shape if shape is not None else default_shape())
+    if cache.dim() != 3 or cache.shape[0] != B:
+        raise MlaError(f"cache must be [B, stride, {width}]")
     out, lse, workspace, s = _decode_io(q_nope, q_pe, w_kv_b, ctx_lens, out, lse, workspace, B, Sq,
                                         max_ctx_len, kv_chunk, shape)
     _check(library().mla_decode(ctypes.byref(s), _ptr(q_nope), _ptr(q_pe), _ptr(w_kv_b), _ptr(cache),
@@ -234,12 +256,12 @@ def mla_decode(q_nope, q_pe, w_kv_b, cache, ctx_lens, max_ctx_len: int, kv_chunk
 def mla_decode_paged(q_nope, q_pe, w_kv_b, cache, block_table, ctx_lens, max_ctx_len: int,
                      kv_chunk: int = 0, out=None, lse=None, workspace=None,
                      shape: MlaShape | None = None, stream=None):
-    """Decode against a paged cache [num_pages, 64, 576]; returns (out, lse)."""
-    _need(cache, torch.bfloat16, "cache")
+    """Decode against a paged cache [num_pages, 64, row]; returns (out, lse)."""
+    width = _check_cache(cache, shape if shape is not None else default_shape())
     _need(block_table, torch.int32, "block_table")
     B, Sq = q_nope.shape[0], q_nope.shape[1]
-    if cache.dim() != 3 or cache.shape[1] != 64 or cache.shape[2] != 576:
-        raise MlaError("cache must be [num_pages, 64, 576]")
+    if cache.dim() != 3 or cache.shape[1] != 64:
+        raise MlaError(f"cache must be [num_pages, 64, {width}]")
     if block_table.dim() != 2 or block_table.shape[0] != B:
         raise MlaError("block_table must be [B, max_pages_per_seq]")
     out, lse, workspace, s = _decode_io(q_nope, q_pe, w_kv_b, ctx_lens, out, lse, workspace, B, Sq,
@@ -258,8 +280,8 @@ def mla_decode_step(q_nope, q_pe, c_kv_new, k_pe_new, w_kv_b, cache, ctx_lens, m
     """One fused decode step: rotate q_pe and the new rope rows at p = L_b - Sq + j, write the new
     tokens' rows [c_kv_new | rot(k_pe_new)] into the cache, then decode.  q_pe and k_pe_new are
     NOT rotated.  ``block_table`` selects the paged layout [num_pages, 64, 576]; otherwise the
-    cache is contiguous [B, stride, 576].  Returns (out, lse)."""
-    _need(cache, torch.bfloat16, "cache")
+    cache is contiguous [B, stride, row].  Returns (out, lse)."""
+    width = _check_cache(cache, shape if shape is not None else default_shape())
     B, Sq = q_nope.shape[0], q_nope.shape[1]
     for t, name, width in ((c_kv_new, "c_kv_new", 512), (k_pe_new, "k_pe_new", 64)):
         if t.dtype != torch.bfloat16 or t.device.type != "cuda" or t.dim() != 2 or t.stride(1) != 1:
@@ -271,8 +293,8 @@ def mla_decode_step(q_nope, q_pe, c_kv_new, k_pe_new, w_kv_b, cache, ctx_lens, m
     r = rope if rope is not None else default_rope()
     lib = library()
     if block_table is None:
-        if cache.dim() != 3 or cache.shape[0] != B or cache.shape[2] != 576:
-            raise MlaError("cache must be [B, stride, 576]")
+        if cache.dim() != 3 or cache.shape[0] != B:
+            raise MlaError(f"cache must be [B, stride, {width}]")
         code = lib.mla_decode_step(ctypes.byref(s), ctypes.byref(r), _ptr(q_nope), _ptr(q_pe), _ptr(c_kv_new),
                                    c_kv_new.stride(0), _ptr(k_pe_new), k_pe_new.stride(0), _ptr(w_kv_b),
                                    _ptr(cache), cache.shape[1], _ptr(ctx_lens), max_ctx_len, B, Sq, kv_chunk,
@@ -280,8 +302,8 @@ def mla_decode_step(q_nope, q_pe, c_kv_new, k_pe_new, w_kv_b, cache, ctx_lens, m
         _check(code, "mla_decode_step")
     else:
         _need(block_table, torch.int32, "block_table")
-        if cache.dim() != 3 or cache.shape[1] != 64 or cache.shape[2] != 576:
-            raise MlaError("cache must be [num_pages, 64, 576]")
+        if cache.dim() != 3 or cache.shape[1] != 64:
+            raise MlaError(f"cache must be [num_pages, 64, {width}]")
         if block_table.dim() != 2 or block_table.shape[0] != B:
             raise MlaError("block_table must be [B, max_pages_per_seq]")
         code = lib.mla_decode_step_paged(ctypes.byref(s), ctypes.byref(r), _ptr(q_nope), _ptr(q_pe),

@@ -36,7 +36,8 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 mla_status check_shape(const mla_shape* s) {
   if (s == nullptr) return MLA_ERR_NULL;
   if (s->num_heads != kHeads || s->kv_lora_rank != kLatent || s->qk_nope_head_dim != kNope ||
-      s->qk_rope_head_dim != kRope || s->v_head_dim != kVDim || s->page_size != kPage)
+      s->qk_rope_head_dim != kRope || s->v_head_dim != kVDim || s->page_size != kPage ||
+      (s->kv_cache_dtype != MLA_CACHE_BF16 && s->kv_cache_dtype != MLA_CACHE_FP8_E4M3))
     return MLA_ERR_SHAPE;
   if (!(s->softmax_scale > 0.f) || !isfinite(s->softmax_scale)) return MLA_ERR_RANGE;
   return MLA_OK;
@@ -187,6 +188,7 @@ mla_status decode_common(const mla_shape* shape, const StepInputs& step, const v
   pp.block_table = block_table;
   pp.max_pages = max_pages;
   pp.paged = paged ? 1 : 0;
+  pp.fp8 = shape->kv_cache_dtype == MLA_CACHE_FP8_E4M3 ? 1 : 0;
   pp.B = B;
   pp.fixed_tiles = kv_chunk / kPage;
   pp.target_segs = target;
@@ -214,7 +216,9 @@ mla_status decode_common(const mla_shape* shape, const StepInputs& step, const v
     hipEvent_t ev0 = (timed && first) ? g_timing.ev[2 * g_timing.used] : nullptr;
     hipEvent_t ev1 = (timed && last) ? g_timing.ev[2 * g_timing.used + 1] : nullptr;
     p.j0 = j0;
-    if (launch_decode(p, (int)segs, qg, paged, s, ev0, ev1) != hipSuccess) return MLA_ERR_DEVICE;
+    const hipError_t e = pp.fp8 ? launch_decode_fp8(p, (int)segs, qg, paged, s, ev0, ev1)
+                                : launch_decode(p, (int)segs, qg, paged, s, ev0, ev1);
+    if (e != hipSuccess) return MLA_ERR_DEVICE;
   }
   if (timed) ++g_timing.used;
 
@@ -249,6 +253,7 @@ mla_status mla_default_shape(mla_shape* shape) {
   shape->qk_rope_head_dim = kRope;
   shape->v_head_dim = kVDim;
   shape->page_size = kPage;
+  shape->kv_cache_dtype = MLA_CACHE_BF16;
   const double mscale = 0.1 * 1.0 * log(64.0) + 1.0;      // mscale_all_dim 1.0, factor 64
   shape->softmax_scale = (float)(mscale * mscale / sqrt((double)(kNope + kRope)));
   return MLA_OK;
@@ -308,6 +313,11 @@ mla_status mla_cache_append(const mla_shape* shape, void* cache, int64_t num_slo
       ((uintptr_t)slot_mapping & 7u) != 0)
     return MLA_ERR_ALIGN;
   if (n > (int64_t)1 << 40) return MLA_ERR_RANGE;
+  if (shape->kv_cache_dtype == MLA_CACHE_FP8_E4M3)
+    return launch_append_fp8((uint8_t*)cache, (const uint16_t*)c_kv, ld_c, (const uint16_t*)k_pe, ld_k,
+                             slot_mapping, n, (hipStream_t)stream) == hipSuccess
+               ? MLA_OK
+               : MLA_ERR_DEVICE;
   return launch_append((uint8_t*)cache, num_slots, (const uint16_t*)c_kv, ld_c, (const uint16_t*)k_pe,
                        ld_k, slot_mapping, n, (hipStream_t)stream) == hipSuccess
              ? MLA_OK

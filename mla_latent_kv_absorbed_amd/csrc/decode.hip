@@ -172,6 +172,11 @@ __global__ void __launch_bounds__(256, 1) splitkv_decode(DecodeParams p) {
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) q[ks] = *(const bf16x8*)(qrow + ks * 32);
   }
+  // Settle the query loads here, once: a wait the compiler placed at their
+  // first use inside the slot loop would count only its own loads and so
+  // also drain the cache slots requested ahead of every iteration.
+#pragma unroll
+  for (int ks = 0; ks < 18; ++ks) asm volatile("" ::"v"(q[ks]));
 
   // LDS read offsets within a slot.  Score reads: token tok_w + 16*blk + n16,
   // chunk 4*ks + g, position (4ks + g) ^ n16 = 16*(ks/4) + ((4*(ks%4)) ^ (g ^ n16));

@@ -236,7 +236,38 @@ __global__ void __launch_bounds__(256) prep_query(PrepParams p) {
       dst[kLatent + col + half] = hi;
     }
   }
-  if (p.c_new != nullptr && pos >= 0 && (h == 0 || (h == 1 && cblk == 0))) {
+  if (p.c_new != nullptr && p.fp8 && pos >= 0 && ((h == 0 && cblk < 4) || (h == 1 && cblk == 0))) {
+    // 8-bit row: latent group cblk (128 values, 2 per lane of this row's wave)
+    // quantised with its own scale; the rope key rotated into bf16 at byte 528
+    int64_t slot;
+    if (p.paged) slot = (int64_t)p.block_table[(size_t)b * p.max_pages + pos / kPage] * kPage + pos % kPage;
+    else slot = (int64_t)b * p.stride_tokens + pos;
+    uint8_t* row = p.cache + slot * kF8Row;
+    if (h == 0) {
+      const uint32_t two = *(const uint32_t*)(p.c_new + r * p.ld_c + cblk * kF8Group + 2 * col);
+      const float x0 = __uint_as_float(two << 16), x1 = __uint_as_float(two & 0xFFFF0000u);
+      float amax = fmaxf(fabsf(x0), fabsf(x1));
+#pragma unroll
+      for (int d = 32; d >= 1; d >>= 1) amax = fmaxf(amax, __shfl_xor(amax, d, 64));
+      const float scale = amax / kE4M3Max;
+      const uint32_t q0 = scale > 0.f ? f32_to_e4m3(x0 / scale) : 0u;
+      const uint32_t q1 = scale > 0.f ? f32_to_e4m3(x1 / scale) : 0u;
+      *(uint16_t*)(row + cblk * kF8Group + 2 * col) = (uint16_t)(q0 | (q1 << 8));
+      if (col == 0) *(float*)(row + kF8ScaleOff + 4 * cblk) = scale;
+    } else {
+      uint16_t* rope = (uint16_t*)(row + kF8RopeOff);
+      const uint16_t* src = p.k_new + r * p.ld_k;
+      if (!p.rotate) {
+        rope[col] = src[col];
+      } else if (col < half) {
+        uint16_t lo, hi;
+        rope_pair(src[col], src[col + half], (double)pos * p.inv.v[col], &lo, &hi);
+        rope[col] = lo;
+        rope[col + half] = hi;
+      }
+    }
+  }
+  if (p.c_new != nullptr && !p.fp8 && pos >= 0 && (h == 0 || (h == 1 && cblk == 0))) {
     int64_t slot;
     if (p.paged) slot = (int64_t)p.block_table[(size_t)b * p.max_pages + pos / kPage] * kPage + pos % kPage;
     else slot = (int64_t)b * p.stride_tokens + pos;
@@ -458,7 +489,54 @@ __global__ void __launch_bounds__(256) cache_append(uint8_t* __restrict__ cache,
   *(uint4*)(cache + slot * kRowBytes + c * 16) = v;
 }
 
+// ---------------------------------------------------------------------------
+// 8-bit cache append: one wave per row.  Lane l holds latent values
+// [8l, 8l + 8) of group l / 16; the 16 lanes of a group agree on
+// amax = max |x|, scale = amax / 448 (fp32), codes e4m3(x / scale) (a group of
+// zeros: scale 0, codes 0); lanes 0..7 copy the bf16 rope key (16 bytes each).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) cache_append_fp8(uint8_t* __restrict__ cache,
+                                                        const uint16_t* __restrict__ c_kv, int64_t ld_c,
+                                                        const uint16_t* __restrict__ k_pe, int64_t ld_k,
+                                                        const int64_t* __restrict__ slots, int64_t n) {
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= n) return;
+  const int64_t slot = slots[t];
+  if (slot < 0) return;
+  const uint4 v = *(const uint4*)(c_kv + t * ld_c + 8 * lane);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float x[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    x[2 * k] = __uint_as_float(w[k] << 16);
+    x[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(x[k]));
+#pragma unroll
+  for (int d = 8; d >= 1; d >>= 1) amax = fmaxf(amax, __shfl_xor(amax, d, 16));
+  const float scale = amax / kE4M3Max;
+  uint32_t q[2] = {0u, 0u};
+  if (scale > 0.f) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) q[k >> 2] |= f32_to_e4m3(x[k] / scale) << (8 * (k & 3));
+  }
+  uint8_t* row = cache + slot * kF8Row;
+  *(uint2*)(row + 8 * lane) = make_uint2(q[0], q[1]);
+  if ((lane & 15) == 0) *(float*)(row + kF8ScaleOff + 4 * (lane >> 4)) = scale;
+  if (lane < 8) *(uint4*)(row + kF8RopeOff + 16 * lane) = *(const uint4*)(k_pe + t * ld_k + 8 * lane);
+}
+
 }  // namespace
+
+hipError_t launch_append_fp8(uint8_t* cache, const uint16_t* c_kv, int64_t ld_c, const uint16_t* k_pe,
+                             int64_t ld_k, const int64_t* slots, int64_t n, hipStream_t stream) {
+  const unsigned blocks = (unsigned)((n + 3) / 4);
+  hipLaunchKernelGGL(cache_append_fp8, dim3(blocks), dim3(256), 0, stream, cache, c_kv, ld_c, k_pe, ld_k, slots, n);
+  return hipGetLastError();
+}
 
 hipError_t launch_prep(const PrepParams& p, hipStream_t stream) {
   const unsigned rb = (unsigned)((p.rows + kPrepRows - 1) / kPrepRows);

@@ -23,6 +23,15 @@ constexpr int kChunksPerRow = kRowBytes / 16;   // 72 sixteen-byte chunks
 constexpr int kWRowsPerHead = kNope + kVDim;    // 256 kv_b_proj rows per head
 constexpr int kMaxQueryGroup = 2;               // query tokens one decode pass handles
 
+// 8-bit latent cache rows: [512 E4M3 codes | 4 fp32 scales (one per 128
+// latent values) | 64 bf16 rope key] = 656 bytes.
+constexpr int kF8Row = 656;
+constexpr int kF8ScaleOff = 512;
+constexpr int kF8RopeOff = 528;
+constexpr int kF8Group = 128;
+constexpr int kF8Tile = kPage * kF8Row;         // 41984 bytes per page
+constexpr float kE4M3Max = 448.0f;
+
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
@@ -94,6 +103,25 @@ struct DecodeParams {
   const uint8_t* zero_row;      // kRowBytes zero bytes
 };
 
+// Encoding of an fp32 value |y| <= 448 as an OCP FP8 E4M3 code, nearest,
+// ties to the even code (sign bit from y).  Below 2^-6 the codes step by
+// 2^-9 (subnormals); above, the fp32 significand is rounded to 3 bits.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = __uint_as_float(u & 0x7FFFFFFFu);
+  uint32_t code;
+  if (a < 0.015625f) {
+    code = (uint32_t)__builtin_rintf(a * 512.0f);     // exact scaling; rint: nearest, ties to even
+  } else {
+    uint32_t ua = __float_as_uint(a);
+    ua += 0x7FFFFu + ((ua >> 20) & 1u);              // round the significand to 3 bits
+    code = ((((ua >> 23) - 120u) << 3) | ((ua >> 20) & 7u));
+    code = code > 0x7Eu ? 0x7Eu : code;              // 448 is the largest finite code
+  }
+  return code | sign;
+}
+
 // Everything that precedes the split-KV pass: the absorbed query rows, the
 // rope part of the query (copied, or rotated at p = L_b - Sq + j), the cache
 // rows of the new tokens (optional), the split schedule and the decode
@@ -120,6 +148,7 @@ struct PrepParams {
   const int32_t* block_table;
   int32_t max_pages;
   int32_t paged;
+  int32_t fp8;                  // cache rows are 8-bit (kF8Row bytes)
   // split schedule
   int32_t fixed_tiles;          // tiles per split, or 0: balance on the device
   int32_t target_segs;          // balanced: aim at no more segments than this
@@ -158,5 +187,9 @@ hipError_t launch_rope(const uint16_t* src, int64_t ld_src, uint16_t* dst, int64
 hipError_t launch_append(uint8_t* cache, int64_t num_slots, const uint16_t* c_kv, int64_t ld_c,
                          const uint16_t* k_pe, int64_t ld_k, const int64_t* slots, int64_t n,
                          hipStream_t stream);
+hipError_t launch_append_fp8(uint8_t* cache, const uint16_t* c_kv, int64_t ld_c, const uint16_t* k_pe,
+                             int64_t ld_k, const int64_t* slots, int64_t n, hipStream_t stream);
+hipError_t launch_decode_fp8(const DecodeParams& p, int segments, int query_group, bool paged,
+                             hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop);
 
 }  // namespace mla

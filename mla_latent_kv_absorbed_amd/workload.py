@@ -20,10 +20,11 @@ import synth
 import synth.gpu as sgpu
 from synth.configs import Workload
 
-from . import (mla_cache_append, mla_decode, mla_decode_paged, mla_decode_step, mla_decode_workspace_size,
-               mla_decode_auto_chunk, mla_rope_yarn)
+from . import (CACHE_BF16, CACHE_FP8_E4M3, cache_row_width, default_shape, mla_cache_append, mla_decode,
+               mla_decode_paged, mla_decode_step, mla_decode_workspace_size, mla_decode_auto_chunk, mla_rope_yarn)
 
 BF16_NAN = 0x7FC1   # bit pattern written into unused cache slots when poisoning
+FP8_NAN = 0x7F      # E4M3 NaN byte, the same for 8-bit cache rows
 
 
 @dataclass
@@ -41,8 +42,12 @@ class LayerInputs:
 
 class DeviceWorkload:
     def __init__(self, wl: Workload, device: str = "cuda:0", paged: bool | None = None,
-                 kv_chunk: int | None = None, poison: bool = False, permute_pages: bool | None = None):
+                 kv_chunk: int | None = None, poison: bool = False, permute_pages: bool | None = None,
+                 cache_dtype: str = "bf16"):
         self.wl = wl
+        self.fp8 = cache_dtype == "fp8"
+        self.shape = default_shape(CACHE_FP8_E4M3 if self.fp8 else CACHE_BF16)
+        self.cache_torch_dtype, self.row_width = cache_row_width(self.shape)
         self.dev = torch.device(device)
         self.B, self.Sq = wl.batch, wl.sq
         self.lens = [int(x) for x in wl.lens]
@@ -59,12 +64,12 @@ class DeviceWorkload:
             self.block_table_host = bt
             self.block_table = torch.from_numpy(bt).to(self.dev)
             self.num_pages = pool
-            self.cache_shape = (pool, 64, 576)
+            self.cache_shape = (pool, 64, self.row_width)
         else:
             self.block_table_host = None
             self.block_table = None
             self.stride = self.max_ctx
-            self.cache_shape = (B, self.stride, 576)
+            self.cache_shape = (B, self.stride, self.row_width)
         # positions of the queries (rows b, j, h) and of the new tokens (b, j)
         qpos, npos = [], []
         for b in range(B):
@@ -76,7 +81,7 @@ class DeviceWorkload:
         self.new_pos = torch.tensor(npos, dtype=torch.int32, device=self.dev)
         self.new_slots = self.slots_of(torch.arange(B, device=self.dev).repeat_interleave(Sq),
                                        self.new_pos.to(torch.int64))
-        self.workspace_bytes = mla_decode_workspace_size(B, Sq, self.max_ctx, self.kv_chunk)
+        self.workspace_bytes = mla_decode_workspace_size(B, Sq, self.max_ctx, self.kv_chunk, self.shape)
         self.workspace = torch.empty(self.workspace_bytes, dtype=torch.uint8, device=self.dev)
         self.chunk_used = self.kv_chunk or mla_decode_auto_chunk(B, Sq, self.max_ctx)
 
@@ -91,12 +96,14 @@ class DeviceWorkload:
     # ---- construction
     def build_layer(self, layer: int) -> LayerInputs:
         B, Sq, dev, seed = self.B, self.Sq, self.dev, self.seed
-        if self.poison:
+        if self.poison and self.fp8:
+            cache = torch.full(self.cache_shape, FP8_NAN, dtype=torch.uint8, device=dev)
+        elif self.poison:
             cache = torch.full(self.cache_shape, 0, dtype=torch.int16, device=dev)
             cache.fill_(BF16_NAN)
             cache = cache.view(torch.bfloat16)
         else:
-            cache = torch.empty(self.cache_shape, dtype=torch.bfloat16, device=dev)
+            cache = torch.empty(self.cache_shape, dtype=self.cache_torch_dtype, device=dev)
         for b, L in enumerate(self.lens):
             step = 1 << 20
             for t0 in range(0, L, step):
@@ -109,7 +116,7 @@ class DeviceWorkload:
                 mla_rope_yarn(k, pos)
                 slots = self.slots_of(torch.full((n,), b, dtype=torch.int64, device=dev),
                                       pos.to(torch.int64))
-                mla_cache_append(cache, c, k, slots)
+                mla_cache_append(cache, c, k, slots, shape=self.shape)
                 del c, k
         w = torch.empty((8192, 512), dtype=torch.bfloat16, device=dev)
         sgpu.wkvb(w, seed, layer)
@@ -133,18 +140,18 @@ class DeviceWorkload:
         ws = self._workspace(chunk)
         return mla_decode_step(li.q_nope, li.q_pe_raw, li.new_c, li.new_kpe_raw, li.w_kv_b, li.cache,
                                self.ctx_lens, self.max_ctx, chunk, block_table=self.block_table,
-                               out=out, lse=lse, workspace=ws)
+                               out=out, lse=lse, workspace=ws, shape=self.shape)
 
     def step_unfused(self, li: LayerInputs, out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
                      kv_chunk: int | None = None):
         """The same step as separate calls: RoPE of q and of the new keys, append, decode."""
         mla_rope_yarn(li.q_pe_raw, self.q_pos, dst=li.q_pe)
         mla_rope_yarn(li.new_kpe_raw, self.new_pos, dst=li.new_kpe)
-        mla_cache_append(li.cache, li.new_c, li.new_kpe, self.new_slots)
+        mla_cache_append(li.cache, li.new_c, li.new_kpe, self.new_slots, shape=self.shape)
         return self.decode(li, out, lse, kv_chunk)
 
     def _workspace(self, chunk: int) -> torch.Tensor:
-        need = mla_decode_workspace_size(self.B, self.Sq, self.max_ctx, chunk)
+        need = mla_decode_workspace_size(self.B, self.Sq, self.max_ctx, chunk, self.shape)
         if need > self.workspace.numel():
             self.workspace = torch.empty(need, dtype=torch.uint8, device=self.dev)
         return self.workspace
@@ -154,6 +161,6 @@ class DeviceWorkload:
         ws = self._workspace(chunk)
         if self.paged:
             return mla_decode_paged(li.q_nope, li.q_pe, li.w_kv_b, li.cache, self.block_table, self.ctx_lens,
-                                    self.max_ctx, chunk, out=out, lse=lse, workspace=ws)
+                                    self.max_ctx, chunk, out=out, lse=lse, workspace=ws, shape=self.shape)
         return mla_decode(li.q_nope, li.q_pe, li.w_kv_b, li.cache, self.ctx_lens, self.max_ctx, chunk,
-                          out=out, lse=lse, workspace=ws)
+                          out=out, lse=lse, workspace=ws, shape=self.shape)

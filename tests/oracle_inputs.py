@@ -61,3 +61,18 @@ def compare(out_gpu, lse_gpu, out_ref, lse_ref):
     assert rel <= OUT_REL_L2, f"rel L2 {rel}"
     assert lmax <= LSE_MAX_ABS, f"lse max abs {lmax}"
     return max_abs, rel, lmax
+
+
+def sequence_inputs_fp8(seed, layer, length, sq, b):
+    """As sequence_inputs, with the latent replaced by its 8-bit cache value
+    (quantised by the oracle, dequantised exactly)."""
+    qn, qp, c, k = sequence_inputs(seed, layer, length, sq, b)
+    codes, scales = O.quantize_latent_fp8(c.astype(np.float32))
+    return qn, qp, O.dequantize_latent_fp8(codes, scales), k
+
+
+def expected_fp8(seed, layer, length, sq, b, heads=None, absorbed=False):
+    """Oracle (out, lse) for sequence b over the 8-bit cache."""
+    qn, qp, c, k = sequence_inputs_fp8(seed, layer, length, sq, b)
+    fn = O.mla_attention_absorbed if absorbed else O.mla_attention_unabsorbed
+    return fn(qn, qp, c, k, weights(seed, layer), O.softmax_scale(), heads)
