@@ -13,7 +13,10 @@ Default workload: batch 1, one query token, context 32768, contiguous cache
 (context 262144, KV chunks of 4096 and the device-balanced split) is
 reported alongside under "ctx256k", and the 32K and 256K workloads over the
 8-bit latent cache (E4M3 codes with per-128 fp32 scales, 656 bytes per token
-and layer) under "fp8_cache".
+and layer) under "fp8_cache".  "other_workloads" reports the batched paged
+decode (16 x 65536), speculative verify of 2, 3 and 4 query tokens per
+sequence (batch 32, log-uniform contexts in [4096, 131072], paged) and one
+sequence of 524288 tokens, all with the device-balanced split.
 
 Output: one JSON line.  "value" is decode tokens/s (batch * query tokens per
 step / step time, timed over --steps replays of a HIP graph of the step).
@@ -258,6 +261,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-256k", action="store_true", help="skip the 256K report")
     ap.add_argument("--no-fp8", action="store_true", help="skip the 8-bit cache report")
+    ap.add_argument("--no-more", action="store_true",
+                    help="skip the report on the other workloads (batched paged, speculative verify, 512K)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="first copy this many MiB device-to-device 3 times (reference for rocprofv3 counters)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -301,6 +306,18 @@ def main():
             fp8[name] = {key: r[key] for key in ("workload", "tokens_per_s", "ms_per_step", "step_latent_gbps",
                                                "kernel_avg_us", "kernel_latent_gbps", "kv_chunk")}
             fp8[name]["kernel_hbm_frac"] = r["kernel_latent_gbps"] / HBM_PEAK_GBPS
+    more = None
+    if not args.no_more:
+        more = {}
+        for k in (2, 4, 7, 5, 6):
+            if k == args.config:
+                continue
+            r = run_workload(k, max(3, min(args.steps, 10)), 2, not args.no_graph, kv_chunk=0, label=f"config{k}")
+            log(f"[config{k}] {json.dumps(r)}")
+            more[r["workload"]] = {key: r[key] for key in ("batch", "query_tokens", "layout", "tokens_per_s",
+                                                         "ms_per_step", "step_latent_gbps", "kernel_avg_us",
+                                                         "kernel_latent_gbps", "kv_chunk")}
+            more[r["workload"]]["kernel_hbm_frac"] = r["kernel_latent_gbps"] / HBM_PEAK_GBPS
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.config)
 
     bpl = main_res["kernel_bytes_per_launch"]
@@ -329,6 +346,7 @@ def main():
         "cpu_baseline": cpu,
         "ctx256k": extra,
         "fp8_cache": fp8,
+        "other_workloads": more,
     }
     print(json.dumps(line), flush=True)
 

@@ -154,12 +154,17 @@ mla_status mla_cache_append(const mla_shape* shape /* host */, void* cache, int6
  *   ctx_lens     int32 [B], Sq <= L_b <= min(max_ctx_len, stride_tokens)
  *   max_ctx_len  host upper bound of ctx_lens
  *   kv_chunk     tokens per split, a multiple of 64, or 0 to let the
- *                library choose
+ *                library choose (splits sized from the actual ctx_lens on the
+ *                device, about one workgroup per compute unit)
  *   out          bf16 [B][Sq][32][128]
  *   lse          fp32 [B][Sq][32] natural-log sum of exp(s_t), or NULL
  *   workspace    device scratch of mla_decode_workspace_size() bytes,
  *                256-byte aligned
- * Supports 1 <= Sq <= 16 and B * Sq <= 65535.  B = 0 is a no-op. */
+ * Supports 1 <= Sq <= 16 and B * Sq <= 65535.  B = 0 is a no-op.  All Sq
+ * query tokens are served by one pass over the cache: the workgroups of the
+ * query groups (two tokens each) of one split read the same rows together.
+ * MLA_ERR_RANGE also when the splits times the ceil(Sq/2) query groups exceed
+ * 2^24 workgroups. */
 mla_status mla_decode(const mla_shape* shape /* host */, const void* q_nope, const void* q_pe,
                       const void* w_kv_b, const void* cache, int64_t stride_tokens,
                       const int32_t* ctx_lens, int32_t max_ctx_len, int32_t B, int32_t Sq,

@@ -153,8 +153,11 @@ mla_status decode_common(const mla_shape* shape, const StepInputs& step, const v
       return MLA_ERR_ALIGN;
   }
   const int target = compute_units();
+  const int groups = query_groups(Sq);
   const int64_t segs = max_segments(B, max_ctx_len, kv_chunk, target);
-  if (segs > 0x7FFFFFFF) return MLA_ERR_RANGE;
+  // one split-KV launch covers every (segment, query group) pair; its
+  // workgroups times 256 threads must fit in 32 bits
+  if (((segs + kXcds - 1) / kXcds) * kXcds * groups > (int64_t)(0xFFFFFFFFu / 256)) return MLA_ERR_RANGE;
   const WorkspaceLayout wl = workspace_layout(B, Sq, (int)segs);
   if (workspace_bytes < wl.total) return MLA_ERR_WORKSPACE;
 
@@ -191,7 +194,7 @@ mla_status decode_common(const mla_shape* shape, const StepInputs& step, const v
   pp.fp8 = shape->kv_cache_dtype == MLA_CACHE_FP8_E4M3 ? 1 : 0;
   pp.B = B;
   pp.fixed_tiles = kv_chunk / kPage;
-  pp.target_segs = target;
+  pp.target_segs = std::max(1, target / groups);   // about one workgroup per compute unit
   pp.max_segs = (int)segs;
   pp.seg_desc = (int4*)(ws + wl.seg_desc);
   pp.seg_start = (int32_t*)(ws + wl.seg_start);
@@ -205,19 +208,18 @@ mla_status decode_common(const mla_shape* shape, const StepInputs& step, const v
   p.max_pages = max_pages;
   p.seg_desc = pp.seg_desc;
   p.Sq = Sq;
+  p.segments = (int)segs;
+  p.groups = groups;
   p.scale_log2 = scale_log2;
   p.part_o = (float*)(ws + wl.part_o);
   p.part_lse = (float*)(ws + wl.part_lse);
   p.zero_row = zero_row;
   const bool timed = g_timing.on && g_timing.used < g_timing.capacity;
-  for (int j0 = 0; j0 < Sq; j0 += kMaxQueryGroup) {
-    const int qg = (Sq - j0 >= 2) ? 2 : 1;
-    const bool first = j0 == 0, last = j0 + qg >= Sq;
-    hipEvent_t ev0 = (timed && first) ? g_timing.ev[2 * g_timing.used] : nullptr;
-    hipEvent_t ev1 = (timed && last) ? g_timing.ev[2 * g_timing.used + 1] : nullptr;
-    p.j0 = j0;
-    const hipError_t e = pp.fp8 ? launch_decode_fp8(p, (int)segs, qg, paged, s, ev0, ev1)
-                                : launch_decode(p, (int)segs, qg, paged, s, ev0, ev1);
+  {
+    hipEvent_t ev0 = timed ? g_timing.ev[2 * g_timing.used] : nullptr;
+    hipEvent_t ev1 = timed ? g_timing.ev[2 * g_timing.used + 1] : nullptr;
+    const hipError_t e = pp.fp8 ? launch_decode_fp8(p, (int)segs, query_group(Sq), paged, s, ev0, ev1)
+                                : launch_decode(p, (int)segs, query_group(Sq), paged, s, ev0, ev1);
     if (e != hipSuccess) return MLA_ERR_DEVICE;
   }
   if (timed) ++g_timing.used;
@@ -428,7 +430,7 @@ mla_status mla_timing_disable(void) {
 mla_status mla_decode_auto_chunk(int32_t B, int32_t Sq, int32_t max_ctx_len, int32_t* kv_chunk) {
   if (kv_chunk == nullptr) return MLA_ERR_NULL;
   if (B < 0 || Sq < 1 || Sq > kMaxSq || max_ctx_len < Sq) return MLA_ERR_RANGE;
-  *kv_chunk = balanced_chunk(B < 1 ? 1 : B, max_ctx_len, compute_units());
+  *kv_chunk = balanced_chunk(B < 1 ? 1 : B, max_ctx_len, std::max(1, compute_units() / query_groups(Sq)));
   return MLA_OK;
 }
 

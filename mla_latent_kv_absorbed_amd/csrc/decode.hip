@@ -105,15 +105,21 @@ __global__ void __launch_bounds__(256, 1) splitkv_decode(DecodeParams p) {
   const int g = lane >> 4, n16 = lane & 15;
   const int rg = wave % RG, tp = wave / RG;
 
-  const int unit = blockIdx.x;   // segment: tokens [t_begin, t_end) of sequence b
+  int unit, grp;   // segment (tokens [t_begin, t_end) of sequence b) and query group
+  work_item(p.groups, unit, grp);
+  if (unit >= p.segments) return;
   const int4 seg = p.seg_desc[unit];
   const int b = seg.x, t_begin = seg.y, t_end = seg.z, L = seg.w;
   if (b < 0 || t_begin >= t_end) return;   // no segment: the combine never reads it
 
-  const int j = p.j0 + (rg >> 1);
+  // Query token of this wave's rows; a repeat of token Sq - 1 (computed, never
+  // written) fills the second half of the last group when Sq is odd.
+  const int j_grp = QG * grp + (rg >> 1);
+  const bool real = j_grp < p.Sq;
+  const int j = real ? j_grp : p.Sq - 1;
   const int limit = min(t_end, L - p.Sq + j + 1);   // rows of this wave see tokens < limit
-  const int rg_glob = 2 * p.j0 + rg;
   // partial rows of this wave's row group: [unit][j*32 + h][512] fp32
+  const int rg_glob = 2 * QG * grp + rg;
   float* out_o = p.part_o + ((size_t)unit * (2 * p.Sq) + rg_glob) * (16 * kLatent);
   float* out_lse = p.part_lse + (size_t)unit * (p.Sq * 32) + rg_glob * 16;
 
@@ -380,6 +386,7 @@ __global__ void __launch_bounds__(256, 1) splitkv_decode(DecodeParams p) {
     m_ref = mm;
   }
   // lane (g, n16) holds row n16, columns 16*cb + 4g .. 16*cb + 4g + 3
+  if (!real) return;
   const float inv = (l_row > 0.f) ? 1.f / l_row : 0.f;
   const float s_own = a_own * inv, s_other = a_other * inv;
   float* orow = out_o + n16 * kLatent + 4 * g;
@@ -402,7 +409,7 @@ __global__ void __launch_bounds__(256, 1) splitkv_decode(DecodeParams p) {
 
 hipError_t launch_decode(const DecodeParams& p, int segments, int query_group, bool paged, hipStream_t stream,
                          hipEvent_t ev_start, hipEvent_t ev_stop) {
-  const dim3 grid((unsigned)segments), block(256);
+  const dim3 grid(decode_grid(segments, p.groups)), block(256);
   // with events, the dispatch itself records them at kernel start and end
   if (query_group == 1) {
     if (paged) hipExtLaunchKernelGGL((splitkv_decode<1, true>), grid, block, 0, stream, ev_start, ev_stop, 0, p);

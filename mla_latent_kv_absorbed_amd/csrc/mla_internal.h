@@ -94,14 +94,45 @@ struct DecodeParams {
   int64_t stride_tokens;        // contiguous layout: tokens per sequence block
   const int32_t* block_table;   // paged layout: [B][max_pages]
   int32_t max_pages;
-  const int4* seg_desc;         // one per workgroup
+  const int4* seg_desc;         // [segments]
+  int32_t segments;             // segment records (grid capacity)
+  int32_t groups;               // query groups per segment (see work_item)
   int32_t Sq;                   // query tokens per sequence
-  int32_t j0;                   // first query token of this pass
   float scale_log2;             // softmax_scale * log2(e)
   float* part_o;
   float* part_lse;
   const uint8_t* zero_row;      // kRowBytes zero bytes
 };
+
+// Query tokens per split-KV workgroup, and the number of such query groups
+// that cover Sq tokens.  A group of two keeps 64 query rows (4 row groups of
+// 16, one per wave); a single query token uses 32 rows.  For odd Sq > 1 the
+// last group repeats token Sq - 1 in its second half and writes nothing for it.
+inline int query_group(int Sq) { return Sq == 1 ? 1 : kMaxQueryGroup; }
+inline int query_groups(int Sq) { return (Sq + query_group(Sq) - 1) / query_group(Sq); }
+
+// Workgroups of one split-KV launch: every (segment, query group) pair.
+// The device hands consecutive workgroups to its 8 XCDs in turn (workgroup
+// x runs on XCD x % 8), and each XCD has its own L2.  With several query
+// groups, the groups of a segment therefore get numbers x, x + 8, x + 16, ...:
+// the same XCD, dispatched one after the other, so they stream the same
+// cache rows at about the same time and only the first read of a row goes
+// to HBM.  The mapping is a locality choice only; any placement is correct.
+constexpr int kXcds = 8;
+inline unsigned decode_grid(int segments, int groups) {
+  return groups == 1 ? (unsigned)segments : (unsigned)(((segments + kXcds - 1) / kXcds) * kXcds * groups);
+}
+__device__ __forceinline__ void work_item(int groups, int& unit, int& grp) {
+  const int x = blockIdx.x;
+  if (groups == 1) {
+    unit = x;
+    grp = 0;
+    return;
+  }
+  const int k = x / kXcds;
+  unit = (k / groups) * kXcds + x % kXcds;
+  grp = k % groups;
+}
 
 // Encoding of an fp32 value |y| <= 448 as an OCP FP8 E4M3 code, nearest,
 // ties to the even code (sign bit from y).  Below 2^-6 the codes step by

@@ -55,7 +55,22 @@ def workload(k: int) -> Workload:
         lens = tuple(int(x) for x in loguniform_lengths(4, 32, 4096, 131072))
         return Workload(4, "mla-mtp-verify-b32-sq2", 32, 2, 40, lens, True, 0,
                         note="batch 32, 2 causal query tokens, log-uniform contexts in [4096, 131072]")
+    # Beyond the five workloads above: deeper speculative verify (drafts of up
+    # to 3 tokens, the --spec-draft-n-max 3 server setting of the
+    # Swift-Qwen3.8-27B-GGUF page; the Xing4.0 pages' MTP drafting) and the
+    # 512,000-token extension that "China Telecom's Xing4.0 Runs a 29B Coding
+    # Agent on 19GB Locally" mentions, taken as 2^19 tokens with the same
+    # YaRN parameters.
+    if k in (5, 7):
+        sq = 4 if k == 5 else 3
+        lens = tuple(int(x) for x in loguniform_lengths(k, 32, 4096, 131072))
+        return Workload(k, f"mla-mtp-verify-b32-sq{sq}", 32, sq, 40, lens, True, 0,
+                        note=f"batch 32, {sq} causal query tokens, log-uniform contexts in [4096, 131072]")
+    if k == 6:
+        return Workload(6, "mla-long-b1-ctx512k", 1, 1, 40, (524288,), False, 0,
+                        note="batch 1, context 524288 (positions past the 262144 of the YaRN table)")
     raise ValueError(f"no workload {k}")
 
 
 ALL = (0, 1, 2, 3, 4)
+EXTENDED = (5, 6, 7)

@@ -63,6 +63,7 @@ RAGGED = [
     (1, (1, 2, 63, 64, 65, 700)),
     (2, (2, 3, 64, 65, 129, 333)),
     (3, (3, 70, 200)),
+    (4, (4, 100, 500)),
 ]
 
 

@@ -76,3 +76,17 @@ def test_mtp_verify_b32_sq2():
     lens = np.array(wl.lens)
     seqs = sorted({int(lens.argmin()), int(lens.argmax()), 5, 17})
     check(wl, 0, go, gl, seqs)
+
+
+@pytest.mark.parametrize("k", [5, 7])
+def test_mtp_verify_b32_deeper(k):
+    # 4 and 3 query tokens per sequence: every query group of a split in one launch
+    wl, go, gl = run_step(k, 0)
+    lens = np.array(wl.lens)
+    seqs = sorted({int(lens.argmin()), int(lens.argmax()), 9})
+    check(wl, 0, go, gl, seqs)
+
+
+def test_ctx512k_b1():
+    wl, go, gl = run_step(6, 0)
+    check(wl, 0, go, gl, [0])

@@ -141,7 +141,9 @@ RAGGED = [
     (1, (1, 2, 63, 64, 65, 700)),
     (2, (2, 3, 64, 65, 129, 333)),
     (3, (3, 70, 200)),
+    (4, (4, 64, 1000)),
     (5, (5, 130)),
+    (16, (16, 17, 300)),
 ]
 
 
