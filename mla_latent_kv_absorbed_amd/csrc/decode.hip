@@ -9,39 +9,38 @@
 // against the latent directly is the W_UK absorption, and the LSE combine and
 // W_UV up-projection of the partials follow in kernels.hip.
 //
-// Work decomposition (one workgroup of 4 waves per split, described by a
-// segment record {b, first token, end token, L_b} of the call's schedule):
+// Work decomposition (one workgroup of 8 waves, two per SIMD, per split and
+// query group; a segment record {b, first token, end token, L_b} of the
+// call's schedule describes the split):
 //  * The split streams through LDS in 64-token slots (one page, 72 KiB) of a
-//    two-slot ring, filled by direct global->LDS 16-byte loads: while the
-//    waves consume one slot the next is in flight, and the first two slots
-//    are requested before anything else.  Slot rows are swizzled at 16-byte
-//    granularity (latent chunk c of token t sits at c ^ (t & 15), rope chunk
-//    64+k at 64 + (k ^ ((t >> 1) & 7))) so that both read patterns below are
-//    free of LDS bank conflicts.
+//    two-slot ring, filled by direct global->LDS 16-byte loads (9 per lane
+//    per slot): while the waves consume one slot the next is in flight.  Slot
+//    rows are swizzled at 16-byte granularity (latent chunk c of token t sits
+//    at c ^ (t & 15), rope chunk 64+k at 64 + (k ^ ((t >> 1) & 7))) so that
+//    the read patterns below are free of LDS bank conflicts.
+//  * The query rows come in the same way, ahead of the first slot, into the
+//    second ring position (same swizzle), from where each wave takes its 16
+//    rows into registers; only then is the second slot requested.  The
+//    first slot is thus awaited on its own, not behind later slots.
 //  * The 32*QG query rows (query token, head) are cut into row groups of 16.
-//    Each wave owns one row group and a share of every slot's tokens and
-//    keeps its own running max, sum and 16 x 512 fp32 accumulator (AGPRs); no
-//    wave waits on another inside the loop apart from one barrier per slot.
-//    With one query token two waves share a row group (32 tokens of each slot
-//    apiece) and merge at the end.
-//  * Scores: S^T[token][row] = C_slot . Q^T on v_mfma_f32_16x16x32_bf16, the
-//    cache rows as the A operand (ds_read_b128 of 8 latent values per lane,
-//    eight reads in flight) and the wave's 16 query rows held in registers as
-//    the B operand.
-//  * The S^T accumulator layout (lane = row, 4 tokens per lane) is exactly the
-//    operand layout of P[row][token] in the value product; the latent values
-//    C[token][col] are fetched in that token order with ds_read_b64_tr_b16
-//    (transposing 4 x 16 blocks), so P never leaves registers.  The product
-//    is taken as O^T = C^T . P^T (latent values as the A operand), so that a
-//    lane's accumulator holds 4 consecutive latent columns of one row and the
-//    partials leave the kernel as plain row-major fp32 rows.
-//  * No rescaling inside the loop: a row's reference max is fixed at its
-//    first visible slot, and p = 2^(s - m_ref) may grow to 2^64 (sums stay far
-//    inside fp32).  Each wave also tracks the rows' true maxima; if any score
-//    ever exceeds its reference by more than 64 (log2 units), the workgroup
-//    streams the split a second time with the references set to the true
-//    maxima, where p <= 1.  The accumulators are therefore only ever
-//    accumulated by MFMAs, zeroed, or written to LDS after the loop.
+//    Scores: wave w takes row group w % RG and a 64/TPW-token share of each
+//    slot (TPW = 8 / RG waves per row group) and forms S^T[token][row] =
+//    C_slot . Q^T on v_mfma_f32_16x16x32_bf16: cache rows as the A operand
+//    (ds_read_b128, several in flight), its query rows in registers as B.
+//  * Softmax without rescaling: a row's reference max m_ref is the maximum of
+//    its scores in the split's first slot (taken across the row group's score
+//    waves through LDS), fixed afterwards; p = 2^(s - m_ref) may grow to 2^64
+//    (sums stay far inside fp32).  The score waves also track the true
+//    maxima; if any score exceeds its reference by more than 64 (log2 units),
+//    the workgroup streams the split a second time with the references set to
+//    the true maxima, where p <= 1.
+//  * P (bf16) goes to a small LDS buffer in the B-operand layout of the value
+//    product; after one barrier, wave w accumulates O^T[col][row] = C^T . P^T
+//    for latent columns [64w, 64w + 64) and every query row, the latent
+//    values C^T fetched with ds_read_b64_tr_b16 (transposing 4 x 16 blocks).
+//    Each cached value is thus read once by the value product, and a wave's
+//    accumulators hold complete sums over the split: after the loop they are
+//    scaled by 1 / sum_t p_t and written as row-major fp32 partial rows.
 #include "mla_internal.h"
 
 #include <hip/hip_ext.h>
@@ -51,26 +50,26 @@ namespace {
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kTau = 64.0f;          // log2 headroom of p above the reference max
-constexpr int kQkRing = 8;             // score operand reads in flight per wave
-constexpr int kPvRing = 6;             // value operand column blocks in flight per wave
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
 constexpr int kSlotTok = 64;           // tokens per ring slot (one page)
 constexpr int kSlotBytes = kSlotTok * kRowBytes;   // 73728
-constexpr int kSlots = 2;              // ring slots: kSlots - 1 in flight while one is consumed
-constexpr int kLoadsPerLane = kSlotBytes / 16 / 256;   // 18
+constexpr int kSlots = 2;              // ring slots: one in flight while one is consumed
+constexpr int kLoadsPerLane = kSlotBytes / 16 / kThreads;   // 9
+constexpr int kCbPerWave = kLatent / 16 / kWaves;           // 4 column blocks of 16 per wave
+static_assert(kLoadsPerLane * 16 * kThreads == kSlotBytes, "slot split");
 
-typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Wait until at most `ahead` slots' worth of direct loads (kLoadsPerLane per
-// lane per slot) are still outstanding.
+// Wait until at most `ahead` (0 or 1) slots' worth of direct loads
+// (PER_SLOT per lane per slot) are still outstanding.
 template <int PER_SLOT>
 __device__ __forceinline__ void wait_slots_ahead(int ahead) {
-  if (ahead >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * PER_SLOT) : "memory");
-  else if (ahead == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PER_SLOT) : "memory");
+  if (ahead >= 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PER_SLOT) : "memory");
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
@@ -91,19 +90,26 @@ __device__ __forceinline__ int tile_slot(int tok, int c) {
 }
 
 template <int QG, bool PAGED>
-__global__ void __launch_bounds__(256, 1) splitkv_decode(DecodeParams p) {
-  constexpr int RG = 2 * QG;          // row groups of 16 rows
-  constexpr int TP = 4 / RG;          // waves per row group
-  constexpr int TOKW = kSlotTok / TP; // tokens of each slot one wave handles
-  constexpr int NBLK = TOKW / 16;     // 16-token score blocks per slot
+__global__ void __launch_bounds__(kThreads, 1) splitkv_decode(DecodeParams p) {
+  constexpr int RG = 2 * QG;           // row groups of 16 query rows
+  constexpr int ROWS = 16 * RG;
+  constexpr int TPW = kWaves / RG;     // score waves per row group
+  constexpr int TOKW = kSlotTok / TPW; // tokens of each slot one score wave handles
+  constexpr int NBLK = TOKW / 16;      // 16-token score blocks per slot and wave
+  constexpr int kQkRing = QG == 1 ? 8 : 4;   // score operand reads in flight per wave
+  static_assert((ROWS * kChunksPerRow) % (kLoadsPerLane * 64) == 0, "query rows fill whole waves' loads");
 
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kSlots * kSlotBytes];
+  // P in bf16, [row group][32-token step][row][32 tokens in MFMA k order]
+  __shared__ __attribute__((aligned(16))) uint8_t pbuf[RG * 2 * 16 * 64];
+  __shared__ float stat[3][TPW][ROWS];   // per score wave and row: slot max, sum, true max
+  __shared__ int flags[kWaves];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, n16 = lane & 15;
-  const int rg = wave % RG, tp = wave / RG;
+  const int rg = wave % RG, tq = wave / RG;   // score role: row group, token share
 
   int unit, grp;   // segment (tokens [t_begin, t_end) of sequence b) and query group
   work_item(p.groups, unit, grp);
@@ -112,16 +118,11 @@ __global__ void __launch_bounds__(256, 1) splitkv_decode(DecodeParams p) {
   const int b = seg.x, t_begin = seg.y, t_end = seg.z, L = seg.w;
   if (b < 0 || t_begin >= t_end) return;   // no segment: the combine never reads it
 
-  // Query token of this wave's rows; a repeat of token Sq - 1 (computed, never
-  // written) fills the second half of the last group when Sq is odd.
+  // Query token of the score role's rows; a repeat of token Sq - 1 (computed,
+  // never written) fills the second half of the last group when Sq is odd.
   const int j_grp = QG * grp + (rg >> 1);
-  const bool real = j_grp < p.Sq;
-  const int j = real ? j_grp : p.Sq - 1;
+  const int j = j_grp < p.Sq ? j_grp : p.Sq - 1;
   const int limit = min(t_end, L - p.Sq + j + 1);   // rows of this wave see tokens < limit
-  // partial rows of this wave's row group: [unit][j*32 + h][512] fp32
-  const int rg_glob = 2 * QG * grp + rg;
-  float* out_o = p.part_o + ((size_t)unit * (2 * p.Sq) + rg_glob) * (16 * kLatent);
-  float* out_lse = p.part_lse + (size_t)unit * (p.Sq * 32) + rg_glob * 16;
 
   // Byte offset inside a slot of each 16-byte chunk this lane loads: LDS
   // position P = (wave*kLoadsPerLane + i)*64 + lane holds chunk (tok = P / 72,
@@ -145,9 +146,8 @@ __global__ void __launch_bounds__(256, 1) splitkv_decode(DecodeParams p) {
   auto issue = [&](int ts, int r) {
     const uint8_t* src;
     if constexpr (PAGED) {
-      constexpr int kSlotsPerPage = kPage / kSlotTok;
-      const int page = p.block_table[(size_t)b * p.max_pages + ts / kSlotsPerPage];
-      src = p.cache + (size_t)page * kTileBytes + (ts % kSlotsPerPage) * kSlotBytes;
+      const int page = p.block_table[(size_t)b * p.max_pages + ts];
+      src = p.cache + (size_t)page * kTileBytes;
     } else {
       src = p.cache + ((size_t)b * p.stride_tokens + (size_t)ts * kSlotTok) * kRowBytes;
     }
@@ -166,62 +166,80 @@ __global__ void __launch_bounds__(256, 1) splitkv_decode(DecodeParams p) {
     }
   };
 
-  // The first two slots (both ring positions) are requested before the query
-  // rows are read.
-  const int pro = min(kSlots, nslot);
-  for (int k = 0; k < pro; ++k) issue(s0 + k, k);
-
-  // The wave's 16 query rows, as MFMA B operands: lane holds row n16, 8 dims.
-  bf16x8 q[18];
-  {
-    const uint16_t* qrow = p.qabs + (((size_t)b * p.Sq + j) * 32 + (rg & 1) * 16 + n16) * kRow + g * 8;
-#pragma unroll
-    for (int ks = 0; ks < 18; ++ks) q[ks] = *(const bf16x8*)(qrow + ks * 32);
-  }
-  // Settle the query loads here, once: a wait the compiler placed at their
-  // first use inside the slot loop would count only its own loads and so
-  // also drain the cache slots requested ahead of every iteration.
-#pragma unroll
-  for (int ks = 0; ks < 18; ++ks) asm volatile("" ::"v"(q[ks]));
-
-  // LDS read offsets within a slot.  Score reads: token tok_w + 16*blk + n16,
-  // chunk 4*ks + g, position (4ks + g) ^ n16 = 16*(ks/4) + ((4*(ks%4)) ^ (g ^ n16));
-  // the 16*(ks/4) and 16*blk parts become instruction immediates.
-  const int tok_w = tp * TOKW;
-  const int qk_row = (tok_w + n16) * kRowBytes;
+  // Offsets of the score reads within a 16-row block of a slot (or of the
+  // query rows): row n16, chunk 4*ks + g sits at position (4ks + g) ^ n16 =
+  // 16*(ks/4) + ((4*(ks%4)) ^ (g ^ n16)); rope chunks 64 + ((4kk + g) ^ (n16 >> 1)).
   int qk_off[4];
 #pragma unroll
-  for (int bb = 0; bb < 4; ++bb) qk_off[bb] = qk_row + (((4 * bb) ^ (g ^ n16)) << 4);
+  for (int bb = 0; bb < 4; ++bb) qk_off[bb] = n16 * kRowBytes + (((4 * bb) ^ (g ^ n16)) << 4);
   int rope_off[2];
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) rope_off[kk] = qk_row + ((64 + ((4 * kk + g) ^ (n16 >> 1))) << 4);
-  // Value reads (transposed, 8 bytes): token tok_w + 4g + (n16 >> 2) (+16 for
-  // the upper half of a 32-token step), columns 16*cb + 4*(n16 & 3); chunk
-  // 2cb + ((n16 >> 1) & 1) sits at position 16*(cb/8) + ((2*(cb%8)) ^ v).
-  const int pv_tok = tok_w + 4 * g + (n16 >> 2);
-  const int pv_v = ((n16 >> 1) & 1) ^ (pv_tok & 15);
-  const int pv_row = pv_tok * kRowBytes + (n16 & 1) * 8;
-  int pv_off[8];
-#pragma unroll
-  for (int bb = 0; bb < 8; ++bb) pv_off[bb] = pv_row + (((2 * bb) ^ pv_v) << 4);
+  for (int kk = 0; kk < 2; ++kk) rope_off[kk] = n16 * kRowBytes + ((64 + ((4 * kk + g) ^ (n16 >> 1))) << 4);
+  auto row_chunk = [&](int ks) -> int { return ks < 16 ? qk_off[ks & 3] + (ks >> 2) * 256 : rope_off[ks - 16]; };
 
-  f32x4 o[32];
+  // ---- prologue: the query rows (row r of the group as "token" r) into the
+  // second ring position, the first slot into the first
+  if (wave * kLoadsPerLane * 64 < ROWS * kChunksPerRow) {
+    const uint32_t dst = ring_lds + kSlotBytes + wave * kLoadsPerLane * 1024;
 #pragma unroll
-  for (int cb = 0; cb < 32; ++cb) o[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_ref = kNegInf;   // reference max of row n16 (log2 units), fixed once set
-  float m_true = kNegInf;  // running true max of row n16
+    for (int i = 0; i < kLoadsPerLane; ++i) {
+      const int r = off[i] / kRowBytes;
+      const int jj = min(QG * grp + (r >> 5), p.Sq - 1);
+      const uint8_t* src = (const uint8_t*)p.qabs + (((size_t)b * p.Sq + jj) * 32 + (r & 31)) * kRowBytes +
+                           (off[i] - r * kRowBytes);
+      dma16(src, dst + i * 1024);
+    }
+  }
+  issue(s0, 0);
+  wait_slots_ahead<kLoadsPerLane>(1);   // the query rows (older than the first slot) have landed
+  lds_barrier();
+  bf16x8 q[18];   // this wave's 16 query rows as MFMA B operands: lane holds row n16, 8 dims
+  {
+    const uint8_t* qb = ring + kSlotBytes + rg * 16 * kRowBytes;
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) q[ks] = *(const bf16x8*)(qb + row_chunk(ks));
+  }
+  lds_barrier();   // every wave has its query rows before the second slot overwrites them
+  if (nslot > 1) issue(s0 + 1, 1);
+
+  // Value reads (transposed, 8 bytes): token 4g + (n16 >> 2) (+16 for the
+  // upper half of a 32-token step, +32 for the second step), columns
+  // 16*cb + 4*(n16 & 3); chunk 2cb + ((n16 >> 1) & 1) sits at position
+  // 16*(cb/8) + ((2*(cb%8)) ^ v).  This wave's blocks: cb = 4*wave + c.
+  int pv_off[kCbPerWave];
+  {
+    const int pv_tok = 4 * g + (n16 >> 2);
+    const int pv_v = ((n16 >> 1) & 1) ^ (pv_tok & 15);
+    const int pv_row = pv_tok * kRowBytes + (n16 & 1) * 8;
+#pragma unroll
+    for (int c = 0; c < kCbPerWave; ++c) {
+      const int cb = kCbPerWave * wave + c;
+      pv_off[c] = pv_row + (((2 * (cb & 7)) ^ pv_v) << 4) + (cb >> 3) * 256;
+    }
+  }
+  // P reads: row n16 of a row group, one 32-token step: 16 bytes at k = 8g.
+  const int pb_rd = n16 * 64 + g * 16;
+
+  f32x4 o[kCbPerWave][RG];
+#pragma unroll
+  for (int c = 0; c < kCbPerWave; ++c)
+#pragma unroll
+    for (int r2 = 0; r2 < RG; ++r2) o[c][r2] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_ref = kNegInf;   // reference max of row rg*16 + n16 (log2 units), fixed once set
+  float m_true = kNegInf;  // running true max of that row over this wave's tokens
   float l_part = 0.f;      // this lane's share of the row sum
   bool overflow = false;   // some score exceeded m_ref + kTau (wave-uniform)
+  int pass = 0;
 
-  auto process = [&](const uint8_t* T, int ts) __attribute__((always_inline)) {
-    const int abs_w = ts * kSlotTok + tok_w;   // absolute position of the wave's first token
+  auto process = [&](const uint8_t* T, int ts, bool first) __attribute__((always_inline)) {
+    const int tok0 = tq * TOKW;                // first token of this wave's share
+    const int abs_w = ts * kSlotTok + tok0;    // its absolute position
 
     // ---- scores S^T = C . Q^T, 16 tokens per block; reads run kQkRing ahead
     constexpr int NQK = NBLK * 18;
     auto qk_src = [&](int i) -> const bf16x8* {
       const int blk = i % NBLK, ks = i / NBLK;
-      const uint8_t* base = T + blk * 16 * kRowBytes;
-      return (const bf16x8*)(ks < 16 ? base + qk_off[ks & 3] + (ks >> 2) * 256 : base + rope_off[ks - 16]);
+      return (const bf16x8*)(T + (tok0 + blk * 16) * kRowBytes + row_chunk(ks));
     };
     f32x4 s[NBLK];
 #pragma unroll
@@ -241,7 +259,7 @@ __global__ void __launch_bounds__(256, 1) splitkv_decode(DecodeParams p) {
       }
     }
 
-    // ---- scale, mask, slot max of row n16
+    // ---- scale, mask, slot max of row n16 over this wave's tokens
     float mt = kNegInf;
 #pragma unroll
     for (int blk = 0; blk < NBLK; ++blk)
@@ -254,73 +272,57 @@ __global__ void __launch_bounds__(256, 1) splitkv_decode(DecodeParams p) {
       }
     mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-
-    // ---- reference max: set at the row's first visible slot (its
-    // accumulator is still zero then), never moved afterwards
     m_true = fmaxf(m_true, mt);
-    m_ref = (m_ref == kNegInf) ? mt : m_ref;
+
+    // ---- reference max: the row's maximum over the split's first slot, the
+    // same for every wave of the row group
+    if (first && pass == 0) {
+      if (g == 0) stat[0][tq][rg * 16 + n16] = mt;
+      lds_barrier();
+      float m = stat[0][0][rg * 16 + n16];
+#pragma unroll
+      for (int k = 1; k < TPW; ++k) m = fmaxf(m, stat[0][k][rg * 16 + n16]);
+      m_ref = m;
+    }
     overflow = overflow || (__builtin_amdgcn_ballot_w64(mt > m_ref + kTau) != 0);
 
-    // ---- P = 2^(s - m_ref) in bf16, in the A-operand layout of P . C
+    // ---- P = 2^(s - m_ref) in bf16 into the value product's B-operand
+    // layout: token t of the slot is step t/32, k = 8*((t%16)/4) + 4*((t/16)%2) + t%4
     const float mref = (m_ref == kNegInf) ? 0.f : m_ref;
-    __bf16 pe[NBLK][4];
 #pragma unroll
-    for (int blk = 0; blk < NBLK; ++blk)
+    for (int blk = 0; blk < NBLK; ++blk) {
+      s16x4 pk;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        pe[blk][i] = (__bf16)__builtin_amdgcn_exp2f(s[blk][i] - mref);
-        l_part += (float)pe[blk][i];
+        const __bf16 e = (__bf16)__builtin_amdgcn_exp2f(s[blk][i] - mref);
+        l_part += (float)e;
+        pk[i] = __builtin_bit_cast(short, e);
       }
+      const int t16 = tok0 + blk * 16;   // first token of the block (a multiple of 16)
+      const int ks = t16 >> 5, bb = (t16 >> 4) & 1;
+      *(s16x4*)(pbuf + ((rg * 2 + ks) * 16 + n16) * 64 + (8 * g + 4 * bb) * 2) = pk;
+    }
+    lds_barrier();
 
-    // ---- O += P . C[:, 0:512]; value operand by transposed LDS reads
-    auto pv_src = [&](int cb) -> const uint8_t* { return T + pv_off[cb & 7] + (cb >> 3) * 256; };
-    if constexpr (NBLK == 1) {
-      // 16 tokens: v_mfma_f32_16x16x16_bf16, one 4-token transposed read per block
-      s16x4 pa;
+    // ---- O^T += C^T . P^T over this wave's 4 column blocks and all rows
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pa[i] = __builtin_bit_cast(short, pe[0][i]);
-      s16x4 rv[kPvRing];
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 pb[RG];
 #pragma unroll
-      for (int i = 0; i < kPvRing; ++i) rv[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)pv_src(i));
-      __builtin_amdgcn_sched_group_barrier(0x100, kPvRing, 1);
+      for (int r2 = 0; r2 < RG; ++r2) pb[r2] = *(const bf16x8*)(pbuf + (r2 * 2 + ks) * 1024 + pb_rd);
+      s16x4 lo[kCbPerWave], hi[kCbPerWave];
 #pragma unroll
-      for (int cb = 0; cb < 32; ++cb) {
-        o[cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(rv[cb % kPvRing], pa, o[cb], 0, 0, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        if (cb + kPvRing < 32) {
-          rv[cb % kPvRing] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)pv_src(cb + kPvRing));
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
-        }
+      for (int c = 0; c < kCbPerWave; ++c) {
+        const uint8_t* a = T + pv_off[c] + ks * 32 * kRowBytes;
+        lo[c] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)a);
+        hi[c] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(a + 16 * kRowBytes));
       }
-    } else {
-      // 32-token k-steps: v_mfma_f32_16x16x32_bf16, two transposed reads per
-      // block (tokens 4g+e and 16+4g+e, the order of the score accumulator)
-      constexpr int NKV = NBLK / 2;
-      constexpr int NPV = NKV * 32;
-      bf16x8 pa[NKV];
 #pragma unroll
-      for (int kk = 0; kk < NKV; ++kk)
+      for (int c = 0; c < kCbPerWave; ++c) {
+        const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo[c], hi[c], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) { pa[kk][i] = pe[2 * kk][i]; pa[kk][4 + i] = pe[2 * kk + 1][i]; }
-      auto pv_at = [&](int i) -> const uint8_t* { return pv_src(i % 32) + (i / 32) * 32 * kRowBytes; };
-      s16x4 lo[kPvRing], hi[kPvRing];
-#pragma unroll
-      for (int i = 0; i < kPvRing; ++i) {
-        lo[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)pv_at(i));
-        hi[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(pv_at(i) + 16 * kRowBytes));
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPvRing, 1);
-#pragma unroll
-      for (int i = 0; i < NPV; ++i) {
-        const int kk = i / 32, cb = i % 32, r = i % kPvRing;
-        const s16x8 both = __builtin_shufflevector(lo[r], hi[r], 0, 1, 2, 3, 4, 5, 6, 7);
-        o[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, both), pa[kk], o[cb], 0, 0, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        if (i + kPvRing < NPV) {
-          lo[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)pv_at(i + kPvRing));
-          hi[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(pv_at(i + kPvRing) + 16 * kRowBytes));
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-        }
+        for (int r2 = 0; r2 < RG; ++r2)
+          o[c][r2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[r2], o[c][r2], 0, 0, 0);
       }
     }
   };
@@ -328,88 +330,74 @@ __global__ void __launch_bounds__(256, 1) splitkv_decode(DecodeParams p) {
   // Slot loop.  Iteration it: wait for slot it (its loads and everyone
   // else's, via the barrier, which also frees the slot consumed at it - 1),
   // request slot it + 1 into that freed ring position (slot 1 came with the
-  // prologue), consume slot it.  Only while slot 0 is awaited can a later
-  // slot's loads be outstanding.
-  // A second pass runs only if some row outgrew its reference by kTau.
-  int pass = 0;
+  // prologue), consume slot it.  A second pass runs only if some row outgrew
+  // its reference by kTau.
   for (;;) {
     for (int it = 0; it < nslot; ++it) {
       wait_slots_ahead<kLoadsPerLane>((it == 0 && nslot > 1) ? 1 : 0);
       lds_barrier();
       if (it >= 1 && it + 1 < nslot) issue(s0 + it + 1, (it + 1) % kSlots);
-      process(ring + (it % kSlots) * kSlotBytes, s0 + it);
+      process(ring + (it % kSlots) * kSlotBytes, s0 + it, it == 0);
     }
-    lds_barrier();   // every wave is done with the last slot
-    int* flag = (int*)ring;
-    if (lane == 0) flag[wave] = overflow ? 1 : 0;
+    // row sums and true maxima of each score wave's token share
+    float lsum = l_part;
+    lsum += __shfl_xor(lsum, 16, 64);
+    lsum += __shfl_xor(lsum, 32, 64);
+    if (g == 0) {
+      stat[1][tq][rg * 16 + n16] = lsum;
+      stat[2][tq][rg * 16 + n16] = m_true;
+    }
+    if (lane == 0) flags[wave] = overflow ? 1 : 0;
     lds_barrier();
-    const bool again = (flag[0] | flag[1] | flag[2] | flag[3]) != 0;
-    lds_barrier();
-    if (!again || pass == 1) break;
+    int any = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) any |= flags[w];
+    if (any == 0 || pass == 1) break;
     pass = 1;
-    m_ref = m_true;
+    float m = stat[2][0][rg * 16 + n16];
+#pragma unroll
+    for (int k = 1; k < TPW; ++k) m = fmaxf(m, stat[2][k][rg * 16 + n16]);
+    m_ref = m;
     overflow = false;
     l_part = 0.f;
 #pragma unroll
-    for (int cb = 0; cb < 32; ++cb) o[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < pro; ++k) issue(s0 + k, k);
+    for (int c = 0; c < kCbPerWave; ++c)
+#pragma unroll
+      for (int r2 = 0; r2 < RG; ++r2) o[c][r2] = f32x4{0.f, 0.f, 0.f, 0.f};
+    lds_barrier();   // flags and stat read by everyone before they are written again
+    for (int k = 0; k < min(kSlots, nslot); ++k) issue(s0 + k, k);
   }
 
-  // ---- finalize.  The accumulators go to LDS straight from AGPRs; each
-  // wave then reads them back four values at a time, merges the two token
-  // halves of its row group (one query token) and normalises.  Keeping every
-  // use of the accumulators out of the vector ALU lets them stay in AGPRs.
-  float l_row = l_part;
-  l_row += __shfl_xor(l_row, 16, 64);
-  l_row += __shfl_xor(l_row, 32, 64);
-
-  constexpr int kRegion = 32 * 64 * 4 + 32;   // floats: accumulators + m + l
-  float* mine = (float*)ring + wave * kRegion;
+  // ---- finalize: row r = r2*16 + n16 of the group is query token
+  // QG*grp + r/32, head r%32; partial rows [unit][j*32 + h][512] fp32
+  const size_t unit_rows = (size_t)unit * p.Sq * 32;
 #pragma unroll
-  for (int cb = 0; cb < 32; ++cb) *(f32x4*)(mine + (cb * 64 + lane) * 4) = o[cb];
-  if (lane < 16) {
-    mine[32 * 64 * 4 + lane] = m_ref;
-    mine[32 * 64 * 4 + 16 + lane] = l_row;
-  }
-  lds_barrier();
-
-  float a_own = 1.f, a_other = 0.f;
-  const float* other = nullptr;
-  if constexpr (TP == 2) {
-    if (tp == 1) return;
-    other = (const float*)ring + (wave + RG) * kRegion;   // the wave sharing these rows
-    const float m1 = other[32 * 64 * 4 + n16], l1 = other[32 * 64 * 4 + 16 + n16];
-    const float mm = fmaxf(m_ref, m1);
-    a_own = (m_ref == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_ref - mm);
-    a_other = (m1 == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
-    l_row = l_row * a_own + l1 * a_other;
-    m_ref = mm;
-  }
-  // lane (g, n16) holds row n16, columns 16*cb + 4g .. 16*cb + 4g + 3
-  if (!real) return;
-  const float inv = (l_row > 0.f) ? 1.f / l_row : 0.f;
-  const float s_own = a_own * inv, s_other = a_other * inv;
-  float* orow = out_o + n16 * kLatent + 4 * g;
+  for (int r2 = 0; r2 < RG; ++r2) {
+    const int jr = QG * grp + (r2 >> 1);
+    if (jr >= p.Sq) continue;
+    const int r = r2 * 16 + n16;
+    float lrow = stat[1][0][r];
 #pragma unroll
-  for (int cb = 0; cb < 32; ++cb) {
-    f32x4 v = *(const f32x4*)(mine + (cb * 64 + lane) * 4);
+    for (int k = 1; k < TPW; ++k) lrow += stat[1][k][r];
+    const float inv = (lrow > 0.f) ? 1.f / lrow : 0.f;
+    float* orow = p.part_o + (unit_rows + (size_t)jr * 32 + (r & 31)) * kLatent + 4 * g;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] *= s_own;
-    if constexpr (TP == 2) {
-      const f32x4 w = *(const f32x4*)(other + (cb * 64 + lane) * 4);
+    for (int c = 0; c < kCbPerWave; ++c) {
+      f32x4 v = o[c][r2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = fmaf(w[i], s_other, v[i]);
+      for (int i = 0; i < 4; ++i) v[i] *= inv;
+      *(f32x4*)(orow + (kCbPerWave * wave + c) * 16) = v;
     }
-    *(f32x4*)(orow + cb * 16) = v;
+    if (tq == 0 && r2 == rg && g == 0)
+      p.part_lse[unit_rows + (size_t)jr * 32 + (r & 31)] = (lrow > 0.f) ? m_ref + __log2f(lrow) : kNegInf;
   }
-  if (lane < 16) out_lse[lane] = (l_row > 0.f) ? m_ref + __log2f(l_row) : kNegInf;
 }
 
 }  // namespace
 
 hipError_t launch_decode(const DecodeParams& p, int segments, int query_group, bool paged, hipStream_t stream,
                          hipEvent_t ev_start, hipEvent_t ev_stop) {
-  const dim3 grid(decode_grid(segments, p.groups)), block(256);
+  const dim3 grid(decode_grid(segments, p.groups)), block(kThreads);
   // with events, the dispatch itself records them at kernel start and end
   if (query_group == 1) {
     if (paged) hipExtLaunchKernelGGL((splitkv_decode<1, true>), grid, block, 0, stream, ev_start, ev_stop, 0, p);
