@@ -224,7 +224,10 @@ mla_status mla_decode_workspace_size(const mla_shape* shape /* host */, int32_t 
                                      int32_t max_ctx_len, int32_t kv_chunk,
                                      size_t* bytes /* host */);
 
-/* The kv_chunk the library would use for kv_chunk = 0 (host). */
+/* The kv_chunk the library would use for kv_chunk = 0 when all B sequences
+ * hold max_ctx_len tokens, for the bf16 cache format (host).  (The 8-bit
+ * format serves each query token with its own workgroups, so for Sq > 1 it
+ * aims at fewer, longer splits.) */
 mla_status mla_decode_auto_chunk(int32_t B, int32_t Sq, int32_t max_ctx_len, int32_t* kv_chunk /* host */);
 
 /* Kernel timing, a profiling aid (not needed to compute anything).

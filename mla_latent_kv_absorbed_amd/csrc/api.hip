@@ -153,7 +153,8 @@ mla_status decode_common(const mla_shape* shape, const StepInputs& step, const v
       return MLA_ERR_ALIGN;
   }
   const int target = compute_units();
-  const int groups = query_groups(Sq);
+  const bool fp8 = shape->kv_cache_dtype == MLA_CACHE_FP8_E4M3;
+  const int groups = query_groups(Sq, fp8);
   const int64_t segs = max_segments(B, max_ctx_len, kv_chunk, target);
   // one split-KV launch covers every (segment, query group) pair; its
   // workgroups times 256 threads must fit in 32 bits
@@ -191,7 +192,7 @@ mla_status decode_common(const mla_shape* shape, const StepInputs& step, const v
   pp.block_table = block_table;
   pp.max_pages = max_pages;
   pp.paged = paged ? 1 : 0;
-  pp.fp8 = shape->kv_cache_dtype == MLA_CACHE_FP8_E4M3 ? 1 : 0;
+  pp.fp8 = fp8 ? 1 : 0;
   pp.B = B;
   pp.fixed_tiles = kv_chunk / kPage;
   pp.target_segs = std::max(1, target / groups);   // about one workgroup per compute unit
@@ -218,8 +219,8 @@ mla_status decode_common(const mla_shape* shape, const StepInputs& step, const v
   {
     hipEvent_t ev0 = timed ? g_timing.ev[2 * g_timing.used] : nullptr;
     hipEvent_t ev1 = timed ? g_timing.ev[2 * g_timing.used + 1] : nullptr;
-    const hipError_t e = pp.fp8 ? launch_decode_fp8(p, (int)segs, query_group(Sq), paged, s, ev0, ev1)
-                                : launch_decode(p, (int)segs, query_group(Sq), paged, s, ev0, ev1);
+    const hipError_t e = fp8 ? launch_decode_fp8(p, (int)segs, paged, s, ev0, ev1)
+                             : launch_decode(p, (int)segs, query_group(Sq, false), paged, s, ev0, ev1);
     if (e != hipSuccess) return MLA_ERR_DEVICE;
   }
   if (timed) ++g_timing.used;
@@ -430,7 +431,7 @@ mla_status mla_timing_disable(void) {
 mla_status mla_decode_auto_chunk(int32_t B, int32_t Sq, int32_t max_ctx_len, int32_t* kv_chunk) {
   if (kv_chunk == nullptr) return MLA_ERR_NULL;
   if (B < 0 || Sq < 1 || Sq > kMaxSq || max_ctx_len < Sq) return MLA_ERR_RANGE;
-  *kv_chunk = balanced_chunk(B < 1 ? 1 : B, max_ctx_len, std::max(1, compute_units() / query_groups(Sq)));
+  *kv_chunk = balanced_chunk(B < 1 ? 1 : B, max_ctx_len, std::max(1, compute_units() / query_groups(Sq, false)));
   return MLA_OK;
 }
 

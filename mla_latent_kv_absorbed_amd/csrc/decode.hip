@@ -60,6 +60,16 @@ constexpr int kCbPerWave = kLatent / 16 / kWaves;           // 4 column blocks o
 static_assert(kLoadsPerLane * 16 * kThreads == kSlotBytes, "slot split");
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+typedef __attribute__((address_space(3))) const uint8_t lds_cu8;
+typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8_t;
+
+// LDS address of a ring position, opaque to the compiler: all reads of a
+// slot then share one base register and use immediate offsets, instead of
+// addresses precomputed for every ring position.
+__device__ __forceinline__ lds_cu8* slot_base(uint32_t lds) {
+  asm volatile("" : "+s"(lds));
+  return (lds_cu8*)lds;
+}
 
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -231,15 +241,15 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode(DecodeParams p) {
   bool overflow = false;   // some score exceeded m_ref + kTau (wave-uniform)
   int pass = 0;
 
-  auto process = [&](const uint8_t* T, int ts, bool first) __attribute__((always_inline)) {
+  auto process = [&](lds_cu8* T, int ts, bool first) __attribute__((always_inline)) {
     const int tok0 = tq * TOKW;                // first token of this wave's share
     const int abs_w = ts * kSlotTok + tok0;    // its absolute position
 
     // ---- scores S^T = C . Q^T, 16 tokens per block; reads run kQkRing ahead
     constexpr int NQK = NBLK * 18;
-    auto qk_src = [&](int i) -> const bf16x8* {
+    auto qk_src = [&](int i) -> lds_bf16x8_t* {
       const int blk = i % NBLK, ks = i / NBLK;
-      return (const bf16x8*)(T + (tok0 + blk * 16) * kRowBytes + row_chunk(ks));
+      return (lds_bf16x8_t*)(T + (tok0 + blk * 16) * kRowBytes + row_chunk(ks));
     };
     f32x4 s[NBLK];
 #pragma unroll
@@ -313,7 +323,7 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode(DecodeParams p) {
       s16x4 lo[kCbPerWave], hi[kCbPerWave];
 #pragma unroll
       for (int c = 0; c < kCbPerWave; ++c) {
-        const uint8_t* a = T + pv_off[c] + ks * 32 * kRowBytes;
+        lds_cu8* a = T + pv_off[c] + ks * 32 * kRowBytes;
         lo[c] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)a);
         hi[c] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(a + 16 * kRowBytes));
       }
@@ -337,7 +347,7 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode(DecodeParams p) {
       wait_slots_ahead<kLoadsPerLane>((it == 0 && nslot > 1) ? 1 : 0);
       lds_barrier();
       if (it >= 1 && it + 1 < nslot) issue(s0 + it + 1, (it + 1) % kSlots);
-      process(ring + (it % kSlots) * kSlotBytes, s0 + it, it == 0);
+      process(slot_base(ring_lds + (it % kSlots) * kSlotBytes), s0 + it, it == 0);
     }
     // row sums and true maxima of each score wave's token share
     float lsum = l_part;

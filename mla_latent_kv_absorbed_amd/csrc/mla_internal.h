@@ -106,10 +106,13 @@ struct DecodeParams {
 
 // Query tokens per split-KV workgroup, and the number of such query groups
 // that cover Sq tokens.  A group of two keeps 64 query rows (4 row groups of
-// 16, one per wave); a single query token uses 32 rows.  For odd Sq > 1 the
-// last group repeats token Sq - 1 in its second half and writes nothing for it.
-inline int query_group(int Sq) { return Sq == 1 ? 1 : kMaxQueryGroup; }
-inline int query_groups(int Sq) { return (Sq + query_group(Sq) - 1) / query_group(Sq); }
+// 16); a single query token uses 32 rows.  For odd Sq > 1 the last group
+// repeats token Sq - 1 in its second half and writes nothing for it.  The
+// 8-bit cache kernel takes one query token per workgroup: with two, its
+// per-wave registers (query rows, accumulators, widened codes) exceed what
+// two waves per SIMD leave.
+inline int query_group(int Sq, bool fp8) { return (Sq == 1 || fp8) ? 1 : kMaxQueryGroup; }
+inline int query_groups(int Sq, bool fp8) { return (Sq + query_group(Sq, fp8) - 1) / query_group(Sq, fp8); }
 
 // Workgroups of one split-KV launch: every (segment, query group) pair.
 // The device hands consecutive workgroups to its 8 XCDs in turn (workgroup
@@ -220,7 +223,7 @@ hipError_t launch_append(uint8_t* cache, int64_t num_slots, const uint16_t* c_kv
                          hipStream_t stream);
 hipError_t launch_append_fp8(uint8_t* cache, const uint16_t* c_kv, int64_t ld_c, const uint16_t* k_pe,
                              int64_t ld_k, const int64_t* slots, int64_t n, hipStream_t stream);
-hipError_t launch_decode_fp8(const DecodeParams& p, int segments, int query_group, bool paged,
-                             hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop);
+hipError_t launch_decode_fp8(const DecodeParams& p, int segments, bool paged, hipStream_t stream,
+                             hipEvent_t ev_start, hipEvent_t ev_stop);
 
 }  // namespace mla
