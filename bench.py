@@ -44,7 +44,7 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
 BYTES_PER_TOKEN_LAYER = 1152    # 576 bf16 cached values per token per layer
 BYTES_PER_TOKEN_LAYER_FP8 = 656  # 512 E4M3 codes + 4 fp32 scales + 64 bf16 rope values
 COUNTERS = os.path.join(ROOT, "profiles", "splitkv_decode_counters.json")
-DECODE_SRC = os.path.join(ROOT, "mla_latent_kv_absorbed_amd", "csrc", "decode.hip")
+DECODE_SRC = [os.path.join(ROOT, "mla_latent_kv_absorbed_amd", "csrc", f) for f in ("decode.hip", "mla_internal.h")]
 
 
 def log(msg):
@@ -52,8 +52,12 @@ def log(msg):
 
 
 def source_hash() -> str:
-    with open(DECODE_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the split-KV kernel's sources (the kernel file and the shared definitions)."""
+    h = hashlib.sha256()
+    for path in DECODE_SRC:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def run_workload(k: int, steps: int, warmup: int, use_graph: bool, kv_chunk=None, label="", cache_dtype="bf16"):
@@ -220,8 +224,8 @@ def summarize_counters(fetch_csv: str, write_csv: str, copy_bytes: int, workload
         scale = (copy_bytes / 1024.0) / copy_kib if copy_kib else None
         res[f"{counter}_copy_kib"] = copy_kib
         res[f"{counter}_scale"] = scale
-        for short, key in (("splitkv_decode", "splitkv_decode"), ("combine_upproject", "combine_upproject"),
-                           ("prep_query", "prep_query")):
+        for short, key in (("splitkv_decode", "splitkv_decode<"), ("combine_blocks", "combine_blocks"),
+                           ("finalize_out", "finalize_out"), ("prep_query", "prep_query")):
             vals = [v for (cn, kn), vs in rows.items() if cn == counter and key in kn for v in vs]
             if vals:
                 kib = statistics.mean(vals)

@@ -212,7 +212,7 @@ mla_status decode_common(const mla_shape* shape, const StepInputs& step, const v
   p.segments = (int)segs;
   p.groups = groups;
   p.scale_log2 = scale_log2;
-  p.part_o = (float*)(ws + wl.part_o);
+  p.part_o = (uint16_t*)(ws + wl.part_o);
   p.part_lse = (float*)(ws + wl.part_lse);
   p.zero_row = zero_row;
   const bool timed = g_timing.on && g_timing.used < g_timing.capacity;

@@ -383,7 +383,7 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode_fp8(DecodeParams p
   }
 
   // ---- finalize: row r = r2*16 + n16 of the group is query token
-  // QG*grp + r/32, head r%32; partial rows [unit][j*32 + h][512] fp32
+  // QG*grp + r/32, head r%32; partial rows [unit][j*32 + h][512] bf16
   const size_t unit_rows = (size_t)unit * p.Sq * 32;
 #pragma unroll
   for (int r2 = 0; r2 < RG; ++r2) {
@@ -394,13 +394,13 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode_fp8(DecodeParams p
 #pragma unroll
     for (int k = 1; k < TPW; ++k) lrow += stat[1][k][r];
     const float inv = (lrow > 0.f) ? 1.f / lrow : 0.f;
-    float* orow = p.part_o + (unit_rows + (size_t)jr * 32 + (r & 31)) * kLatent + 4 * g;
+    uint16_t* orow = p.part_o + (unit_rows + (size_t)jr * 32 + (r & 31)) * kLatent + 4 * g;
 #pragma unroll
     for (int c = 0; c < kCbPerWave; ++c) {
-      f32x4 v = o[c][r2];
+      s16x4 v;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] *= inv;
-      *(f32x4*)(orow + (kCbPerWave * wave + c) * 16) = v;
+      for (int i = 0; i < 4; ++i) v[i] = __builtin_bit_cast(short, (__bf16)(o[c][r2][i] * inv));
+      *(s16x4*)(orow + (kCbPerWave * wave + c) * 16) = v;
     }
     if (tq == 0 && r2 == rg && g == 0)
       p.part_lse[unit_rows + (size_t)jr * 32 + (r & 31)] = (lrow > 0.f) ? m_ref + __log2f(lrow) : kNegInf;

@@ -331,7 +331,7 @@ __global__ void __launch_bounds__(256) combine_blocks(CombineParams p) {
   const int seg0 = p.seg_start[b];
   const int nseg = min(p.seg_start[b + 1], p.max_segs) - seg0;
   const size_t unit_rows = (size_t)p.Sq * kHeads;
-  const float* obase = p.part_o + ((size_t)seg0 * unit_rows + j * kHeads + h) * kLatent + cb * 64 + 4 * c4;
+  const uint16_t* obase = p.part_o + ((size_t)seg0 * unit_rows + j * kHeads + h) * kLatent + cb * 64 + 4 * c4;
   const float* lbase = p.part_lse + (size_t)seg0 * unit_rows + j * kHeads + h;
   const size_t ostride = unit_rows * kLatent;
 
@@ -339,12 +339,12 @@ __global__ void __launch_bounds__(256) combine_blocks(CombineParams p) {
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int s0 = grp; s0 < nseg; s0 += kCombGroups * kCombBatch) {
     float l[kCombBatch];
-    f32x4 o4[kCombBatch];
+    uint2 o4[kCombBatch];   // 4 bf16 values
 #pragma unroll
     for (int k = 0; k < kCombBatch; ++k) {
       const int s = min(s0 + k * kCombGroups, nseg - 1);   // past the end: re-read, weight 0 below
       l[k] = lbase[s * unit_rows];
-      o4[k] = *(const f32x4*)(obase + s * ostride);
+      o4[k] = *(const uint2*)(obase + s * ostride);
     }
     __builtin_amdgcn_sched_barrier(0);   // every load of the batch in flight before the first use
 #pragma unroll
@@ -362,8 +362,10 @@ __global__ void __launch_bounds__(256) combine_blocks(CombineParams p) {
     for (int k = 0; k < kCombBatch; ++k) {
       const float wt = (l[k] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(l[k] - bm);
       wsum += wt;
+      const float ov[4] = {__uint_as_float(o4[k].x << 16), __uint_as_float(o4[k].x & 0xFFFF0000u),
+                           __uint_as_float(o4[k].y << 16), __uint_as_float(o4[k].y & 0xFFFF0000u)};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = fmaf(wt, o4[k][i], acc[i]);
+      for (int i = 0; i < 4; ++i) acc[i] = fmaf(wt, ov[i], acc[i]);
     }
   }
   red_acc[grp][c4] = acc;

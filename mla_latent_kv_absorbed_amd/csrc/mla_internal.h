@@ -51,7 +51,7 @@ constexpr int kMinTilesPerSplit = 2;
 struct WorkspaceLayout {
   size_t qabs;      // bf16 [rows][32][576]: [W_UK^T q_nope | rotated q_pe]
   size_t qres;      // fp32 [rows][32][512]: W_UK^T q_nope - bf16(W_UK^T q_nope)
-  size_t part_o;    // fp32 [max_segs][Sq*32][512]: normalised segment partials
+  size_t part_o;    // bf16 [max_segs][Sq*32][512]: normalised segment partials
   size_t part_lse;  // fp32 [max_segs][Sq*32], log2 domain
   size_t seg_desc;  // int4 [max_segs]: {b, first token, end token, L_b}; b = -1: none
   size_t seg_start; // int32 [B + 1]
@@ -71,7 +71,7 @@ inline WorkspaceLayout workspace_layout(int B, int Sq, int max_segs) {
   size_t off = 0;
   w.qabs = off;      off = align256(off + hrows * kRow * 2);
   w.qres = off;      off = align256(off + hrows * kLatent * 4);
-  w.part_o = off;    off = align256(off + size_t(max_segs) * seq_rows * kLatent * 4);
+  w.part_o = off;    off = align256(off + size_t(max_segs) * seq_rows * kLatent * 2);
   w.part_lse = off;  off = align256(off + size_t(max_segs) * seq_rows * 4);
   w.seg_desc = off;  off = align256(off + size_t(max_segs) * 16);
   w.seg_start = off; off = align256(off + (size_t(B) + 1) * 4);
@@ -99,7 +99,7 @@ struct DecodeParams {
   int32_t groups;               // query groups per segment (see work_item)
   int32_t Sq;                   // query tokens per sequence
   float scale_log2;             // softmax_scale * log2(e)
-  float* part_o;
+  uint16_t* part_o;             // bf16 normalised partial rows
   float* part_lse;
   const uint8_t* zero_row;      // kRowBytes zero bytes
 };
@@ -192,7 +192,7 @@ struct PrepParams {
 };
 
 struct CombineParams {
-  const float* part_o;
+  const uint16_t* part_o;
   const float* part_lse;
   const int32_t* seg_start;
   int32_t max_segs;

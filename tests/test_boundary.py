@@ -113,11 +113,12 @@ def test_workspace_size_and_auto_chunk():
         chunk = M.mla_decode_auto_chunk(B, Sq, L)
         assert chunk % 64 == 0 and chunk >= 128
         assert B * -(-L // chunk) <= 256 or chunk == 128
-        # partials for up to 256 + B segments, plus the query rows
+        # partials (512 bf16 + one fp32 LSE per row) for up to 256 + B
+        # segments, plus the query rows
         need = M.mla_decode_workspace_size(B, Sq, L)
-        assert need >= B * Sq * 32 * (576 * 2 + 512 * 4) + (256 + B) * Sq * 32 * 513 * 4
+        assert need >= B * Sq * 32 * (576 * 2 + 512 * 4) + (256 + B) * Sq * 32 * (512 * 2 + 4)
         fixed = M.mla_decode_workspace_size(B, Sq, L, kv_chunk=128)
-        assert fixed >= B * Sq * 32 * (576 * 2 + 512 * 4) + B * -(-L // 128) * Sq * 32 * 513 * 4
+        assert fixed >= B * Sq * 32 * (576 * 2 + 512 * 4) + B * -(-L // 128) * Sq * 32 * (512 * 2 + 4)
     with pytest.raises(M.MlaError):
         M.mla_decode_workspace_size(1, 1, 100, kv_chunk=65)
     # an empty batch needs no workspace and must not trip the split heuristic
