@@ -261,6 +261,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=1, help="workload index (1 = 32K, 3 = 256K)")
+    ap.add_argument("--kv-chunk", type=int, default=None,
+                    help="tokens per split for the main workload (0: device-balanced; default: the workload's own)")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-256k", action="store_true", help="skip the 256K report")
@@ -287,7 +289,8 @@ def main():
     torch.cuda.init()
     if args.copy_calibration_mb:
         copy_calibration(args.copy_calibration_mb << 20)
-    main_res = run_workload(args.config, args.steps, args.warmup, not args.no_graph, label=f"config{args.config}")
+    main_res = run_workload(args.config, args.steps, args.warmup, not args.no_graph, kv_chunk=args.kv_chunk,
+                            label=f"config{args.config}")
     log(f"[config{args.config}] {json.dumps(main_res)}")
     extra = None
     if not args.no_256k and args.config != 3:
