@@ -230,6 +230,37 @@ mla_status mla_decode_workspace_size(const mla_shape* shape /* host */, int32_t 
  * aims at fewer, longer splits.) */
 mla_status mla_decode_auto_chunk(int32_t B, int32_t Sq, int32_t max_ctx_len, int32_t* kv_chunk /* host */);
 
+/* Workspace bytes mla_prefill needs for a context of ctx_len tokens (host):
+ * the expanded rows, 16,512 B per token (ctx_len rounded up to 128).
+ * MLA_ERR_UNSUPPORTED for the 8-bit cache format. */
+mla_status mla_prefill_workspace_size(const mla_shape* shape /* host */, int32_t ctx_len,
+                                      size_t* bytes /* host */);
+
+/* Chunked prefill of one sequence, in the un-absorbed form.  The chunk's Tq
+ * query tokens sit at positions p = L - Tq + j (L = ctx_len; their cache rows
+ * are already written, e.g. by mla_rope_yarn + mla_cache_append) and each sees
+ * tokens 0..p.  kv_b_proj expands every cached latent into per-head keys and
+ * values ([MLA-arch]: "实时展开"):
+ *   K_nope[t][h] = W_UK[h] c_t,  V[t][h] = W_UV[h] c_t   (bf16, fp32 sums)
+ *   s_jt = softmax_scale * (q_nope[j][h] . K_nope[t][h] + q_pe[j][h] . k_pe_t)
+ *   out[j][h] = sum_t softmax(s)_t V[t][h],  lse[j][h] = ln sum_t exp(s_jt)
+ * which for many query tokens costs fewer flops than the absorbed form of
+ * mla_decode (2*32*(192+128) per query and visible token, plus 2*512*8192 per
+ * cached token for the expansion, against 2*32*(576+512)).
+ *   q_nope       bf16 [Tq][32][128]
+ *   q_pe         bf16 [Tq][32][64], already rotated
+ *   w_kv_b       bf16 [8192][512]
+ *   cache        bf16 rows [ctx_len][576] of the sequence (contiguous; a paged
+ *                sequence is gathered first)
+ *   out          bf16 [Tq][32][128];  lse  fp32 [Tq][32] or NULL
+ *   workspace    device scratch of mla_prefill_workspace_size() bytes,
+ *                16-byte aligned
+ * Supports 1 <= Tq <= ctx_len <= 2^20 and the bf16 cache format only
+ * (MLA_ERR_UNSUPPORTED for the 8-bit format). */
+mla_status mla_prefill(const mla_shape* shape /* host */, const void* q_nope, const void* q_pe,
+                       const void* w_kv_b, const void* cache, int32_t ctx_len, int32_t Tq, void* out,
+                       float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Kernel timing, a profiling aid (not needed to compute anything).
  * After mla_timing_enable(n), each of the next n decode calls has its
  * split-KV attention kernel(s) record a HIP event pair themselves, at the

@@ -20,6 +20,7 @@ __all__ = [
     "CACHE_BF16", "CACHE_FP8_E4M3", "cache_row_width",
     "mla_rope_yarn", "mla_cache_append", "mla_decode", "mla_decode_paged", "mla_decode_step",
     "mla_decode_workspace_size", "mla_decode_auto_chunk", "mla_status_string",
+    "mla_prefill", "mla_prefill_workspace_size",
     "mla_timing_enable", "mla_timing_collect", "mla_timing_disable",
 ]
 
@@ -77,6 +78,8 @@ def library() -> ctypes.CDLL:
             "mla_decode_workspace_size": [ctypes.POINTER(MlaShape), _I32, _I32, _I32, _I32,
                                           ctypes.POINTER(ctypes.c_size_t)],
             "mla_decode_auto_chunk": [_I32, _I32, _I32, ctypes.POINTER(_I32)],
+            "mla_prefill_workspace_size": [ctypes.POINTER(MlaShape), _I32, ctypes.POINTER(ctypes.c_size_t)],
+            "mla_prefill": [ctypes.POINTER(MlaShape), _P, _P, _P, _P, _I32, _I32, _P, _P, _P, ctypes.c_size_t, _P],
             "mla_timing_enable": [_I32],
             "mla_timing_collect": [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I32)],
             "mla_timing_disable": [],
@@ -313,6 +316,46 @@ def mla_decode_step(q_nope, q_pe, c_kv_new, k_pe_new, w_kv_b, cache, ctx_lens, m
                                          _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
                                          _stream(stream))
         _check(code, "mla_decode_step_paged")
+    return out, lse
+
+
+def mla_prefill_workspace_size(ctx_len: int, shape: MlaShape | None = None) -> int:
+    s = shape if shape is not None else default_shape()
+    out = ctypes.c_size_t()
+    _check(library().mla_prefill_workspace_size(ctypes.byref(s), ctx_len, ctypes.byref(out)),
+           "mla_prefill_workspace_size")
+    return out.value
+
+
+def mla_prefill(q_nope, q_pe, w_kv_b, cache, ctx_len: int, out=None, lse=None, workspace=None,
+                shape: MlaShape | None = None, stream=None):
+    """Chunked prefill of one sequence: q_nope [Tq, 32, 128], q_pe [Tq, 32, 64] (rotated) at
+    positions ctx_len - Tq + j, cache [>= ctx_len, 576] bf16 rows; returns (out, lse)."""
+    _need(q_nope, torch.bfloat16, "q_nope")
+    _need(q_pe, torch.bfloat16, "q_pe")
+    _need(w_kv_b, torch.bfloat16, "w_kv_b")
+    Tq = q_nope.shape[0]
+    if tuple(q_nope.shape) != (Tq, 32, 128) or tuple(q_pe.shape) != (Tq, 32, 64):
+        raise MlaError("q_nope must be [Tq, 32, 128] and q_pe [Tq, 32, 64]")
+    if tuple(w_kv_b.shape) != (8192, 512):
+        raise MlaError("w_kv_b must be [8192, 512]")
+    s = shape if shape is not None else default_shape()
+    width = _check_cache(cache, s)
+    if cache.dim() != 2 or cache.shape[0] < ctx_len:
+        raise MlaError(f"cache must be [>= ctx_len, {width}]")
+    dev = q_nope.device
+    if out is None:
+        out = torch.empty((Tq, 32, 128), dtype=torch.bfloat16, device=dev)
+    _need(out, torch.bfloat16, "out")
+    if lse is not None:
+        _need(lse, torch.float32, "lse")
+    need = mla_prefill_workspace_size(ctx_len, s)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _need(workspace, torch.uint8, "workspace")
+    _check(library().mla_prefill(ctypes.byref(s), _ptr(q_nope), _ptr(q_pe), _ptr(w_kv_b), _ptr(cache), ctx_len,
+                                 Tq, _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream)),
+           "mla_prefill")
     return out, lse
 
 

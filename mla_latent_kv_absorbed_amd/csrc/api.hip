@@ -33,6 +33,10 @@ void timing_free() {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Longest context of one prefill call (32-bit byte offsets inside a tile of
+// expanded rows stay far inside range; the workspace is 16.5 KiB per token).
+constexpr int32_t kMaxPrefillCtx = 1 << 20;
+
 mla_status check_shape(const mla_shape* s) {
   if (s == nullptr) return MLA_ERR_NULL;
   if (s->num_heads != kHeads || s->kv_lora_rank != kLatent || s->qk_nope_head_dim != kNope ||
@@ -370,6 +374,37 @@ mla_status mla_decode_step_paged(const mla_shape* shape, const mla_rope_params* 
   return decode_common(shape, StepInputs{rope, c_kv_new, ld_c, k_pe_new, ld_k}, q_nope, q_pe, w_kv_b, cache,
                        0, num_pages, block_table, max_pages_per_seq, ctx_lens, max_ctx_len, B, Sq, kv_chunk,
                        out, lse, workspace, workspace_bytes, stream, true);
+}
+
+mla_status mla_prefill_workspace_size(const mla_shape* shape, int32_t ctx_len, size_t* bytes) {
+  mla_status st = check_shape(shape);
+  if (st != MLA_OK) return st;
+  if (shape->kv_cache_dtype != MLA_CACHE_BF16) return MLA_ERR_UNSUPPORTED;
+  if (bytes == nullptr) return MLA_ERR_NULL;
+  if (ctx_len < 1 || ctx_len > kMaxPrefillCtx) return MLA_ERR_RANGE;
+  *bytes = prefill_workspace_bytes(ctx_len);
+  return MLA_OK;
+}
+
+mla_status mla_prefill(const mla_shape* shape, const void* q_nope, const void* q_pe, const void* w_kv_b,
+                       const void* cache, int32_t ctx_len, int32_t Tq, void* out, float* lse, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  mla_status st = check_shape(shape);
+  if (st != MLA_OK) return st;
+  if (shape->kv_cache_dtype != MLA_CACHE_BF16) return MLA_ERR_UNSUPPORTED;
+  if (ctx_len < 1 || ctx_len > kMaxPrefillCtx || Tq < 1 || Tq > ctx_len) return MLA_ERR_RANGE;
+  if (!q_nope || !q_pe || !w_kv_b || !cache || !out || !workspace) return MLA_ERR_NULL;
+  if (!aligned16(q_nope) || !aligned16(q_pe) || !aligned16(w_kv_b) || !aligned16(cache) || !aligned16(out) ||
+      !aligned16(workspace))
+    return MLA_ERR_ALIGN;
+  if (lse != nullptr && ((uintptr_t)lse & 3u) != 0) return MLA_ERR_ALIGN;
+  if (workspace_bytes < prefill_workspace_bytes(ctx_len)) return MLA_ERR_WORKSPACE;
+  const float scale_log2 = shape->softmax_scale * 1.44269504088896340736f;
+  if (launch_prefill((const uint16_t*)q_nope, (const uint16_t*)q_pe, (const uint16_t*)w_kv_b, (const uint8_t*)cache,
+                     ctx_len, Tq, scale_log2, (uint16_t*)workspace, (uint16_t*)out, lse,
+                     (hipStream_t)stream) != hipSuccess)
+    return MLA_ERR_DEVICE;
+  return MLA_OK;
 }
 
 mla_status mla_decode_workspace_size(const mla_shape* shape, int32_t B, int32_t Sq, int32_t max_ctx_len,

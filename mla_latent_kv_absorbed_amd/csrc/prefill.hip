@@ -1,0 +1,415 @@
+// Chunked prefill of MLA attention on gfx950: the un-absorbed form.
+//
+// A chunk of Tq new tokens (positions L - Tq .. L - 1 of one sequence, their
+// cache rows already written) attends causally to the sequence's L cached
+// tokens.  With many query tokens the keys and values are worth expanding:
+// kv_b_proj turns each cached latent c_t into per-head K_nope[h] = W_UK[h] c_t
+// and V[h] = W_UV[h] c_t ("mHC+MLA+MTP 是什么", MLA section), after which the
+// attention is plain multi-head attention with a 192-wide key
+// [K_nope | k_pe_t] (the rope key shared by all heads) and a 128-wide value:
+//     s_jt = scale * (q_nope[j,h] . K_nope[t,h] + q_pe[j,h] . k_pe[t]),  t <= L - Tq + j
+//     out[j,h] = sum_t softmax_t(s_jt) V[t,h]
+// per query token 2*32*(192 + 128) flops per visible token, against
+// 2*32*(576 + 512) for the absorbed form: above a few hundred query tokens
+// the expansion (2*512*8192 flops per cached token, once) pays for itself.
+//
+// Two kernels:
+//  * expand_kv: KV[t][o] = bf16(sum_k W[o][k] c_t[k]) for the 8192 rows o of
+//    kv_b_proj (per head [k_nope 128 | v 128]); a 128 x 128 output tile per
+//    workgroup of 4 waves, v_mfma_f32_16x16x32_bf16, 64-wide k stages
+//    double-buffered in LDS through direct global->LDS loads.
+//  * prefill_attention: flash attention with online rescaling; a workgroup
+//    of 4 waves takes 128 query rows of one head, each wave 32 rows (two row
+//    groups of 16, so every LDS read of a key or value tile feeds two MFMAs);
+//    64-token tiles of [K_nope | k_pe] and V stream through a two-tile LDS
+//    ring.  S^T = K . Q^T with the keys as the A operand; the S^T accumulator
+//    layout is the B-operand layout of P in O^T += V^T P^T, with V^T fetched
+//    by ds_read_b64_tr_b16, so P stays in registers.  The query tiles of a
+//    head are placed on one XCD (workgroups x, x + 8, ...), where they read
+//    the head's key and value tiles from the same L2.
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr int kKvRow = kHeads * kWRowsPerHead;   // 8192 expanded values per token
+constexpr int kKvStride = kKvRow + kRope;         // workspace row: [8192 expanded | 64 rope key]
+
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+typedef __attribute__((address_space(3))) const uint8_t lds_cu8;
+typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8_t;
+
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(gaddr)
+               : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ lds_cu8* lds_base(uint32_t lds) {
+  asm volatile("" : "+s"(lds));
+  return (lds_cu8*)lds;
+}
+
+// ---------------------------------------------------------------------------
+// expand_kv.  Output tile: kv_b_proj rows [o0, o0 + 128) x tokens [t0, t0 + 128).
+// D[o][t] = W[o][:] . c_t: W rows as the A operand, cache rows as B (both read
+// k-contiguous, 16 bytes per lane).  Wave (wo, wt) owns rows o0 + 64 wo ..
+// and tokens t0 + 64 wt .., i.e. 4 x 4 blocks of 16 x 16.  LDS stage: W tile
+// [128][64] and C tile [128][64] bf16, rows of 8 chunks of 16 bytes; chunk c
+// of row r sits at position c ^ ((r >> 1) & 7), which keeps both reads free
+// of bank conflicts.
+// ---------------------------------------------------------------------------
+constexpr int kExpTile = 128;
+constexpr int kExpStageK = 64;
+constexpr int kExpStageBytes = 2 * kExpTile * kExpStageK * 2;   // 32 KiB: W tile then C tile
+constexpr int kExpStages = kLatent / kExpStageK;                // 8
+constexpr int kExpLoads = kExpStageBytes / 16 / 256;             // 8 per lane per stage
+
+__global__ void __launch_bounds__(256, 2) expand_kv(const uint16_t* __restrict__ w, const uint8_t* __restrict__ cache,
+                                                 int32_t L, uint16_t* __restrict__ kv) {
+  __shared__ __attribute__((aligned(1024))) uint8_t st[2 * kExpStageBytes];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, n16 = lane & 15;
+  // tile of this workgroup: the 64 output tiles of a token tile run back to
+  // back on one XCD (workgroup x on XCD x % 8), sharing its cache rows in L2
+  const int x = blockIdx.x;
+  const int k8 = x / kXcds;
+  const int ot = k8 % (kKvRow / kExpTile);
+  const int tt = (k8 / (kKvRow / kExpTile)) * kXcds + x % kXcds;
+  const int t0 = tt * kExpTile;
+  if (t0 >= L) return;
+  const int o0 = ot * kExpTile;
+  const uint32_t st_lds = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)st);
+
+  // load i of this lane: LDS position P = (wave*8 + i)*64 + lane (16-byte
+  // units); waves 0-1 fill the W tile, waves 2-3 the C tile
+  int src_off[kExpLoads];
+#pragma unroll
+  for (int i = 0; i < kExpLoads; ++i) {
+    const int P = (wave * kExpLoads + i) * 64 + lane;
+    const int Q = P & 1023;
+    const int row = Q >> 3, c = (Q & 7) ^ ((row >> 1) & 7);
+    src_off[i] = (P < 1024) ? ((o0 + row) * kLatent + c * 8) * 2
+                            : (min(t0 + row, L - 1) * kRow + c * 8) * 2;
+  }
+  const uint8_t* wsrc = (const uint8_t*)w;
+  auto issue = [&](int s, int buf) {
+    const uint32_t dst = st_lds + buf * kExpStageBytes + wave * kExpLoads * 1024;
+#pragma unroll
+    for (int i = 0; i < kExpLoads; ++i)
+      dma16((wave < 2 ? wsrc : cache) + src_off[i] + s * kExpStageK * 2, dst + i * 1024);
+  };
+
+  const int wo = wave & 1, wt = wave >> 1;
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // read offsets within a tile: row r (of the wave's 16-row block), chunk 4ks + g
+  auto rd = [&](int row, int ks) -> int { return row * 128 + (((4 * ks + g) ^ ((row >> 1) & 7)) << 4); };
+
+  issue(0, 0);
+  issue(1, 1);
+  for (int s = 0; s < kExpStages; ++s) {
+    if (s + 1 < kExpStages) vm_wait<kExpLoads>();
+    else vm_wait<0>();
+    lds_barrier();
+    lds_cu8* W = lds_base(st_lds + (s & 1) * kExpStageBytes);
+    lds_cu8* C = W + kExpTile * kExpStageK * 2;
+#pragma unroll
+    for (int ks = 0; ks < kExpStageK / 32; ++ks) {
+      bf16x8 a[4], bb[4];
+#pragma unroll
+      for (int ob = 0; ob < 4; ++ob) a[ob] = *(lds_bf16x8_t*)(W + rd(64 * wo + 16 * ob + n16, ks));
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) bb[tb] = *(lds_bf16x8_t*)(C + rd(64 * wt + 16 * tb + n16, ks));
+#pragma unroll
+      for (int ob = 0; ob < 4; ++ob)
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+          acc[ob][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ob], bb[tb], acc[ob][tb], 0, 0, 0);
+    }
+    lds_barrier();   // every wave is done with this buffer before it is refilled
+    if (s + 2 < kExpStages) issue(s + 2, s & 1);
+  }
+  // lane (g, n16) of block (ob, tb) holds rows o0 + 64wo + 16ob + 4g + i of
+  // token t0 + 64wt + 16tb + n16.  Every row of the tile is written (rows past
+  // L repeat row L - 1), so that the attention's last tile reads defined values.
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) {
+    const int t = t0 + 64 * wt + 16 * tb + n16;
+#pragma unroll
+    for (int ob = 0; ob < 4; ++ob) {
+      s16x4 v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = __builtin_bit_cast(short, (__bf16)acc[ob][tb][i]);
+      *(s16x4*)(kv + (size_t)t * kKvStride + o0 + 64 * wo + 16 * ob + 4 * g) = v;
+    }
+  }
+  if (ot == 0) {   // the tile's rope keys, copied next to the expanded rows
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e = k * 256 + tid, t = e >> 3, c = e & 7;
+      const uint4 r = *(const uint4*)(cache + (size_t)min(t0 + t, L - 1) * kRowBytes + (kLatent + 8 * c) * 2);
+      *(uint4*)(kv + (size_t)(t0 + t) * kKvStride + kKvRow + 8 * c) = r;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// prefill_attention.  Key tile: 64 tokens x 24 chunks ([K_nope 16 | k_pe 8],
+// 384-byte rows); K_nope chunk c of token t at c ^ (t & 15), k_pe chunk k at
+// 16 + (k ^ ((t >> 1) & 7)).  Value tile: 64 tokens x 16 chunks (256-byte
+// rows), chunk c at c ^ (2t & 14).  Both read patterns below are then free
+// of bank conflicts.
+// ---------------------------------------------------------------------------
+constexpr int kPfQRows = 128;                       // query rows per workgroup (one head)
+constexpr int kPfTile = 64;                         // tokens per key/value tile
+constexpr int kPfKBytes = kPfTile * 24 * 16;        // 24576
+constexpr int kPfVBytes = kPfTile * 16 * 16;        // 16384
+constexpr int kPfTileBytes = kPfKBytes + kPfVBytes; // 40960
+constexpr int kPfLoads = kPfTileBytes / 16 / 256;   // 10 per lane per tile
+static_assert(kPfLoads * 16 * 256 == kPfTileBytes, "tile split");
+
+struct PrefillParams {
+  const uint16_t* q_nope;   // bf16 [Tq][32][128]
+  const uint16_t* q_pe;     // bf16 [Tq][32][64], rotated
+  const uint16_t* kv;       // bf16 [L rounded up to 128][8256]: expanded rows and rope keys
+  int32_t L, Tq, qtiles;
+  float scale_log2;
+  uint16_t* out;            // bf16 [Tq][32][128]
+  float* lse;               // fp32 [Tq][32] or null
+};
+
+__global__ void __launch_bounds__(256, 2) prefill_attention(PrefillParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[2 * kPfTileBytes];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, n16 = lane & 15;
+  const int x = blockIdx.x;
+  const int k8 = x / kXcds;
+  const int h = (k8 / p.qtiles) * kXcds + x % kXcds;
+  const int qt = k8 % p.qtiles;
+  const int q0 = qt * kPfQRows;
+  const int base = p.L - p.Tq;                     // position of query row 0
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)ring);
+
+  // this wave's rows: q0 + 32 wave + 16 rg + n16 (rows past Tq repeat Tq - 1, never stored)
+  bf16x8 q[2][6];
+#pragma unroll
+  for (int rg = 0; rg < 2; ++rg) {
+    const int j = min(q0 + 32 * wave + 16 * rg + n16, p.Tq - 1);
+    const uint16_t* qn = p.q_nope + ((size_t)j * kHeads + h) * kNope + 8 * g;
+    const uint16_t* qp = p.q_pe + ((size_t)j * kHeads + h) * kRope + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) q[rg][ks] = *(const bf16x8*)(qn + 32 * ks);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) q[rg][4 + ks] = *(const bf16x8*)(qp + 32 * ks);
+  }
+  // settle the query loads before the direct loads start (a wait placed at
+  // their first use would also drain the tiles in flight)
+#pragma unroll
+  for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+    for (int ks = 0; ks < 6; ++ks) asm volatile("" ::"v"(q[rg][ks]));
+
+  // key/value tiles of tokens [0, last visible of the workgroup's rows]
+  const int last_row = min(q0 + kPfQRows, p.Tq) - 1;
+  const int ntiles = (base + last_row) / kPfTile + 1;
+
+  // direct loads: LDS position P = (wave*10 + i)*64 + lane holds, for
+  // P < 1536, chunk (t = P / 24, slot P % 24) of the key tile, else chunk
+  // (t = (P - 1536) / 16, slot P % 16) of the value tile.  The offsets are
+  // recomputed at each tile (a few integer operations) rather than kept in
+  // registers.
+  auto issue = [&](int tile, int buf) {
+    const uint8_t* src = (const uint8_t*)(p.kv + (size_t)tile * kPfTile * kKvStride);
+    const uint32_t dst = ring_lds + buf * kPfTileBytes + wave * kPfLoads * 1024;
+    int P0 = wave * kPfLoads * 64 + lane;
+    asm volatile("" : "+v"(P0));
+#pragma unroll
+    for (int i = 0; i < kPfLoads; ++i) {
+      const int P = P0 + i * 64;
+      const int tk = P / 24, pos = P - tk * 24;
+      const int ek = (pos < 16) ? h * kWRowsPerHead + 8 * (pos ^ (tk & 15))
+                                : kKvRow + 8 * ((pos - 16) ^ ((tk >> 1) & 7));
+      const int Q = P - kPfTile * 24;
+      const int tv = Q >> 4;
+      const int ev = h * kWRowsPerHead + kNope + 8 * ((Q & 15) ^ ((2 * tv) & 14));
+      const bool key = P < kPfTile * 24;
+      dma16(src + ((key ? tk : tv) * kKvStride + (key ? ek : ev)) * 2, dst + i * 1024);
+    }
+  };
+
+  // score reads: token 16 tb + n16, chunk 4 ks + g
+  int k_off[6];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) k_off[ks] = n16 * 384 + (((4 * ks + g) ^ n16) << 4);
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) k_off[4 + ks] = n16 * 384 + ((16 + ((4 * ks + g) ^ (n16 >> 1))) << 4);
+  // value reads (transposed, 8 bytes): token 4g + (n16 >> 2) (+16, +32),
+  // columns 16 vb + 4 (n16 & 3): chunk 2 vb + ((n16 >> 1) & 1)
+  const int v_tok = 4 * g + (n16 >> 2);
+  const int v_h = (n16 >> 1) & 1;
+  const int v_x = (2 * v_tok) & 14;
+  const int v_row = kPfKBytes + v_tok * 256 + (n16 & 1) * 8;
+
+  f32x4 o[2][8];
+#pragma unroll
+  for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+    for (int vb = 0; vb < 8; ++vb) o[rg][vb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[2] = {kNegInf, kNegInf}, l[2] = {0.f, 0.f};
+  // visibility: row r sees tokens <= base + r
+  int lim[2];
+#pragma unroll
+  for (int rg = 0; rg < 2; ++rg) lim[rg] = base + q0 + 32 * wave + 16 * rg + n16;
+
+  issue(0, 0);
+  if (ntiles > 1) issue(1, 1);
+  for (int it = 0; it < ntiles; ++it) {
+    if (it + 1 < ntiles) vm_wait<kPfLoads>();
+    else vm_wait<0>();
+    lds_barrier();
+    lds_cu8* T = lds_base(ring_lds + (it & 1) * kPfTileBytes);
+    const int t0 = it * kPfTile;
+
+    // The tile is taken in two 32-token halves, each: scores, online
+    // softmax (rescaling O and l), value product.
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      // ---- S^T = K . Q^T for 2 token blocks x 2 row groups
+      f32x4 s[2][2];
+#pragma unroll
+      for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) s[rg][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 6; ++ks) {
+        bf16x8 a[2];
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) a[tb] = *(lds_bf16x8_t*)(T + (2 * hb + tb) * 16 * 384 + k_off[ks]);
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+          for (int rg = 0; rg < 2; ++rg)
+            s[rg][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[tb], q[rg][ks], s[rg][tb], 0, 0, 0);
+      }
+
+      // ---- online softmax per row (lane n16 of each row group; 8 tokens per lane)
+      bf16x8 pa[2];
+#pragma unroll
+      for (int rg = 0; rg < 2; ++rg) {
+        float mt = kNegInf;
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = t0 + 32 * hb + 16 * tb + 4 * g + i;
+            const float v = (t <= lim[rg]) ? s[rg][tb][i] * p.scale_log2 : kNegInf;
+            s[rg][tb][i] = v;
+            mt = fmaxf(mt, v);
+          }
+        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        const float mn = fmaxf(m[rg], mt);
+        const float alpha = (mn == kNegInf || m[rg] == kNegInf) ? (mn == kNegInf ? 1.f : 0.f)
+                                                                : __builtin_amdgcn_exp2f(m[rg] - mn);
+        const float msub = (mn == kNegInf) ? 0.f : mn;
+        m[rg] = mn;
+        float ls = 0.f;
+        // k order of the 32-token step: tokens 4g+i of block 0, then of block 1
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const __bf16 e = (__bf16)__builtin_amdgcn_exp2f(s[rg][tb][i] - msub);
+            ls += (float)e;
+            pa[rg][tb * 4 + i] = e;
+          }
+        l[rg] = l[rg] * alpha + ls;
+#pragma unroll
+        for (int vb = 0; vb < 8; ++vb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[rg][vb][i] *= alpha;
+      }
+
+      // ---- O^T += V^T . P^T: 8 value blocks of 16 columns, this 32-token step
+#pragma unroll
+      for (int vb = 0; vb < 8; ++vb) {
+        lds_cu8* a = T + v_row + hb * 32 * 256 + (((2 * vb + v_h) ^ v_x) << 4);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)a);
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(a + 16 * 256));
+        const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int rg = 0; rg < 2; ++rg)
+          o[rg][vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pa[rg], o[rg][vb], 0, 0, 0);
+      }
+    }
+    lds_barrier();   // every wave is done with this tile before it is refilled
+    if (it + 2 < ntiles) issue(it + 2, it & 1);
+  }
+
+  // ---- output: lane (g, n16) holds columns 16 vb + 4g .. + 3 of row n16
+#pragma unroll
+  for (int rg = 0; rg < 2; ++rg) {
+    float lr = l[rg];
+    lr += __shfl_xor(lr, 16, 64);
+    lr += __shfl_xor(lr, 32, 64);
+    const int j = q0 + 32 * wave + 16 * rg + n16;
+    if (j >= p.Tq) continue;
+    const float inv = (lr > 0.f) ? 1.f / lr : 0.f;
+    uint16_t* orow = p.out + ((size_t)j * kHeads + h) * kVDim + 4 * g;
+#pragma unroll
+    for (int vb = 0; vb < 8; ++vb) {
+      s16x4 v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = __builtin_bit_cast(short, (__bf16)(o[rg][vb][i] * inv));
+      *(s16x4*)(orow + 16 * vb) = v;
+    }
+    if (p.lse != nullptr && g == 0)
+      p.lse[(size_t)j * kHeads + h] = (lr > 0.f) ? (m[rg] + __log2f(lr)) * 0.69314718055994530942f : kNegInf;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const uint16_t* q_nope, const uint16_t* q_pe, const uint16_t* w_kv_b, const uint8_t* cache,
+                          int32_t L, int32_t Tq, float scale_log2, uint16_t* kv, uint16_t* out, float* lse,
+                          hipStream_t stream) {
+  const int ttiles = (L + kExpTile - 1) / kExpTile;
+  const unsigned egrid = (unsigned)(((ttiles + kXcds - 1) / kXcds) * kXcds * (kKvRow / kExpTile));
+  hipLaunchKernelGGL(expand_kv, dim3(egrid), dim3(256), 0, stream, w_kv_b, cache, L, kv);
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  PrefillParams pp;
+  pp.q_nope = q_nope;
+  pp.q_pe = q_pe;
+  pp.kv = kv;
+  pp.L = L;
+  pp.Tq = Tq;
+  pp.qtiles = (Tq + kPfQRows - 1) / kPfQRows;
+  pp.scale_log2 = scale_log2;
+  pp.out = out;
+  pp.lse = lse;
+  hipLaunchKernelGGL(prefill_attention, dim3((unsigned)(pp.qtiles * kHeads)), dim3(256), 0, stream, pp);
+  return hipGetLastError();
+}
+
+size_t prefill_workspace_bytes(int32_t L) {
+  return (size_t)((L + kExpTile - 1) / kExpTile) * kExpTile * kKvStride * 2;
+}
+
+}  // namespace mla

@@ -1,4 +1,4 @@
-"""Device-resident decode inputs for one workload, built with the library itself.
+"""Device-resident decode (and chunked-prefill) inputs, built with the library itself.
 
 For each layer: the seeded raw values (``synth.gpu``) are drawn straight into
 device memory, the rope keys of all cached tokens are rotated by
@@ -21,7 +21,8 @@ import synth.gpu as sgpu
 from synth.configs import Workload
 
 from . import (CACHE_BF16, CACHE_FP8_E4M3, cache_row_width, default_shape, mla_cache_append, mla_decode,
-               mla_decode_paged, mla_decode_step, mla_decode_workspace_size, mla_decode_auto_chunk, mla_rope_yarn)
+               mla_decode_paged, mla_decode_step, mla_decode_workspace_size, mla_decode_auto_chunk, mla_prefill,
+               mla_prefill_workspace_size, mla_rope_yarn)
 
 BF16_NAN = 0x7FC1   # bit pattern written into unused cache slots when poisoning
 FP8_NAN = 0x7F      # E4M3 NaN byte, the same for 8-bit cache rows
@@ -164,3 +165,51 @@ class DeviceWorkload:
                                     self.max_ctx, chunk, out=out, lse=lse, workspace=ws, shape=self.shape)
         return mla_decode(li.q_nope, li.q_pe, li.w_kv_b, li.cache, self.ctx_lens, self.max_ctx, chunk,
                           out=out, lse=lse, workspace=ws, shape=self.shape)
+
+
+@dataclass
+class PrefillInputs:
+    layer: int
+    cache: torch.Tensor        # bf16 [L, 576]: the sequence's rows, the chunk's own included
+    w_kv_b: torch.Tensor       # bf16 [8192, 512]
+    q_nope: torch.Tensor       # [Tq, 32, 128]
+    q_pe: torch.Tensor         # [Tq, 32, 64], rotated at L - Tq + j
+
+
+class DevicePrefill:
+    """Device inputs of a chunked prefill: one sequence of L cached tokens whose last
+    Tq are the chunk (synthetic, seeded as the decode workloads: sequence 0 of seed)."""
+
+    def __init__(self, seed: int, L: int, Tq: int, device: str = "cuda:0"):
+        self.seed, self.L, self.Tq = seed, L, Tq
+        self.dev = torch.device(device)
+        self.workspace = torch.empty(mla_prefill_workspace_size(L), dtype=torch.uint8, device=self.dev)
+        self.q_pos = (torch.arange(Tq, dtype=torch.int32, device=self.dev) + (L - Tq)).repeat_interleave(32)
+
+    def build_layer(self, layer: int) -> PrefillInputs:
+        dev, L, Tq, seed = self.dev, self.L, self.Tq, self.seed
+        cache = torch.empty((L, 576), dtype=torch.bfloat16, device=dev)
+        step = 1 << 18
+        for t0 in range(0, L, step):
+            n = min(step, L - t0)
+            c = torch.empty((n, 512), dtype=torch.bfloat16, device=dev)
+            k = torch.empty((n, 64), dtype=torch.bfloat16, device=dev)
+            sgpu.latent(c, seed, layer, 0, t0)
+            sgpu.kpe(k, seed, layer, 0, t0)
+            pos = torch.arange(t0, t0 + n, dtype=torch.int32, device=dev)
+            mla_rope_yarn(k, pos)
+            mla_cache_append(cache, c, k, pos.to(torch.int64))
+            del c, k
+        w = torch.empty((8192, 512), dtype=torch.bfloat16, device=dev)
+        sgpu.wkvb(w, seed, layer)
+        q_nope = torch.empty((Tq, 32, 128), dtype=torch.bfloat16, device=dev)
+        q_pe = torch.empty((Tq, 32, 64), dtype=torch.bfloat16, device=dev)
+        sgpu.qnope(q_nope, seed, layer, 0)
+        sgpu.qpe(q_pe, seed, layer, 0)
+        mla_rope_yarn(q_pe.view(-1, 64), self.q_pos)
+        return PrefillInputs(layer, cache, w, q_nope, q_pe)
+
+    def run(self, li: PrefillInputs, out=None, lse=None):
+        return mla_prefill(li.q_nope, li.q_pe, li.w_kv_b, li.cache, self.L, out=out, lse=lse,
+                           workspace=self.workspace)
+

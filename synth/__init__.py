@@ -22,7 +22,8 @@ multi-gigabyte caches can be generated in device memory; a GPU test checks
 the two agree.
 
 Logical element indices (``TOKMAX = 2**20`` tokens per sequence, ``QMAX = 16``
-query tokens per sequence):
+query tokens per sequence; a single-sequence prefill chunk, b = 0, may take any
+number of query tokens, its indices running on past QMAX):
 
 ====================  =========================================
 tensor (id)           flat index of element

@@ -49,7 +49,16 @@ OUT_REL_L2 = 5e-3
 LSE_MAX_ABS = 5e-3
 
 
-def compare(out_gpu, lse_gpu, out_ref, lse_ref):
+# Chunked prefill (un-absorbed form): the expanded keys and values are rounded
+# to bf16 before the attention, errors the decode path does not have (the design doc
+# derives both bounds): a score moves by up to ~5.5e-3 for one visible token
+# (rms 1.8e-3), an output by half a bf16 ulp of V plus half an ulp of the
+# output (< 3.2e-2 for |V|, |out| < 8).  rel-L2 keeps the path's 5e-3.
+PREFILL_LSE_MAX_ABS = 1e-2
+PREFILL_OUT_MAX_ABS = 4e-2
+
+
+def compare(out_gpu, lse_gpu, out_ref, lse_ref, lse_tol=LSE_MAX_ABS, abs_tol=OUT_MAX_ABS):
     """Returns (max_abs, rel_l2, lse_max_abs); asserts the tolerances."""
     og = np.asarray(out_gpu, dtype=np.float64)
     d = og - out_ref
@@ -57,9 +66,9 @@ def compare(out_gpu, lse_gpu, out_ref, lse_ref):
     rel = float(np.linalg.norm(d) / max(np.linalg.norm(out_ref), 1e-30))
     lmax = float(np.abs(np.asarray(lse_gpu, dtype=np.float64) - lse_ref).max()) if lse_gpu is not None else 0.0
     assert np.isfinite(og).all(), "non-finite GPU output"
-    assert max_abs <= OUT_MAX_ABS, f"max abs {max_abs}"
+    assert max_abs <= abs_tol, f"max abs {max_abs}"
     assert rel <= OUT_REL_L2, f"rel L2 {rel}"
-    assert lmax <= LSE_MAX_ABS, f"lse max abs {lmax}"
+    assert lmax <= lse_tol, f"lse max abs {lmax}"
     return max_abs, rel, lmax
 
 

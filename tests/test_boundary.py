@@ -124,3 +124,30 @@ def test_workspace_size_and_auto_chunk():
     # an empty batch needs no workspace and must not trip the split heuristic
     assert M.mla_decode_workspace_size(0, 1, 1024) == 0
     assert M.mla_decode_auto_chunk(0, 1, 1024) % 64 == 0
+
+
+def _prefill(lib, shape, **kw):
+    a = dict(q=FAKE, qp=FAKE, w=FAKE, cache=FAKE, L=1024, Tq=256, out=FAKE, lse=None, ws=FAKE, wsb=1 << 40)
+    a.update(kw)
+    return lib.mla_prefill(ctypes.byref(shape), a["q"], a["qp"], a["w"], a["cache"], a["L"], a["Tq"], a["out"],
+                           a["lse"], a["ws"], a["wsb"], None)
+
+
+def test_prefill_argument_errors_and_workspace():
+    lib = M.library()
+    s = M.default_shape()
+    assert _prefill(lib, s, q=None) == ERR_NULL
+    assert _prefill(lib, s, ws=None) == ERR_NULL
+    assert _prefill(lib, s, Tq=0) == ERR_RANGE
+    assert _prefill(lib, s, Tq=1025) == ERR_RANGE                 # more query tokens than context
+    assert _prefill(lib, s, L=(1 << 20) + 1, Tq=1) == ERR_RANGE
+    assert _prefill(lib, s, out=FAKE + 8) == ERR_ALIGN
+    assert _prefill(lib, s, wsb=1000) == ERR_WORKSPACE
+    f8 = M.default_shape(M.CACHE_FP8_E4M3)
+    assert _prefill(lib, f8) == 7                                 # MLA_ERR_UNSUPPORTED
+    # expanded rows [8192 | 64 rope] bf16 per token, context rounded up to 128
+    assert M.mla_prefill_workspace_size(1024) == 1024 * 8256 * 2
+    assert M.mla_prefill_workspace_size(1000) == 1024 * 8256 * 2
+    assert M.mla_prefill_workspace_size(129) == 256 * 8256 * 2
+    with pytest.raises(M.MlaError):
+        M.mla_prefill_workspace_size(0)

@@ -1,0 +1,60 @@
+"""Chunked prefill (mla_prefill) against the oracle's un-absorbed definition.
+
+Inputs come from ``synth`` on both sides: sequence 0 of the seed, Tq query
+tokens at positions L - Tq .. L - 1, the chunk's own cache rows included.
+Small cases compare every output with the fp64 un-absorbed oracle; the
+full-size chunk (4096 new tokens on a 32768-token context) compares sampled
+rows, each against the oracle run on that row's visible prefix.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from mla_latent_kv_absorbed_amd.workload import DevicePrefill
+
+from oracle_inputs import PREFILL_LSE_MAX_ABS, PREFILL_OUT_MAX_ABS, compare, expected, sequence_inputs, weights
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def gpu_run(seed, L, Tq, layer=0, reps=1):
+    dp = DevicePrefill(seed, L, Tq, device=DEV)
+    li = dp.build_layer(layer)
+    outs = []
+    for _ in range(reps):
+        lse = torch.empty((Tq, 32), dtype=torch.float32, device=DEV)
+        out, lse = dp.run(li, lse=lse)
+        torch.cuda.synchronize()
+        outs.append((out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy(), out.clone()))
+    del li, dp
+    torch.cuda.empty_cache()
+    return outs
+
+
+@pytest.mark.parametrize("L,Tq", [(1024, 256), (333, 100), (200, 200), (777, 1), (130, 129)])
+def test_prefill_matches_the_unabsorbed_oracle(L, Tq):
+    go, gl, _ = gpu_run(81, L, Tq, layer=1)[0]
+    ref_o, ref_l = expected(81, 1, L, Tq, 0)
+    s = compare(go, gl, ref_o, ref_l, lse_tol=PREFILL_LSE_MAX_ABS, abs_tol=PREFILL_OUT_MAX_ABS)
+    print(f"prefill L={L} Tq={Tq}: max_abs={s[0]:.3e} rel_l2={s[1]:.3e} lse={s[2]:.3e}", flush=True)
+
+
+def test_prefill_is_deterministic():
+    runs = gpu_run(82, 700, 300, reps=2)
+    assert torch.equal(runs[0][2], runs[1][2])
+    assert np.array_equal(runs[0][1], runs[1][1])
+
+
+def test_prefill_fullsize_chunk4k_ctx32k_sampled_rows():
+    L, Tq, seed = 32768, 4096, 8
+    go, gl, _ = gpu_run(seed, L, Tq)[0]
+    qn, qp, c, k = sequence_inputs(seed, 0, L, Tq, 0)
+    w = weights(seed, 0)
+    for j in (0, 1, 2047, 4095):
+        Lj = L - Tq + j + 1
+        ref_o, ref_l = O.mla_attention_absorbed(qn[j:j + 1], qp[j:j + 1], c[:Lj], k[:Lj], w, O.softmax_scale())
+        s = compare(go[j:j + 1], gl[j:j + 1], ref_o, ref_l, lse_tol=PREFILL_LSE_MAX_ABS, abs_tol=PREFILL_OUT_MAX_ABS)
+        print(f"prefill 4K/32K row {j}: max_abs={s[0]:.3e} rel_l2={s[1]:.3e} lse={s[2]:.3e}", flush=True)
