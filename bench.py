@@ -16,7 +16,9 @@ reported alongside under "ctx256k", and the 32K and 256K workloads over the
 and layer) under "fp8_cache".  "other_workloads" reports the batched paged
 decode (16 x 65536), speculative verify of 2, 3 and 4 query tokens per
 sequence (batch 32, log-uniform contexts in [4096, 131072], paged) and one
-sequence of 524288 tokens, all with the device-balanced split.
+sequence of 524288 tokens, all with the device-balanced split; "prefill" the
+chunked prefill (un-absorbed form) of 4096 new tokens on 32K and 128K
+contexts, in TFLOP/s against the 2.5 PFLOP/s bf16 matrix peak.
 
 Output: one JSON line.  "value" is decode tokens/s (batch * query tokens per
 step / step time, timed over --steps replays of a HIP graph of the step).
@@ -41,6 +43,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MLA decode tokens/s + latent-KV GB/s (% HBM peak) at 32K and 256K ctx, 1 GPU"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
+MFMA_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 matrix peak, 2.5 PFLOP/s
 BYTES_PER_TOKEN_LAYER = 1152    # 576 bf16 cached values per token per layer
 BYTES_PER_TOKEN_LAYER_FP8 = 656  # 512 E4M3 codes + 4 fp32 scales + 64 bf16 rope values
 COUNTERS = os.path.join(ROOT, "profiles", "splitkv_decode_counters.json")
@@ -144,6 +147,37 @@ def run_workload(k: int, steps: int, warmup: int, use_graph: bool, kv_chunk=None
     del layers, outs, lses, ref, graph
     torch.cuda.empty_cache()
     return res
+
+
+def run_prefill(L: int, Tq: int, steps: int, warmup: int, seed: int = 8):
+    """Chunked prefill of one layer: Tq new tokens on an L-token context (the chunk's rows
+    included), timed over `steps` calls; flops = expansion + attention of the visible tokens."""
+    import torch
+    from mla_latent_kv_absorbed_amd.workload import DevicePrefill
+
+    dp = DevicePrefill(seed, L, Tq)
+    li = dp.build_layer(0)
+    out = torch.empty((Tq, 32, 128), dtype=torch.bfloat16, device=dp.dev)
+    lse = torch.empty((Tq, 32), dtype=torch.float32, device=dp.dev)
+    for _ in range(warmup):
+        dp.run(li, out, lse)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        dp.run(li, out, lse)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    visible = Tq * (L - Tq) + Tq * (Tq + 1) // 2
+    flops_attn = visible * 32 * (192 + 128) * 2
+    flops_expand = L * 512 * 8192 * 2
+    tflops = (flops_attn + flops_expand) / (ms * 1e-3) / 1e12
+    del li, dp, out, lse
+    torch.cuda.empty_cache()
+    return dict(workload=f"mla-prefill-chunk{Tq}-ctx{L}", context=L, chunk_tokens=Tq, ms_per_layer=ms,
+                tokens_per_s=Tq / (ms * 1e-3), tflops_per_s=tflops, mfma_frac=tflops / MFMA_PEAK_TFLOPS,
+                flops_per_call=flops_attn + flops_expand)
 
 
 def cpu_baseline(k: int, budget_s: float = 15.0):
@@ -325,6 +359,13 @@ def main():
                                                          "ms_per_step", "step_latent_gbps", "kernel_avg_us",
                                                          "kernel_latent_gbps", "kv_chunk")}
             more[r["workload"]]["kernel_hbm_frac"] = r["kernel_latent_gbps"] / HBM_PEAK_GBPS
+    prefill = None
+    if not args.no_more:
+        prefill = {}
+        for L, Tq in ((32768, 4096), (131072, 4096)):
+            r = run_prefill(L, Tq, 5, 2)
+            log(f"[prefill {Tq}/{L}] {json.dumps(r)}")
+            prefill[r["workload"]] = r
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.config)
 
     bpl = main_res["kernel_bytes_per_launch"]
@@ -354,6 +395,7 @@ def main():
         "ctx256k": extra,
         "fp8_cache": fp8,
         "other_workloads": more,
+        "prefill": prefill,
     }
     print(json.dumps(line), flush=True)
 

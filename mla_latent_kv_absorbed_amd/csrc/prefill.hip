@@ -18,7 +18,8 @@
 //    kv_b_proj (per head [k_nope 128 | v 128]); a 128 x 128 output tile per
 //    workgroup of 4 waves, v_mfma_f32_16x16x32_bf16, 64-wide k stages
 //    double-buffered in LDS through direct global->LDS loads.
-//  * prefill_attention: flash attention with online rescaling; a workgroup
+//  * prefill_attention: flash attention (rescaling only when a row's maximum
+//    outgrows its reference by 2^8); a workgroup
 //    of 4 waves takes 128 query rows of one head, each wave 32 rows (two row
 //    groups of 16, so every LDS read of a key or value tile feeds two MFMAs);
 //    64-token tiles of [K_nope | k_pe] and V stream through a two-tile LDS
@@ -176,12 +177,12 @@ __global__ void __launch_bounds__(256, 2) expand_kv(const uint16_t* __restrict__
 // rows), chunk c at c ^ (2t & 14).  Both read patterns below are then free
 // of bank conflicts.
 // ---------------------------------------------------------------------------
-constexpr int kPfQRows = 128;                       // query rows per workgroup (one head)
 constexpr int kPfTile = 64;                         // tokens per key/value tile
 constexpr int kPfKBytes = kPfTile * 24 * 16;        // 24576
 constexpr int kPfVBytes = kPfTile * 16 * 16;        // 16384
 constexpr int kPfTileBytes = kPfKBytes + kPfVBytes; // 40960
 constexpr int kPfLoads = kPfTileBytes / 16 / 256;   // 10 per lane per tile
+constexpr float kPfTau = 8.0f;                      // log2 headroom of p above the row's reference
 static_assert(kPfLoads * 16 * 256 == kPfTileBytes, "tile split");
 
 struct PrefillParams {
@@ -194,7 +195,14 @@ struct PrefillParams {
   float* lse;               // fp32 [Tq][32] or null
 };
 
-__global__ void __launch_bounds__(256, 2) prefill_attention(PrefillParams p) {
+// RG row groups of 16 query rows per wave.  Launched with RG = 2: two waves
+// per SIMD, two workgroups per compute unit.  (RG = 4, one wave per SIMD with
+// up to 512 registers and every key/value read feeding four MFMAs, measured
+// 25% slower: with one wave per SIMD the LDS and softmax latencies stay exposed.)
+template <int RG>
+__global__ void __launch_bounds__(256, RG == 2 ? 2 : 1) prefill_attention(PrefillParams p) {
+  constexpr int kRowsW = 16 * RG;           // query rows per wave
+  constexpr int kQRows = 4 * kRowsW;        // query rows per workgroup (one head)
   __shared__ __attribute__((aligned(1024))) uint8_t ring[2 * kPfTileBytes];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -203,15 +211,15 @@ __global__ void __launch_bounds__(256, 2) prefill_attention(PrefillParams p) {
   const int k8 = x / kXcds;
   const int h = (k8 / p.qtiles) * kXcds + x % kXcds;
   const int qt = k8 % p.qtiles;
-  const int q0 = qt * kPfQRows;
+  const int q0 = qt * kQRows;
   const int base = p.L - p.Tq;                     // position of query row 0
   const uint32_t ring_lds = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)ring);
 
-  // this wave's rows: q0 + 32 wave + 16 rg + n16 (rows past Tq repeat Tq - 1, never stored)
-  bf16x8 q[2][6];
+  // this wave's rows: q0 + kRowsW wave + 16 rg + n16 (rows past Tq repeat Tq - 1, never stored)
+  bf16x8 q[RG][6];
 #pragma unroll
-  for (int rg = 0; rg < 2; ++rg) {
-    const int j = min(q0 + 32 * wave + 16 * rg + n16, p.Tq - 1);
+  for (int rg = 0; rg < RG; ++rg) {
+    const int j = min(q0 + kRowsW * wave + 16 * rg + n16, p.Tq - 1);
     const uint16_t* qn = p.q_nope + ((size_t)j * kHeads + h) * kNope + 8 * g;
     const uint16_t* qp = p.q_pe + ((size_t)j * kHeads + h) * kRope + 8 * g;
 #pragma unroll
@@ -222,12 +230,12 @@ __global__ void __launch_bounds__(256, 2) prefill_attention(PrefillParams p) {
   // settle the query loads before the direct loads start (a wait placed at
   // their first use would also drain the tiles in flight)
 #pragma unroll
-  for (int rg = 0; rg < 2; ++rg)
+  for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
     for (int ks = 0; ks < 6; ++ks) asm volatile("" ::"v"(q[rg][ks]));
 
   // key/value tiles of tokens [0, last visible of the workgroup's rows]
-  const int last_row = min(q0 + kPfQRows, p.Tq) - 1;
+  const int last_row = min(q0 + kQRows, p.Tq) - 1;
   const int ntiles = (base + last_row) / kPfTile + 1;
 
   // direct loads: LDS position P = (wave*10 + i)*64 + lane holds, for
@@ -267,16 +275,22 @@ __global__ void __launch_bounds__(256, 2) prefill_attention(PrefillParams p) {
   const int v_x = (2 * v_tok) & 14;
   const int v_row = kPfKBytes + v_tok * 256 + (n16 & 1) * 8;
 
-  f32x4 o[2][8];
+  f32x4 o[RG][8];
 #pragma unroll
-  for (int rg = 0; rg < 2; ++rg)
+  for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
     for (int vb = 0; vb < 8; ++vb) o[rg][vb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m[2] = {kNegInf, kNegInf}, l[2] = {0.f, 0.f};
-  // visibility: row r sees tokens <= base + r
-  int lim[2];
+  float m[RG], l[RG];
 #pragma unroll
-  for (int rg = 0; rg < 2; ++rg) lim[rg] = base + q0 + 32 * wave + 16 * rg + n16;
+  for (int rg = 0; rg < RG; ++rg) {
+    m[rg] = kNegInf;
+    l[rg] = 0.f;
+  }
+  // visibility: row r sees tokens <= base + r; lim_wave is the wave's smallest
+  int lim[RG];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) lim[rg] = base + q0 + kRowsW * wave + 16 * rg + n16;
+  const int lim_wave = base + q0 + kRowsW * wave;
 
   issue(0, 0);
   if (ntiles > 1) issue(1, 1);
@@ -292,9 +306,9 @@ __global__ void __launch_bounds__(256, 2) prefill_attention(PrefillParams p) {
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
       // ---- S^T = K . Q^T for 2 token blocks x 2 row groups
-      f32x4 s[2][2];
+      f32x4 s[RG][2];
 #pragma unroll
-      for (int rg = 0; rg < 2; ++rg)
+      for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) s[rg][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -305,31 +319,42 @@ __global__ void __launch_bounds__(256, 2) prefill_attention(PrefillParams p) {
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-          for (int rg = 0; rg < 2; ++rg)
+          for (int rg = 0; rg < RG; ++rg)
             s[rg][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[tb], q[rg][ks], s[rg][tb], 0, 0, 0);
       }
 
-      // ---- online softmax per row (lane n16 of each row group; 8 tokens per lane)
-      bf16x8 pa[2];
+      // ---- softmax per row (lane n16 of each row group; 8 tokens per lane)
+      // with a lazily moved reference: p = 2^(s - m_ref) may reach 2^kPfTau;
+      // only when a row's maximum exceeds m_ref + kPfTau (or at its first
+      // visible token) does m_ref move, and O and l are rescaled.  The mask
+      // is skipped for halves every row of the wave sees entirely.
+      const bool full = t0 + 32 * hb + 31 <= lim_wave;
+      bf16x8 pa[RG];
 #pragma unroll
-      for (int rg = 0; rg < 2; ++rg) {
+      for (int rg = 0; rg < RG; ++rg) {
         float mt = kNegInf;
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int t = t0 + 32 * hb + 16 * tb + 4 * g + i;
-            const float v = (t <= lim[rg]) ? s[rg][tb][i] * p.scale_log2 : kNegInf;
+            float v = s[rg][tb][i] * p.scale_log2;
+            if (!full) v = (t0 + 32 * hb + 16 * tb + 4 * g + i <= lim[rg]) ? v : kNegInf;
             s[rg][tb][i] = v;
             mt = fmaxf(mt, v);
           }
         mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
         mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-        const float mn = fmaxf(m[rg], mt);
-        const float alpha = (mn == kNegInf || m[rg] == kNegInf) ? (mn == kNegInf ? 1.f : 0.f)
-                                                                : __builtin_amdgcn_exp2f(m[rg] - mn);
-        const float msub = (mn == kNegInf) ? 0.f : mn;
-        m[rg] = mn;
+        const bool move = mt > m[rg] + kPfTau;   // also true at the row's first visible token
+        if (__builtin_amdgcn_ballot_w64(move) != 0) {
+          const float alpha = move ? (m[rg] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m[rg] - mt)) : 1.f;
+          m[rg] = move ? mt : m[rg];
+          l[rg] *= alpha;
+#pragma unroll
+          for (int vb = 0; vb < 8; ++vb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[rg][vb][i] *= alpha;
+        }
+        const float msub = (m[rg] == kNegInf) ? 0.f : m[rg];
         float ls = 0.f;
         // k order of the 32-token step: tokens 4g+i of block 0, then of block 1
 #pragma unroll
@@ -340,11 +365,7 @@ __global__ void __launch_bounds__(256, 2) prefill_attention(PrefillParams p) {
             ls += (float)e;
             pa[rg][tb * 4 + i] = e;
           }
-        l[rg] = l[rg] * alpha + ls;
-#pragma unroll
-        for (int vb = 0; vb < 8; ++vb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) o[rg][vb][i] *= alpha;
+        l[rg] += ls;
       }
 
       // ---- O^T += V^T . P^T: 8 value blocks of 16 columns, this 32-token step
@@ -355,7 +376,7 @@ __global__ void __launch_bounds__(256, 2) prefill_attention(PrefillParams p) {
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(a + 16 * 256));
         const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-        for (int rg = 0; rg < 2; ++rg)
+        for (int rg = 0; rg < RG; ++rg)
           o[rg][vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pa[rg], o[rg][vb], 0, 0, 0);
       }
     }
@@ -365,11 +386,11 @@ __global__ void __launch_bounds__(256, 2) prefill_attention(PrefillParams p) {
 
   // ---- output: lane (g, n16) holds columns 16 vb + 4g .. + 3 of row n16
 #pragma unroll
-  for (int rg = 0; rg < 2; ++rg) {
+  for (int rg = 0; rg < RG; ++rg) {
     float lr = l[rg];
     lr += __shfl_xor(lr, 16, 64);
     lr += __shfl_xor(lr, 32, 64);
-    const int j = q0 + 32 * wave + 16 * rg + n16;
+    const int j = q0 + kRowsW * wave + 16 * rg + n16;
     if (j >= p.Tq) continue;
     const float inv = (lr > 0.f) ? 1.f / lr : 0.f;
     uint16_t* orow = p.out + ((size_t)j * kHeads + h) * kVDim + 4 * g;
@@ -400,11 +421,11 @@ hipError_t launch_prefill(const uint16_t* q_nope, const uint16_t* q_pe, const ui
   pp.kv = kv;
   pp.L = L;
   pp.Tq = Tq;
-  pp.qtiles = (Tq + kPfQRows - 1) / kPfQRows;
   pp.scale_log2 = scale_log2;
   pp.out = out;
   pp.lse = lse;
-  hipLaunchKernelGGL(prefill_attention, dim3((unsigned)(pp.qtiles * kHeads)), dim3(256), 0, stream, pp);
+  pp.qtiles = (Tq + 127) / 128;
+  hipLaunchKernelGGL(prefill_attention<2>, dim3((unsigned)(pp.qtiles * kHeads)), dim3(256), 0, stream, pp);
   return hipGetLastError();
 }
 

@@ -48,13 +48,21 @@ def test_prefill_is_deterministic():
     assert np.array_equal(runs[0][1], runs[1][1])
 
 
-def test_prefill_fullsize_chunk4k_ctx32k_sampled_rows():
-    L, Tq, seed = 32768, 4096, 8
+def check_sampled_rows(seed, L, Tq, rows):
     go, gl, _ = gpu_run(seed, L, Tq)[0]
     qn, qp, c, k = sequence_inputs(seed, 0, L, Tq, 0)
     w = weights(seed, 0)
-    for j in (0, 1, 2047, 4095):
+    for j in rows:
         Lj = L - Tq + j + 1
         ref_o, ref_l = O.mla_attention_absorbed(qn[j:j + 1], qp[j:j + 1], c[:Lj], k[:Lj], w, O.softmax_scale())
         s = compare(go[j:j + 1], gl[j:j + 1], ref_o, ref_l, lse_tol=PREFILL_LSE_MAX_ABS, abs_tol=PREFILL_OUT_MAX_ABS)
-        print(f"prefill 4K/32K row {j}: max_abs={s[0]:.3e} rel_l2={s[1]:.3e} lse={s[2]:.3e}", flush=True)
+        print(f"prefill {Tq}/{L} row {j}: max_abs={s[0]:.3e} rel_l2={s[1]:.3e} lse={s[2]:.3e}", flush=True)
+
+
+def test_prefill_fullsize_chunk4k_ctx32k_sampled_rows():
+    check_sampled_rows(8, 32768, 4096, (0, 1, 255, 256, 2047, 4095))
+
+
+def test_prefill_long_chunk_from_scratch_sampled_rows():
+    # a long chunk from an empty context: ragged last tiles, first rows seeing few tokens
+    check_sampled_rows(83, 2100, 2100, (0, 1, 2, 63, 64, 255, 256, 1000, 2047, 2048, 2099))
