@@ -37,6 +37,7 @@ constexpr float kNegInf = -__builtin_inff();
 constexpr int kKvRow = kHeads * kWRowsPerHead;   // 8192 expanded values per token
 constexpr int kKvStride = kKvRow + kRope;         // workspace row: [8192 expanded | 64 rope key]
 
+typedef __attribute__((__vector_size__(8 * sizeof(float)))) float f32x8;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 typedef __attribute__((address_space(3))) const uint8_t lds_cu8;
 typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8_t;
@@ -181,9 +182,9 @@ constexpr int kPfTile = 64;                         // tokens per key/value tile
 constexpr int kPfKBytes = kPfTile * 24 * 16;        // 24576
 constexpr int kPfVBytes = kPfTile * 16 * 16;        // 16384
 constexpr int kPfTileBytes = kPfKBytes + kPfVBytes; // 40960
-constexpr int kPfLoads = kPfTileBytes / 16 / 256;   // 10 per lane per tile
 constexpr float kPfTau = 8.0f;                      // log2 headroom of p above the row's reference
-static_assert(kPfLoads * 16 * 256 == kPfTileBytes, "tile split");
+constexpr int kPfWaves = 8;                         // waves per workgroup (32 query rows each)
+constexpr int kPfSlots = 3;                         // key/value tiles in the LDS ring
 
 struct PrefillParams {
   const uint16_t* q_nope;   // bf16 [Tq][32][128]
@@ -195,22 +196,49 @@ struct PrefillParams {
   float* lse;               // fp32 [Tq][32] or null
 };
 
-// RG row groups of 16 query rows per wave.  Launched with RG = 2: two waves
-// per SIMD, two workgroups per compute unit.  (RG = 4, one wave per SIMD with
-// up to 512 registers and every key/value read feeding four MFMAs, measured
-// 25% slower: with one wave per SIMD the LDS and softmax latencies stay exposed.)
-template <int RG>
-__global__ void __launch_bounds__(256, RG == 2 ? 2 : 1) prefill_attention(PrefillParams p) {
-  constexpr int kRowsW = 16 * RG;           // query rows per wave
-  constexpr int kQRows = 4 * kRowsW;        // query rows per workgroup (one head)
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[2 * kPfTileBytes];
+// One 16-byte direct global->LDS load from a wave-uniform base plus a
+// per-lane 32-bit offset (LDS byte lds + 16 * lane).
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+
+// Maximum over lanes n, n + 16, n + 32, n + 48 (the four 16-lane rows of a
+// wave), by two lane-half swaps instead of LDS permutes.
+__device__ __forceinline__ float max_rows4(float v) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  v = fmaxf(__builtin_bit_cast(float, a[0]), __builtin_bit_cast(float, a[1]));
+  const unsigned w = __builtin_bit_cast(unsigned, v);
+  const auto b = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+  return fmaxf(__builtin_bit_cast(float, b[0]), __builtin_bit_cast(float, b[1]));
+}
+
+// WAVES waves of 32 query rows (two row groups of 16) take one head's
+// 32 * WAVES consecutive query rows; SLOTS tiles rotate through LDS, so
+// SLOTS - 1 tiles are loading while one is consumed.  Launched with 8 waves
+// (two per SIMD, 256 query rows: every key and value byte fetched from L2
+// feeds twice the work of a 4-wave workgroup) and a three-tile ring.
+template <int WAVES, int SLOTS>
+__global__ void __launch_bounds__(WAVES * 64, 2) prefill_attention(PrefillParams p) {
+  constexpr int RG = 2;                       // row groups of 16 query rows per wave
+  constexpr int kRowsW = 16 * RG;             // query rows per wave
+  constexpr int kQRows = WAVES * kRowsW;      // query rows per workgroup (one head)
+  constexpr int NL = kPfTileBytes / 16 / (WAVES * 64);   // direct loads per lane and tile
+  static_assert(NL * 16 * WAVES * 64 == kPfTileBytes, "tile split");
+  static_assert(SLOTS == 2 || SLOTS == 3, "ring depth");
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[SLOTS * kPfTileBytes];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, n16 = lane & 15;
+  // workgroup x on XCD x % 8 takes head (k8 / qtiles) * 8 + x % 8: a head's
+  // query tiles share one XCD's L2; the longest (last) query tiles go first
   const int x = blockIdx.x;
   const int k8 = x / kXcds;
   const int h = (k8 / p.qtiles) * kXcds + x % kXcds;
-  const int qt = k8 % p.qtiles;
+  const int qt = p.qtiles - 1 - k8 % p.qtiles;
   const int q0 = qt * kQRows;
   const int base = p.L - p.Tq;                     // position of query row 0
   const uint32_t ring_lds = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)ring);
@@ -238,28 +266,30 @@ __global__ void __launch_bounds__(256, RG == 2 ? 2 : 1) prefill_attention(Prefil
   const int last_row = min(q0 + kQRows, p.Tq) - 1;
   const int ntiles = (base + last_row) / kPfTile + 1;
 
-  // direct loads: LDS position P = (wave*10 + i)*64 + lane holds, for
-  // P < 1536, chunk (t = P / 24, slot P % 24) of the key tile, else chunk
-  // (t = (P - 1536) / 16, slot P % 16) of the value tile.  The offsets are
-  // recomputed at each tile (a few integer operations) rather than kept in
-  // registers.
-  auto issue = [&](int tile, int buf) {
-    const uint8_t* src = (const uint8_t*)(p.kv + (size_t)tile * kPfTile * kKvStride);
-    const uint32_t dst = ring_lds + buf * kPfTileBytes + wave * kPfLoads * 1024;
-    int P0 = wave * kPfLoads * 64 + lane;
-    asm volatile("" : "+v"(P0));
+  // direct loads: LDS position P = (wave * NL + i) * 64 + lane (16-byte
+  // units) holds, for P < 1536, chunk (t = P / 24, slot P % 24) of the key
+  // tile, else chunk (t = (P - 1536) / 16, slot P % 16) of the value tile.
+  // The byte offsets within a tile are the same for every tile.
+  uint32_t off[NL];
 #pragma unroll
-    for (int i = 0; i < kPfLoads; ++i) {
-      const int P = P0 + i * 64;
+  for (int i = 0; i < NL; ++i) {
+    const int P = (wave * NL + i) * 64 + lane;
+    int e;
+    if (P < kPfTile * 24) {
       const int tk = P / 24, pos = P - tk * 24;
-      const int ek = (pos < 16) ? h * kWRowsPerHead + 8 * (pos ^ (tk & 15))
-                                : kKvRow + 8 * ((pos - 16) ^ ((tk >> 1) & 7));
-      const int Q = P - kPfTile * 24;
-      const int tv = Q >> 4;
-      const int ev = h * kWRowsPerHead + kNope + 8 * ((Q & 15) ^ ((2 * tv) & 14));
-      const bool key = P < kPfTile * 24;
-      dma16(src + ((key ? tk : tv) * kKvStride + (key ? ek : ev)) * 2, dst + i * 1024);
+      e = tk * kKvStride + ((pos < 16) ? h * kWRowsPerHead + 8 * (pos ^ (tk & 15))
+                                       : kKvRow + 8 * ((pos - 16) ^ ((tk >> 1) & 7)));
+    } else {
+      const int Q = P - kPfTile * 24, tv = Q >> 4;
+      e = tv * kKvStride + h * kWRowsPerHead + kNope + 8 * ((Q & 15) ^ ((2 * tv) & 14));
     }
+    off[i] = (uint32_t)e * 2u;
+  }
+  auto issue = [&](int tile, int slot) {
+    const uint8_t* src = (const uint8_t*)p.kv + (size_t)tile * (kPfTile * kKvStride * 2);
+    const uint32_t dst = ring_lds + slot * kPfTileBytes + wave * NL * 1024;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) dma16s(src, off[i], dst + i * 1024);
   };
 
   // score reads: token 16 tb + n16, chunk 4 ks + g
@@ -280,7 +310,7 @@ __global__ void __launch_bounds__(256, RG == 2 ? 2 : 1) prefill_attention(Prefil
   for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
     for (int vb = 0; vb < 8; ++vb) o[rg][vb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m[RG], l[RG];
+  float m[RG], l[RG];   // m: reference maximum of scale * s in log2 units; l: this lane's share of the sum
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) {
     m[rg] = kNegInf;
@@ -292,19 +322,22 @@ __global__ void __launch_bounds__(256, RG == 2 ? 2 : 1) prefill_attention(Prefil
   for (int rg = 0; rg < RG; ++rg) lim[rg] = base + q0 + kRowsW * wave + 16 * rg + n16;
   const int lim_wave = base + q0 + kRowsW * wave;
 
-  issue(0, 0);
-  if (ntiles > 1) issue(1, 1);
+#pragma unroll
+  for (int k = 0; k < SLOTS - 1; ++k)
+    if (k < ntiles) issue(k, k);
   for (int it = 0; it < ntiles; ++it) {
-    if (it + 1 < ntiles) vm_wait<kPfLoads>();
+    // tile it has landed (tile it + 1 may still be loading), and every wave
+    // is done with the slot that tile it + SLOTS - 1 refills
+    if (SLOTS == 3 && it + 1 < ntiles) vm_wait<NL>();
     else vm_wait<0>();
     lds_barrier();
-    lds_cu8* T = lds_base(ring_lds + (it & 1) * kPfTileBytes);
-    const int t0 = it * kPfTile;
+    if (it + SLOTS - 1 < ntiles) issue(it + SLOTS - 1, (it + SLOTS - 1) % SLOTS);
+    lds_cu8* T = lds_base(ring_lds + (it % SLOTS) * kPfTileBytes);
 
-    // The tile is taken in two 32-token halves, each: scores, online
-    // softmax (rescaling O and l), value product.
+    // two 32-token steps, each: scores, online softmax, value product
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
+      const int tk0 = it * kPfTile + 32 * hb;
       // ---- S^T = K . Q^T for 2 token blocks x 2 row groups
       f32x4 s[RG][2];
 #pragma unroll
@@ -322,28 +355,30 @@ __global__ void __launch_bounds__(256, RG == 2 ? 2 : 1) prefill_attention(Prefil
           for (int rg = 0; rg < RG; ++rg)
             s[rg][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[tb], q[rg][ks], s[rg][tb], 0, 0, 0);
       }
+      // causal mask, only on steps that reach past the wave's first row
+      // (a wave-uniform branch; the empty asm keeps it a branch)
+      if (tk0 + 31 > lim_wave) {
+        asm volatile("");
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              s[rg][tb][i] = (tk0 + 16 * tb + 4 * g + i <= lim[rg]) ? s[rg][tb][i] : kNegInf;
+      }
 
       // ---- softmax per row (lane n16 of each row group; 8 tokens per lane)
-      // with a lazily moved reference: p = 2^(s - m_ref) may reach 2^kPfTau;
-      // only when a row's maximum exceeds m_ref + kPfTau (or at its first
-      // visible token) does m_ref move, and O and l are rescaled.  The mask
-      // is skipped for halves every row of the wave sees entirely.
-      const bool full = t0 + 32 * hb + 31 <= lim_wave;
+      // with a lazily moved reference: p = 2^(scale s - m_ref) may reach
+      // 2^kPfTau; only when a row's maximum exceeds m_ref + kPfTau (or at
+      // its first visible token) does m_ref move, and O and l are rescaled.
+      // The scale is positive, so the maximum is taken on the raw scores.
       bf16x8 pa[RG];
 #pragma unroll
       for (int rg = 0; rg < RG; ++rg) {
-        float mt = kNegInf;
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float v = s[rg][tb][i] * p.scale_log2;
-            if (!full) v = (t0 + 32 * hb + 16 * tb + 4 * g + i <= lim[rg]) ? v : kNegInf;
-            s[rg][tb][i] = v;
-            mt = fmaxf(mt, v);
-          }
-        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        float mt = fmaxf(fmaxf(fmaxf(s[rg][0][0], s[rg][0][1]), fmaxf(s[rg][0][2], s[rg][0][3])),
+                         fmaxf(fmaxf(s[rg][1][0], s[rg][1][1]), fmaxf(s[rg][1][2], s[rg][1][3])));
+        mt = max_rows4(mt) * p.scale_log2;
         const bool move = mt > m[rg] + kPfTau;   // also true at the row's first visible token
         if (__builtin_amdgcn_ballot_w64(move) != 0) {
           const float alpha = move ? (m[rg] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m[rg] - mt)) : 1.f;
@@ -354,18 +389,15 @@ __global__ void __launch_bounds__(256, RG == 2 ? 2 : 1) prefill_attention(Prefil
 #pragma unroll
             for (int i = 0; i < 4; ++i) o[rg][vb][i] *= alpha;
         }
-        const float msub = (m[rg] == kNegInf) ? 0.f : m[rg];
-        float ls = 0.f;
+        const float nsub = (m[rg] == kNegInf) ? 0.f : -m[rg];
         // k order of the 32-token step: tokens 4g+i of block 0, then of block 1
+        f32x8 e;
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const __bf16 e = (__bf16)__builtin_amdgcn_exp2f(s[rg][tb][i] - msub);
-            ls += (float)e;
-            pa[rg][tb * 4 + i] = e;
-          }
-        l[rg] += ls;
+          for (int i = 0; i < 4; ++i) e[4 * tb + i] = __builtin_amdgcn_exp2f(fmaf(s[rg][tb][i], p.scale_log2, nsub));
+        l[rg] += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+        pa[rg] = __builtin_convertvector(e, bf16x8);
       }
 
       // ---- O^T += V^T . P^T: 8 value blocks of 16 columns, this 32-token step
@@ -380,8 +412,6 @@ __global__ void __launch_bounds__(256, RG == 2 ? 2 : 1) prefill_attention(Prefil
           o[rg][vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pa[rg], o[rg][vb], 0, 0, 0);
       }
     }
-    lds_barrier();   // every wave is done with this tile before it is refilled
-    if (it + 2 < ntiles) issue(it + 2, it & 1);
   }
 
   // ---- output: lane (g, n16) holds columns 16 vb + 4g .. + 3 of row n16
@@ -424,8 +454,10 @@ hipError_t launch_prefill(const uint16_t* q_nope, const uint16_t* q_pe, const ui
   pp.scale_log2 = scale_log2;
   pp.out = out;
   pp.lse = lse;
-  pp.qtiles = (Tq + 127) / 128;
-  hipLaunchKernelGGL(prefill_attention<2>, dim3((unsigned)(pp.qtiles * kHeads)), dim3(256), 0, stream, pp);
+  constexpr int kRows = 32 * kPfWaves;
+  pp.qtiles = (Tq + kRows - 1) / kRows;
+  hipLaunchKernelGGL((prefill_attention<kPfWaves, kPfSlots>), dim3((unsigned)(pp.qtiles * kHeads)),
+                     dim3(64 * kPfWaves), 0, stream, pp);
   return hipGetLastError();
 }
 
