@@ -172,19 +172,26 @@ __global__ void __launch_bounds__(256, 2) expand_kv(const uint16_t* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-// prefill_attention.  Key tile: 64 tokens x 24 chunks ([K_nope 16 | k_pe 8],
-// 384-byte rows); K_nope chunk c of token t at c ^ (t & 15), k_pe chunk k at
-// 16 + (k ^ ((t >> 1) & 7)).  Value tile: 64 tokens x 16 chunks (256-byte
-// rows), chunk c at c ^ (2t & 14).  Both read patterns below are then free
-// of bank conflicts.
+// prefill_attention.  A key/value tile of 64 tokens sits in LDS as padded
+// rows: key rows of 416 bytes ([K_nope 16 chunks | k_pe 8 chunks | pad 2],
+// chunk = 16 bytes) and value rows of 288 bytes ([V 16 chunks | pad 2]).
+// Both the 16-byte key reads (lanes: tokens t..t+15 x 4 chunks) and the
+// 8-byte transposed value reads (8 tokens x 4 column quarters per 32 lanes)
+// are then free of bank conflicts (measured with the LDS bank-conflict
+// counter: a 400-byte key row or a 272-byte value row conflicts two-way),
+// and every read of a tile is one per-lane base plus an immediate offset.
 // ---------------------------------------------------------------------------
-constexpr int kPfTile = 64;                         // tokens per key/value tile
-constexpr int kPfKBytes = kPfTile * 24 * 16;        // 24576
-constexpr int kPfVBytes = kPfTile * 16 * 16;        // 16384
-constexpr int kPfTileBytes = kPfKBytes + kPfVBytes; // 40960
-constexpr float kPfTau = 8.0f;                      // log2 headroom of p above the row's reference
-constexpr int kPfWaves = 8;                         // waves per workgroup (32 query rows each)
-constexpr int kPfSlots = 3;                         // key/value tiles in the LDS ring
+constexpr int kPfTile = 64;                          // tokens per key/value tile
+constexpr int kPfKRow = 416;                         // LDS bytes per key row
+constexpr int kPfVRow = 288;                         // LDS bytes per value row
+constexpr int kPfKBytes = kPfTile * kPfKRow;         // 26624
+constexpr int kPfTileBytes = kPfKBytes + kPfTile * kPfVRow;   // 45056
+constexpr int kPfInstr = kPfTileBytes / 1024;        // 44 wave-wide direct loads per tile
+constexpr int kPfWaves = 8;                          // waves per workgroup (32 query rows each)
+constexpr int kPfSlots = 3;                          // tiles in the LDS ring
+constexpr int kPfWide = kPfInstr - 5 * kPfWaves;     // waves 0..3 issue 6 loads per tile, the rest 5
+constexpr float kPfTau = 8.0f;                       // log2 headroom of p above the row's reference
+static_assert(kPfInstr * 1024 == kPfTileBytes && kPfWide == 4, "tile split");
 
 struct PrefillParams {
   const uint16_t* q_nope;   // bf16 [Tq][32][128]
@@ -205,6 +212,19 @@ __device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_
                : "memory", "m0");
 }
 
+// Maxima of finite or infinite scores (no NaN handling needed; written as
+// the plain instructions so that no quieting of the MFMA results is added).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float fmax2f(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // Maximum over lanes n, n + 16, n + 32, n + 48 (the four 16-lane rows of a
 // wave), by two lane-half swaps instead of LDS permutes.
 __device__ __forceinline__ float max_rows4(float v) {
@@ -216,19 +236,15 @@ __device__ __forceinline__ float max_rows4(float v) {
   return fmaxf(__builtin_bit_cast(float, b[0]), __builtin_bit_cast(float, b[1]));
 }
 
-// WAVES waves of 32 query rows (two row groups of 16) take one head's
-// 32 * WAVES consecutive query rows; SLOTS tiles rotate through LDS, so
-// SLOTS - 1 tiles are loading while one is consumed.  Launched with 8 waves
-// (two per SIMD, 256 query rows: every key and value byte fetched from L2
-// feeds twice the work of a 4-wave workgroup) and a three-tile ring.
-template <int WAVES, int SLOTS>
-__global__ void __launch_bounds__(WAVES * 64, 2) prefill_attention(PrefillParams p) {
+// Eight waves of 32 query rows (two row groups of 16; two waves per SIMD)
+// take 256 consecutive query rows of one head, so every key and value byte
+// brought into LDS feeds 256 rows.  Three tiles rotate through the LDS ring:
+// two are loading while one is consumed.
+__global__ void __launch_bounds__(kPfWaves * 64, 2) prefill_attention(PrefillParams p) {
   constexpr int RG = 2;                       // row groups of 16 query rows per wave
   constexpr int kRowsW = 16 * RG;             // query rows per wave
-  constexpr int kQRows = WAVES * kRowsW;      // query rows per workgroup (one head)
-  constexpr int NL = kPfTileBytes / 16 / (WAVES * 64);   // direct loads per lane and tile
-  static_assert(NL * 16 * WAVES * 64 == kPfTileBytes, "tile split");
-  static_assert(SLOTS == 2 || SLOTS == 3, "ring depth");
+  constexpr int kQRows = kPfWaves * kRowsW;   // query rows per workgroup (one head)
+  constexpr int SLOTS = kPfSlots;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[SLOTS * kPfTileBytes];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -266,56 +282,59 @@ __global__ void __launch_bounds__(WAVES * 64, 2) prefill_attention(PrefillParams
   const int last_row = min(q0 + kQRows, p.Tq) - 1;
   const int ntiles = (base + last_row) / kPfTile + 1;
 
-  // direct loads: LDS position P = (wave * NL + i) * 64 + lane (16-byte
-  // units) holds, for P < 1536, chunk (t = P / 24, slot P % 24) of the key
-  // tile, else chunk (t = (P - 1536) / 16, slot P % 16) of the value tile.
-  // The byte offsets within a tile are the same for every tile.
-  uint32_t off[NL];
+  // direct loads: wave-wide load I of a tile fills LDS bytes [1024 I,
+  // 1024 (I + 1)); waves 0..3 issue loads 6w .. 6w + 5, waves 4..7 loads
+  // 24 + 5 (w - 4) .. + 4.  Lane position P = 64 I + lane (16-byte units):
+  // P < 1664 is chunk P % 26 of key row P / 26, else chunk Q % 18 of value
+  // row Q / 18 (Q = P - 1664); pad chunks repeat the row's first chunk.  The
+  // byte offsets within a tile are the same for every tile.
+  const bool wide = wave < kPfWide;
+  const int i0 = wide ? 6 * wave : kPfWide + 5 * wave;
+  uint32_t off[6];
 #pragma unroll
-  for (int i = 0; i < NL; ++i) {
-    const int P = (wave * NL + i) * 64 + lane;
+  for (int i = 0; i < 6; ++i) {
+    const int P = (i0 + i) * 64 + lane;
     int e;
-    if (P < kPfTile * 24) {
-      const int tk = P / 24, pos = P - tk * 24;
-      e = tk * kKvStride + ((pos < 16) ? h * kWRowsPerHead + 8 * (pos ^ (tk & 15))
-                                       : kKvRow + 8 * ((pos - 16) ^ ((tk >> 1) & 7)));
+    if (P < kPfTile * 26) {
+      const int t = P / 26, c = P - 26 * t;
+      e = t * kKvStride + (c < 16 ? h * kWRowsPerHead + 8 * c : (c < 24 ? kKvRow + 8 * (c - 16) : h * kWRowsPerHead));
     } else {
-      const int Q = P - kPfTile * 24, tv = Q >> 4;
-      e = tv * kKvStride + h * kWRowsPerHead + kNope + 8 * ((Q & 15) ^ ((2 * tv) & 14));
+      const int Q = P - kPfTile * 26, t = Q / 18, c = Q - 18 * t;
+      e = t * kKvStride + h * kWRowsPerHead + kNope + (c < 16 ? 8 * c : 0);
     }
     off[i] = (uint32_t)e * 2u;
   }
   auto issue = [&](int tile, int slot) {
     const uint8_t* src = (const uint8_t*)p.kv + (size_t)tile * (kPfTile * kKvStride * 2);
-    const uint32_t dst = ring_lds + slot * kPfTileBytes + wave * NL * 1024;
+    const uint32_t dst = ring_lds + slot * kPfTileBytes + i0 * 1024;
 #pragma unroll
-    for (int i = 0; i < NL; ++i) dma16s(src, off[i], dst + i * 1024);
+    for (int i = 0; i < 5; ++i) dma16s(src, off[i], dst + i * 1024);
+    if (wide) dma16s(src, off[5], dst + 5 * 1024);
   };
 
-  // score reads: token 16 tb + n16, chunk 4 ks + g
-  int k_off[6];
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) k_off[ks] = n16 * 384 + (((4 * ks + g) ^ n16) << 4);
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) k_off[4 + ks] = n16 * 384 + ((16 + ((4 * ks + g) ^ (n16 >> 1))) << 4);
-  // value reads (transposed, 8 bytes): token 4g + (n16 >> 2) (+16, +32),
-  // columns 16 vb + 4 (n16 & 3): chunk 2 vb + ((n16 >> 1) & 1)
-  const int v_tok = 4 * g + (n16 >> 2);
-  const int v_h = (n16 >> 1) & 1;
-  const int v_x = (2 * v_tok) & 14;
-  const int v_row = kPfKBytes + v_tok * 256 + (n16 & 1) * 8;
+  // score reads: token 16 tb + n16 of the step, chunk 4 ks + g
+  const int k_lane = n16 * kPfKRow + 16 * g;
+  // value reads (transposed, 8 bytes): token 4g + (n16 >> 2) (+16) of the
+  // step, columns 16 vb + 4 (n16 & 3) .. + 3 (bytes 32 vb + 8 (n16 & 3))
+  const int v_lane = kPfKBytes + (4 * g + (n16 >> 2)) * kPfVRow + 8 * (n16 & 3);
 
   f32x4 o[RG][8];
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
     for (int vb = 0; vb < 8; ++vb) o[rg][vb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m[RG], l[RG];   // m: reference maximum of scale * s in log2 units; l: this lane's share of the sum
+  // per row: m, the reference maximum of scale * s (log2 units); nsub = -m
+  // (0 while the row has seen nothing); thr = (m + kPfTau) / scale, the raw
+  // score above which the reference has to move; l, this lane's share of the sum
+  float m[RG], nsub[RG], thr[RG], l[RG];
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) {
     m[rg] = kNegInf;
+    nsub[rg] = 0.f;
+    thr[rg] = kNegInf;
     l[rg] = 0.f;
   }
+  const float inv_scale = 1.f / p.scale_log2;
   // visibility: row r sees tokens <= base + r; lim_wave is the wave's smallest
   int lim[RG];
 #pragma unroll
@@ -328,14 +347,19 @@ __global__ void __launch_bounds__(WAVES * 64, 2) prefill_attention(PrefillParams
   for (int it = 0; it < ntiles; ++it) {
     // tile it has landed (tile it + 1 may still be loading), and every wave
     // is done with the slot that tile it + SLOTS - 1 refills
-    if (SLOTS == 3 && it + 1 < ntiles) vm_wait<NL>();
-    else vm_wait<0>();
+    if (it + 1 < ntiles) {
+      if (wide) vm_wait<6>();
+      else vm_wait<5>();
+    } else {
+      vm_wait<0>();
+    }
     lds_barrier();
     if (it + SLOTS - 1 < ntiles) issue(it + SLOTS - 1, (it + SLOTS - 1) % SLOTS);
     lds_cu8* T = lds_base(ring_lds + (it % SLOTS) * kPfTileBytes);
 
-    // two 32-token steps, each: scores, online softmax, value product
-#pragma unroll
+    // two 32-token steps, each: scores, online softmax, value product (kept
+    // as a loop: unrolled, the rescale branch costs register copies)
+#pragma unroll 1
     for (int hb = 0; hb < 2; ++hb) {
       const int tk0 = it * kPfTile + 32 * hb;
       // ---- S^T = K . Q^T for 2 token blocks x 2 row groups
@@ -348,7 +372,8 @@ __global__ void __launch_bounds__(WAVES * 64, 2) prefill_attention(PrefillParams
       for (int ks = 0; ks < 6; ++ks) {
         bf16x8 a[2];
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) a[tb] = *(lds_bf16x8_t*)(T + (2 * hb + tb) * 16 * 384 + k_off[ks]);
+        for (int tb = 0; tb < 2; ++tb)
+          a[tb] = *(lds_bf16x8_t*)(T + k_lane + (32 * hb + 16 * tb) * kPfKRow + 16 * (ks < 4 ? 4 * ks : 16 + 4 * (ks - 4)));
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
@@ -369,33 +394,47 @@ __global__ void __launch_bounds__(WAVES * 64, 2) prefill_attention(PrefillParams
       }
 
       // ---- softmax per row (lane n16 of each row group; 8 tokens per lane)
-      // with a lazily moved reference: p = 2^(scale s - m_ref) may reach
-      // 2^kPfTau; only when a row's maximum exceeds m_ref + kPfTau (or at
-      // its first visible token) does m_ref move, and O and l are rescaled.
-      // The scale is positive, so the maximum is taken on the raw scores.
-      bf16x8 pa[RG];
+      // with a lazily moved reference: p = 2^(scale s - m) may reach
+      // 2^kPfTau.  Each lane compares its own scores with the row's raw
+      // threshold; only when one exceeds it (or at the row's first visible
+      // token) is the row maximum formed across the four lanes of the row,
+      // m moved and O and l rescaled.  The scale is positive, so maxima are
+      // taken on the raw scores.
+      float lm[RG];
+      bool over = false;
 #pragma unroll
       for (int rg = 0; rg < RG; ++rg) {
-        float mt = fmaxf(fmaxf(fmaxf(s[rg][0][0], s[rg][0][1]), fmaxf(s[rg][0][2], s[rg][0][3])),
-                         fmaxf(fmaxf(s[rg][1][0], s[rg][1][1]), fmaxf(s[rg][1][2], s[rg][1][3])));
-        mt = max_rows4(mt) * p.scale_log2;
-        const bool move = mt > m[rg] + kPfTau;   // also true at the row's first visible token
-        if (__builtin_amdgcn_ballot_w64(move) != 0) {
+        lm[rg] = max3f(max3f(s[rg][0][0], s[rg][0][1], s[rg][0][2]), max3f(s[rg][0][3], s[rg][1][0], s[rg][1][1]),
+                       fmax2f(s[rg][1][2], s[rg][1][3]));
+        over |= lm[rg] > thr[rg];
+      }
+      if (__builtin_amdgcn_ballot_w64(over) != 0) {
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg) {
+          const float mt = max_rows4(lm[rg]) * p.scale_log2;
+          const bool move = mt > m[rg] + kPfTau;
           const float alpha = move ? (m[rg] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m[rg] - mt)) : 1.f;
           m[rg] = move ? mt : m[rg];
+          if (m[rg] != kNegInf) {
+            nsub[rg] = -m[rg];
+            thr[rg] = (m[rg] + kPfTau) * inv_scale;
+          }
           l[rg] *= alpha;
 #pragma unroll
           for (int vb = 0; vb < 8; ++vb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) o[rg][vb][i] *= alpha;
         }
-        const float nsub = (m[rg] == kNegInf) ? 0.f : -m[rg];
+      }
+      bf16x8 pa[RG];
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg) {
         // k order of the 32-token step: tokens 4g+i of block 0, then of block 1
         f32x8 e;
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) e[4 * tb + i] = __builtin_amdgcn_exp2f(fmaf(s[rg][tb][i], p.scale_log2, nsub));
+          for (int i = 0; i < 4; ++i) e[4 * tb + i] = __builtin_amdgcn_exp2f(fmaf(s[rg][tb][i], p.scale_log2, nsub[rg]));
         l[rg] += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
         pa[rg] = __builtin_convertvector(e, bf16x8);
       }
@@ -403,9 +442,9 @@ __global__ void __launch_bounds__(WAVES * 64, 2) prefill_attention(PrefillParams
       // ---- O^T += V^T . P^T: 8 value blocks of 16 columns, this 32-token step
 #pragma unroll
       for (int vb = 0; vb < 8; ++vb) {
-        lds_cu8* a = T + v_row + hb * 32 * 256 + (((2 * vb + v_h) ^ v_x) << 4);
+        lds_cu8* a = T + v_lane + 32 * hb * kPfVRow + 32 * vb;
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)a);
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(a + 16 * 256));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(a + 16 * kPfVRow));
         const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int rg = 0; rg < RG; ++rg)
@@ -456,7 +495,7 @@ hipError_t launch_prefill(const uint16_t* q_nope, const uint16_t* q_pe, const ui
   pp.lse = lse;
   constexpr int kRows = 32 * kPfWaves;
   pp.qtiles = (Tq + kRows - 1) / kRows;
-  hipLaunchKernelGGL((prefill_attention<kPfWaves, kPfSlots>), dim3((unsigned)(pp.qtiles * kHeads)),
+  hipLaunchKernelGGL(prefill_attention, dim3((unsigned)(pp.qtiles * kHeads)),
                      dim3(64 * kPfWaves), 0, stream, pp);
   return hipGetLastError();
 }
