@@ -231,7 +231,7 @@ mla_status mla_decode_workspace_size(const mla_shape* shape /* host */, int32_t 
 mla_status mla_decode_auto_chunk(int32_t B, int32_t Sq, int32_t max_ctx_len, int32_t* kv_chunk /* host */);
 
 /* Workspace bytes mla_prefill needs for a context of ctx_len tokens (host):
- * the expanded rows, 16,512 B per token (ctx_len rounded up to 128).
+ * the expanded rows, 16,512 B per token (ctx_len rounded up to 256).
  * MLA_ERR_UNSUPPORTED for the 8-bit cache format. */
 mla_status mla_prefill_workspace_size(const mla_shape* shape /* host */, int32_t ctx_len,
                                       size_t* bytes /* host */);

@@ -224,7 +224,7 @@ hipError_t launch_append(uint8_t* cache, int64_t num_slots, const uint16_t* c_kv
 hipError_t launch_append_fp8(uint8_t* cache, const uint16_t* c_kv, int64_t ld_c, const uint16_t* k_pe,
                              int64_t ld_k, const int64_t* slots, int64_t n, hipStream_t stream);
 // Chunked prefill (prefill.hip): expand the L context rows through kv_b_proj
-// into kv (bf16 rows [8192 expanded | 64 rope key], L rounded up to 128 rows,
+// into kv (bf16 rows [8192 expanded | 64 rope key], L rounded up to 256 rows,
 // prefill_workspace_bytes), then causal attention of the Tq chunk tokens.
 hipError_t launch_prefill(const uint16_t* q_nope, const uint16_t* q_pe, const uint16_t* w_kv_b, const uint8_t* cache,
                           int32_t L, int32_t Tq, float scale_log2, uint16_t* kv, uint16_t* out, float* lse,

@@ -38,6 +38,8 @@ constexpr int kKvRow = kHeads * kWRowsPerHead;   // 8192 expanded values per tok
 constexpr int kKvStride = kKvRow + kRope;         // workspace row: [8192 expanded | 64 rope key]
 
 typedef __attribute__((__vector_size__(8 * sizeof(float)))) float f32x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(2 * sizeof(unsigned)))) unsigned u32x2;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 typedef __attribute__((address_space(3))) const uint8_t lds_cu8;
 typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8_t;
@@ -53,6 +55,15 @@ __device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds) {
                : "memory", "m0");
 }
 
+// One 16-byte direct global->LDS load from a wave-uniform base plus a
+// per-lane 32-bit offset (LDS byte lds + 16 * lane).
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+
 template <int N>
 __device__ __forceinline__ void vm_wait() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -64,109 +75,154 @@ __device__ __forceinline__ lds_cu8* lds_base(uint32_t lds) {
 }
 
 // ---------------------------------------------------------------------------
-// expand_kv.  Output tile: kv_b_proj rows [o0, o0 + 128) x tokens [t0, t0 + 128).
-// D[o][t] = W[o][:] . c_t: W rows as the A operand, cache rows as B (both read
-// k-contiguous, 16 bytes per lane).  Wave (wo, wt) owns rows o0 + 64 wo ..
-// and tokens t0 + 64 wt .., i.e. 4 x 4 blocks of 16 x 16.  LDS stage: W tile
-// [128][64] and C tile [128][64] bf16, rows of 8 chunks of 16 bytes; chunk c
-// of row r sits at position c ^ ((r >> 1) & 7), which keeps both reads free
-// of bank conflicts.
+// expand_kv.  KV[t][o] = bf16(W[o][:] . c_t) for the 8192 rows o of kv_b_proj.
+// Output tiles of 256 rows x 256 tokens; one workgroup of 8 waves per compute
+// unit walks its tiles with one pipeline of 64-wide k stages across tile
+// boundaries (the next tile's first stages load while the current tile
+// finishes and is written).  W rows are the A operand, cache rows B (both read
+// k-contiguous, 16 bytes per lane); wave (wo, wt) owns rows o0 + 128 wo ..
+// and tokens t0 + 64 wt .., i.e. 8 x 4 blocks of 16 x 16, so every 16-byte
+// read feeds 4 or 8 products.  LDS stage: W tile [256][64] and C tile
+// [256][64] bf16, rows of 8 chunks of 16 bytes; chunk c of row r sits at
+// position c ^ ((r >> 1) & 7), which keeps the reads free of bank conflicts.
+// Tile placement: workgroup x runs on XCD x % 8 and takes the 4 row tiles
+// [4 (x % 8), 4 (x % 8) + 4) of kv_b_proj (1 MiB of W, resident in that
+// XCD's L2) for token tiles x / 32, x / 32 + 8, ...
 // ---------------------------------------------------------------------------
-constexpr int kExpTile = 128;
+constexpr int kExpTile = 256;
 constexpr int kExpStageK = 64;
-constexpr int kExpStageBytes = 2 * kExpTile * kExpStageK * 2;   // 32 KiB: W tile then C tile
-constexpr int kExpStages = kLatent / kExpStageK;                // 8
-constexpr int kExpLoads = kExpStageBytes / 16 / 256;             // 8 per lane per stage
+constexpr int kExpStageBytes = 2 * kExpTile * kExpStageK * 2;   // 64 KiB: W tile then C tile
+constexpr int kExpStages = kLatent / kExpStageK;                // 8 per tile
+constexpr int kExpLoads = kExpStageBytes / 16 / 512;             // 8 per lane per stage
+constexpr int kExpGrid = 256;                                    // persistent workgroups
+constexpr int kExpOTiles = kKvRow / kExpTile;                    // 32
+static_assert(kExpOTiles == 4 * kXcds && kExpGrid == kExpOTiles * kXcds, "tile placement");
 
-__global__ void __launch_bounds__(256, 2) expand_kv(const uint16_t* __restrict__ w, const uint8_t* __restrict__ cache,
+__global__ void __launch_bounds__(512, 2) expand_kv(const uint16_t* __restrict__ w, const uint8_t* __restrict__ cache,
                                                  int32_t L, uint16_t* __restrict__ kv) {
   __shared__ __attribute__((aligned(1024))) uint8_t st[2 * kExpStageBytes];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, n16 = lane & 15;
-  // tile of this workgroup: the 64 output tiles of a token tile run back to
-  // back on one XCD (workgroup x on XCD x % 8), sharing its cache rows in L2
   const int x = blockIdx.x;
-  const int k8 = x / kXcds;
-  const int ot = k8 % (kKvRow / kExpTile);
-  const int tt = (k8 / (kKvRow / kExpTile)) * kXcds + x % kXcds;
-  const int t0 = tt * kExpTile;
-  if (t0 >= L) return;
+  const int ot = 4 * (x % kXcds) + ((x / kXcds) & 3);
   const int o0 = ot * kExpTile;
+  const int tt0 = x / (4 * kXcds);                 // first token tile; then every 8th
+  const int ntt = (L + kExpTile - 1) / kExpTile;
+  const int ntiles = tt0 < ntt ? (ntt - tt0 + kXcds - 1) / kXcds : 0;
+  if (ntiles == 0) return;
+  const int nst = ntiles * kExpStages;
   const uint32_t st_lds = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)st);
 
-  // load i of this lane: LDS position P = (wave*8 + i)*64 + lane (16-byte
-  // units); waves 0-1 fill the W tile, waves 2-3 the C tile
-  int src_off[kExpLoads];
+  // load i of this lane: LDS position P = (wave * 8 + i) * 64 + lane
+  // (16-byte units); waves 0-3 fill the W tile, waves 4-7 the C tile.  The
+  // in-tile byte offsets are fixed; the tile and stage enter through the
+  // wave-uniform base.
+  const bool wpart = wave < 4;
+  uint32_t off[kExpLoads];
 #pragma unroll
   for (int i = 0; i < kExpLoads; ++i) {
-    const int P = (wave * kExpLoads + i) * 64 + lane;
-    const int Q = P & 1023;
+    const int Q = ((wave & 3) * kExpLoads + i) * 64 + lane;
     const int row = Q >> 3, c = (Q & 7) ^ ((row >> 1) & 7);
-    src_off[i] = (P < 1024) ? ((o0 + row) * kLatent + c * 8) * 2
-                            : (min(t0 + row, L - 1) * kRow + c * 8) * 2;
+    off[i] = (uint32_t)((wpart ? row * kLatent : row * kRow) + c * 8) * 2u;
   }
-  const uint8_t* wsrc = (const uint8_t*)w;
   auto issue = [&](int s, int buf) {
+    const int kst = s & (kExpStages - 1);
+    const int t0 = (tt0 + kXcds * (s / kExpStages)) * kExpTile;
     const uint32_t dst = st_lds + buf * kExpStageBytes + wave * kExpLoads * 1024;
+    if (wpart) {
+      const uint8_t* src = (const uint8_t*)w + ((size_t)o0 * kLatent + kst * kExpStageK) * 2;
 #pragma unroll
-    for (int i = 0; i < kExpLoads; ++i)
-      dma16((wave < 2 ? wsrc : cache) + src_off[i] + s * kExpStageK * 2, dst + i * 1024);
+      for (int i = 0; i < kExpLoads; ++i) dma16s(src, off[i], dst + i * 1024);
+    } else if (t0 + kExpTile <= L) {
+      const uint8_t* src = cache + ((size_t)t0 * kRow + kst * kExpStageK) * 2;
+#pragma unroll
+      for (int i = 0; i < kExpLoads; ++i) dma16s(src, off[i], dst + i * 1024);
+    } else {   // last token tile: rows past L repeat row L - 1
+#pragma unroll
+      for (int i = 0; i < kExpLoads; ++i) {
+        const int row = off[i] / (kRow * 2);
+        const uint32_t inrow = off[i] - row * (kRow * 2);
+        dma16(cache + ((size_t)min(t0 + row, L - 1) * kRow + kst * kExpStageK) * 2 + inrow, dst + i * 1024);
+      }
+    }
   };
 
   const int wo = wave & 1, wt = wave >> 1;
-  f32x4 acc[4][4];
+  f32x4 acc[8][4];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < 8; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // read offsets within a tile: row r (of the wave's 16-row block), chunk 4ks + g
+  // read offsets within a tile: row r, chunk 4 ks + g
   auto rd = [&](int row, int ks) -> int { return row * 128 + (((4 * ks + g) ^ ((row >> 1) & 7)) << 4); };
 
   issue(0, 0);
-  issue(1, 1);
-  for (int s = 0; s < kExpStages; ++s) {
-    if (s + 1 < kExpStages) vm_wait<kExpLoads>();
-    else vm_wait<0>();
+  if (nst > 1) issue(1, 1);
+  for (int s = 0; s < nst; ++s) {
+    // stage s has landed; stage s + 1 may still load, and after a tile's
+    // stores (issued between the loads of stages s and s + 1) those may
+    // still drain
+    if (s + 1 < nst) {
+      if (s > 0 && (s & (kExpStages - 1)) == 0) vm_wait<kExpLoads + 16>();
+      else vm_wait<kExpLoads>();
+    } else {
+      vm_wait<0>();
+    }
     lds_barrier();
     lds_cu8* W = lds_base(st_lds + (s & 1) * kExpStageBytes);
     lds_cu8* C = W + kExpTile * kExpStageK * 2;
 #pragma unroll
     for (int ks = 0; ks < kExpStageK / 32; ++ks) {
-      bf16x8 a[4], bb[4];
+      bf16x8 a[8], bb[4];
 #pragma unroll
-      for (int ob = 0; ob < 4; ++ob) a[ob] = *(lds_bf16x8_t*)(W + rd(64 * wo + 16 * ob + n16, ks));
+      for (int ob = 0; ob < 8; ++ob) a[ob] = *(lds_bf16x8_t*)(W + rd(128 * wo + 16 * ob + n16, ks));
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) bb[tb] = *(lds_bf16x8_t*)(C + rd(64 * wt + 16 * tb + n16, ks));
 #pragma unroll
-      for (int ob = 0; ob < 4; ++ob)
+      for (int ob = 0; ob < 8; ++ob)
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb)
           acc[ob][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ob], bb[tb], acc[ob][tb], 0, 0, 0);
     }
     lds_barrier();   // every wave is done with this buffer before it is refilled
-    if (s + 2 < kExpStages) issue(s + 2, s & 1);
-  }
-  // lane (g, n16) of block (ob, tb) holds rows o0 + 64wo + 16ob + 4g + i of
-  // token t0 + 64wt + 16tb + n16.  Every row of the tile is written (rows past
-  // L repeat row L - 1), so that the attention's last tile reads defined values.
+    if ((s & (kExpStages - 1)) == kExpStages - 1) {
+      // tile done: lane (g, n16) of block (ob, tb) holds rows
+      // o0 + 128 wo + 16 ob + 4 g .. + 3 of token t0 + 64 wt + 16 tb + n16.
+      // For each pair of blocks (2p, 2p + 1) one lane-row swap
+      // (v_permlane16_swap: rows [A0 B0 A2 B2], [A1 B1 A3 B3]) gives lane row
+      // g the 8 consecutive rows 16 (2p + (g & 1)) + 8 (g >> 1) .. + 7 of its
+      // token, stored as 16 bytes (64 contiguous bytes per token and pair).
+      // Every row of the tile is written (rows past L repeat row L - 1), so
+      // that the attention's last tile reads defined values.
+      const int t0 = (tt0 + kXcds * (s / kExpStages)) * kExpTile;
 #pragma unroll
-  for (int tb = 0; tb < 4; ++tb) {
-    const int t = t0 + 64 * wt + 16 * tb + n16;
+      for (int tb = 0; tb < 4; ++tb) {
+        const int t = t0 + 64 * wt + 16 * tb + n16;
+        uint16_t* krow = kv + (size_t)t * kKvStride + o0 + 128 * wo + 16 * (g & 1) + 8 * (g >> 1);
 #pragma unroll
-    for (int ob = 0; ob < 4; ++ob) {
-      s16x4 v;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = __builtin_bit_cast(short, (__bf16)acc[ob][tb][i]);
-      *(s16x4*)(kv + (size_t)t * kKvStride + o0 + 64 * wo + 16 * ob + 4 * g) = v;
+        for (int pr = 0; pr < 4; ++pr) {
+          const u32x2 a = __builtin_bit_cast(u32x2, __builtin_convertvector(acc[2 * pr][tb], bf16x4));
+          const u32x2 b = __builtin_bit_cast(u32x2, __builtin_convertvector(acc[2 * pr + 1][tb], bf16x4));
+          const auto lo = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+          const auto hi = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+          *(uint4*)(krow + 32 * pr) = make_uint4(lo[0], hi[0], lo[1], hi[1]);
+          acc[2 * pr][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          acc[2 * pr + 1][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
     }
+    if (s + 2 < nst) issue(s + 2, s & 1);
   }
-  if (ot == 0) {   // the tile's rope keys, copied next to the expanded rows
+  if (ot == 0) {   // the tiles' rope keys, copied next to the expanded rows (after the pipeline)
+    for (int k = 0; k < ntiles; ++k) {
+      const int t0 = (tt0 + kXcds * k) * kExpTile;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int e = k * 256 + tid, t = e >> 3, c = e & 7;
-      const uint4 r = *(const uint4*)(cache + (size_t)min(t0 + t, L - 1) * kRowBytes + (kLatent + 8 * c) * 2);
-      *(uint4*)(kv + (size_t)(t0 + t) * kKvStride + kKvRow + 8 * c) = r;
+      for (int j = 0; j < 4; ++j) {
+        const int e = j * 512 + tid, tk = e >> 3, c = e & 7;
+        const uint4 r = *(const uint4*)(cache + (size_t)min(t0 + tk, L - 1) * kRowBytes + (kLatent + 8 * c) * 2);
+        *(uint4*)(kv + (size_t)(t0 + tk) * kKvStride + kKvRow + 8 * c) = r;
+      }
     }
   }
 }
@@ -196,21 +252,13 @@ static_assert(kPfInstr * 1024 == kPfTileBytes && kPfWide == 4, "tile split");
 struct PrefillParams {
   const uint16_t* q_nope;   // bf16 [Tq][32][128]
   const uint16_t* q_pe;     // bf16 [Tq][32][64], rotated
-  const uint16_t* kv;       // bf16 [L rounded up to 128][8256]: expanded rows and rope keys
+  const uint16_t* kv;       // bf16 [L rounded up to 256][8256]: expanded rows and rope keys
   int32_t L, Tq, qtiles;
   float scale_log2;
   uint16_t* out;            // bf16 [Tq][32][128]
   float* lse;               // fp32 [Tq][32] or null
 };
 
-// One 16-byte direct global->LDS load from a wave-uniform base plus a
-// per-lane 32-bit offset (LDS byte lds + 16 * lane).
-__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :
-               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(sbase)
-               : "memory", "m0");
-}
 
 // Maxima of finite or infinite scores (no NaN handling needed; written as
 // the plain instructions so that no quieting of the MFMA results is added).
@@ -480,9 +528,7 @@ __global__ void __launch_bounds__(kPfWaves * 64, 2) prefill_attention(PrefillPar
 hipError_t launch_prefill(const uint16_t* q_nope, const uint16_t* q_pe, const uint16_t* w_kv_b, const uint8_t* cache,
                           int32_t L, int32_t Tq, float scale_log2, uint16_t* kv, uint16_t* out, float* lse,
                           hipStream_t stream) {
-  const int ttiles = (L + kExpTile - 1) / kExpTile;
-  const unsigned egrid = (unsigned)(((ttiles + kXcds - 1) / kXcds) * kXcds * (kKvRow / kExpTile));
-  hipLaunchKernelGGL(expand_kv, dim3(egrid), dim3(256), 0, stream, w_kv_b, cache, L, kv);
+  hipLaunchKernelGGL(expand_kv, dim3(kExpGrid), dim3(512), 0, stream, w_kv_b, cache, L, kv);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   PrefillParams pp;
   pp.q_nope = q_nope;

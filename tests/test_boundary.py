@@ -149,5 +149,6 @@ def test_prefill_argument_errors_and_workspace():
     assert M.mla_prefill_workspace_size(1024) == 1024 * 8256 * 2
     assert M.mla_prefill_workspace_size(1000) == 1024 * 8256 * 2
     assert M.mla_prefill_workspace_size(129) == 256 * 8256 * 2
+    assert M.mla_prefill_workspace_size(300) == 512 * 8256 * 2
     with pytest.raises(M.MlaError):
         M.mla_prefill_workspace_size(0)
