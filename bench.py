@@ -303,6 +303,8 @@ def main():
     ap.add_argument("--no-fp8", action="store_true", help="skip the 8-bit cache report")
     ap.add_argument("--no-more", action="store_true",
                     help="skip the report on the other workloads (batched paged, speculative verify, 512K)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="run only the chunked-prefill report (4096 new tokens on 32K and 128K contexts) and print it")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="first copy this many MiB device-to-device 3 times (reference for rocprofv3 counters)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -321,6 +323,13 @@ def main():
 
     import torch
     torch.cuda.init()
+    if args.prefill_only:
+        res = {}
+        for L, Tq in ((32768, 4096), (131072, 4096)):
+            r = run_prefill(L, Tq, args.steps, args.warmup)
+            res[r["workload"]] = r
+        print(json.dumps({"prefill": res}), flush=True)
+        return
     if args.copy_calibration_mb:
         copy_calibration(args.copy_calibration_mb << 20)
     main_res = run_workload(args.config, args.steps, args.warmup, not args.no_graph, kv_chunk=args.kv_chunk,
