@@ -15,19 +15,20 @@
 //
 // Two kernels:
 //  * expand_kv: KV[t][o] = bf16(sum_k W[o][k] c_t[k]) for the 8192 rows o of
-//    kv_b_proj (per head [k_nope 128 | v 128]); a 128 x 128 output tile per
-//    workgroup of 4 waves, v_mfma_f32_16x16x32_bf16, 64-wide k stages
-//    double-buffered in LDS through direct global->LDS loads.
+//    kv_b_proj (per head [k_nope 128 | v 128]); 256 persistent workgroups of
+//    8 waves walk 256 x 256 output tiles with one pipeline of 64-wide k stages
+//    (double-buffered in LDS through direct global->LDS loads), on
+//    v_mfma_f32_16x16x32_bf16.
 //  * prefill_attention: flash attention (rescaling only when a row's maximum
-//    outgrows its reference by 2^8); a workgroup
-//    of 4 waves takes 128 query rows of one head, each wave 32 rows (two row
-//    groups of 16, so every LDS read of a key or value tile feeds two MFMAs);
-//    64-token tiles of [K_nope | k_pe] and V stream through a two-tile LDS
-//    ring.  S^T = K . Q^T with the keys as the A operand; the S^T accumulator
-//    layout is the B-operand layout of P in O^T += V^T P^T, with V^T fetched
-//    by ds_read_b64_tr_b16, so P stays in registers.  The query tiles of a
-//    head are placed on one XCD (workgroups x, x + 8, ...), where they read
-//    the head's key and value tiles from the same L2.
+//    outgrows its reference by 2^8); a workgroup of 8 waves takes 256 query
+//    rows of one head, each wave 32 rows (two row groups of 16, so every LDS
+//    read of a key or value tile feeds two MFMAs); 64-token tiles of
+//    [K_nope | k_pe] and V stream through a three-tile LDS ring.
+//    S^T = K . Q^T with the keys as the A operand; the S^T accumulator layout
+//    is the B-operand layout of P in O^T += V^T P^T, with V^T fetched by
+//    ds_read_b64_tr_b16, so P stays in registers.  The query tiles of a head
+//    are placed on one XCD (workgroups x, x + 8, ...), where they read the
+//    head's key and value tiles from the same L2.
 #include "mla_internal.h"
 
 namespace mla {
@@ -258,7 +259,6 @@ struct PrefillParams {
   uint16_t* out;            // bf16 [Tq][32][128]
   float* lse;               // fp32 [Tq][32] or null
 };
-
 
 // Maxima of finite or infinite scores (no NaN handling needed; written as
 // the plain instructions so that no quieting of the MFMA results is added).
