@@ -77,6 +77,19 @@ __device__ __forceinline__ void wait_slots_ahead(int ahead) {
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// One 16-byte direct global->LDS load from a wave-uniform base plus a
+// per-lane 32-bit offset (LDS byte lds + 16 * lane).
+// The base must be wave-uniform; it is moved to scalar registers explicitly.
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds) {
+  const uint64_t a = (uint64_t)(uintptr_t)sbase;
+  const uint64_t su = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"((const void*)(uintptr_t)su)
+               : "memory", "m0");
+}
+
 // One 16-byte direct global->LDS load (LDS byte lds + 16 * lane).
 __device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
@@ -154,12 +167,26 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode_fp8(DecodeParams p
     }
     const int nval = min(kSlotTok, t_end - ts * kSlotTok);
     const uint32_t dst = ring_lds + r * kSlotLds + wave * kLoadsPerLane * 1024;
+    if (nval == kSlotTok) {
+      // a whole slot: byte offset 16 P from the slot's (wave-uniform) start;
+      // the pad positions P >= kChunks re-read the slot's first chunks.  (The
+      // lane's offset is recomputed here, not kept in a register.)
+      uint32_t dma_base = (uint32_t)lane;
+      asm volatile("" : "+v"(dma_base));
+      dma_base = 16u * (dma_base + (uint32_t)(wave * kLoadsPerLane * 64));
 #pragma unroll
-    for (int i = 0; i < kLoadsPerLane; ++i) {
-      const int P = (wave * kLoadsPerLane + i) * 64 + lane;
-      const int tok = (P < kChunks) ? P / kF8ChunksPerRow : kSlotTok;
-      const uint8_t* a = (tok < nval) ? src + P * 16 : p.zero_row + (P % kF8ChunksPerRow) * 16;
-      dma16(a, dst + i * 1024);
+      for (int i = 0; i < kLoadsPerLane; ++i) {
+        const bool pad = wave * kLoadsPerLane + i >= kChunks / 64;
+        dma16s(src, dma_base + 1024u * i - (pad ? (uint32_t)kSlotBytes : 0u), dst + i * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kLoadsPerLane; ++i) {
+        const int P = (wave * kLoadsPerLane + i) * 64 + lane;
+        const int tok = (P < kChunks) ? P / kF8ChunksPerRow : kSlotTok;
+        const uint8_t* a = (tok < nval) ? src + P * 16 : p.zero_row + (P % kF8ChunksPerRow) * 16;
+        dma16(a, dst + i * 1024);
+      }
     }
   };
 
