@@ -34,7 +34,10 @@ def gpu_run(seed, L, Tq, layer=0, reps=1):
     return outs
 
 
-@pytest.mark.parametrize("L,Tq", [(1024, 256), (333, 100), (200, 200), (777, 1), (130, 129)])
+# one token; exactly one and one-plus 256-token expansion tile; query tiles of
+# 256 rows with a ragged last tile; a context that is all query tokens
+@pytest.mark.parametrize("L,Tq", [(1024, 256), (333, 100), (200, 200), (777, 1), (130, 129), (1, 1), (256, 256),
+                                  (257, 2), (2100, 600), (600, 600)])
 def test_prefill_matches_the_unabsorbed_oracle(L, Tq):
     go, gl, _ = gpu_run(81, L, Tq, layer=1)[0]
     ref_o, ref_l = expected(81, 1, L, Tq, 0)
