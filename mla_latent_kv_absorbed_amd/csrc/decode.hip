@@ -12,15 +12,19 @@
 // Work decomposition (one workgroup of 8 waves, two per SIMD, per split and
 // query group; a segment record {b, first token, end token, L_b} of the
 // call's schedule describes the split):
-//  * The split streams through LDS in 64-token slots (one page, 72 KiB) of a
-//    two-slot ring, filled by direct global->LDS 16-byte loads (9 per lane
-//    per slot): while the waves consume one slot the next is in flight.  Slot
-//    rows are swizzled at 16-byte granularity (latent chunk c of token t sits
-//    at c ^ (t & 15), rope chunk 64+k at 64 + (k ^ ((t >> 1) & 7))) so that
-//    the read patterns below are free of LDS bank conflicts.
-//  * The query rows come in the same way, ahead of the first slot, into the
-//    second ring position (same swizzle), from where each wave takes its 16
-//    rows into registers; only then is the second slot requested.  The
+//  * The split streams through LDS in 64-token slots (one page) of a
+//    two-slot ring, filled by direct global->LDS 16-byte loads (9 or 10 per
+//    lane per slot): while the waves consume one slot the next is in flight.
+//    A slot row in LDS is the token's 1,152 bytes followed by 32 pad bytes
+//    (1,184-byte rows): with that stride both read patterns below are free of
+//    LDS bank conflicts (measured with the bank-conflict counter; the
+//    XOR-swizzled 1,152-byte rows used before conflicted two-way on the
+//    score reads), and every read of a slot is one per-lane base plus an
+//    immediate offset.
+//  * The query rows come ahead of the first slot into the second ring
+//    position (1,152-byte rows, latent chunk c of row r at c ^ (r & 15), rope
+//    chunk 64+k at 64 + (k ^ ((r >> 1) & 7))), from where each wave takes its
+//    16 rows into registers; only then is the second slot requested.  The
 //    first slot is thus awaited on its own, not behind later slots.
 //  * The 32*QG query rows (query token, head) are cut into row groups of 16.
 //    Scores: wave w takes row group w % RG and a 64/TPW-token share of each
@@ -53,11 +57,14 @@ constexpr float kTau = 64.0f;          // log2 headroom of p above the reference
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kSlotTok = 64;           // tokens per ring slot (one page)
-constexpr int kSlotBytes = kSlotTok * kRowBytes;   // 73728
+constexpr int kRowLds = kRowBytes + 32;                     // 1184: LDS bytes per slot row
+constexpr int kSlotLds = kSlotTok * kRowLds;                // 75776
+constexpr int kSlotInstr = kSlotLds / 1024;                 // 74 wave-wide direct loads per slot
+constexpr int kWide = kSlotInstr - 9 * kWaves;              // waves 0..1 issue 10 loads per slot, the rest 9
 constexpr int kSlots = 2;              // ring slots: one in flight while one is consumed
-constexpr int kLoadsPerLane = kSlotBytes / 16 / kThreads;   // 9
+constexpr int kQLoads = 9;             // query-row loads per lane of a wave that has query rows
 constexpr int kCbPerWave = kLatent / 16 / kWaves;           // 4 column blocks of 16 per wave
-static_assert(kLoadsPerLane * 16 * kThreads == kSlotBytes, "slot split");
+static_assert(kSlotInstr * 1024 == kSlotLds && kWide == 2, "slot split");
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 typedef __attribute__((address_space(3))) const uint8_t lds_cu8;
@@ -75,12 +82,15 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Wait until at most `ahead` (0 or 1) slots' worth of direct loads
-// (PER_SLOT per lane per slot) are still outstanding.
-template <int PER_SLOT>
-__device__ __forceinline__ void wait_slots_ahead(int ahead) {
-  if (ahead >= 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PER_SLOT) : "memory");
-  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+// Wait until at most `ahead` (0 or 1) slots' worth of this wave's direct
+// loads (10 per slot for the wide waves, else 9) are still outstanding.
+__device__ __forceinline__ void wait_slots_ahead(bool wide, int ahead) {
+  if (ahead >= 1) {
+    if (wide) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
 }
 
 // One 16-byte direct global->LDS load: LDS byte lds + 16 * lane receives the
@@ -94,7 +104,19 @@ __device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds) {
                : "memory", "m0");
 }
 
-// Chunk <-> slot-row position swizzle (an involution within each group).
+// The same from a wave-uniform base (moved to scalar registers) plus a
+// per-lane 32-bit offset.
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds) {
+  const uint64_t a = (uint64_t)(uintptr_t)sbase;
+  const uint64_t su = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"((const void*)(uintptr_t)su)
+               : "memory", "m0");
+}
+
+// Chunk <-> query-row position swizzle (an involution within each group).
 __device__ __forceinline__ int tile_slot(int tok, int c) {
   return c < 64 ? (c ^ (tok & 15)) : (64 + ((c - 64) ^ ((tok >> 1) & 7)));
 }
@@ -106,10 +128,11 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode(DecodeParams p) {
   constexpr int TPW = kWaves / RG;     // score waves per row group
   constexpr int TOKW = kSlotTok / TPW; // tokens of each slot one score wave handles
   constexpr int NBLK = TOKW / 16;      // 16-token score blocks per slot and wave
-  constexpr int kQkRing = QG == 1 ? 8 : 4;   // score operand reads in flight per wave
-  static_assert((ROWS * kChunksPerRow) % (kLoadsPerLane * 64) == 0, "query rows fill whole waves' loads");
+  constexpr int kQkRing = QG == 1 ? 8 : 6;   // score operand reads in flight per wave
+  static_assert((ROWS * kChunksPerRow) % (kQLoads * 64) == 0, "query rows fill whole waves' loads");
+  static_assert(ROWS * kRowBytes <= kSlotLds, "query rows fit in a ring position");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[kSlots * kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kSlots * kSlotLds];
   // P in bf16, [row group][32-token step][row][32 tokens in MFMA k order]
   __shared__ __attribute__((aligned(16))) uint8_t pbuf[RG * 2 * 16 * 64];
   __shared__ float stat[3][TPW][ROWS];   // per score wave and row: slot max, sum, true max
@@ -134,16 +157,21 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode(DecodeParams p) {
   const int j = j_grp < p.Sq ? j_grp : p.Sq - 1;
   const int limit = min(t_end, L - p.Sq + j + 1);   // rows of this wave see tokens < limit
 
-  // Byte offset inside a slot of each 16-byte chunk this lane loads: LDS
-  // position P = (wave*kLoadsPerLane + i)*64 + lane holds chunk (tok = P / 72,
-  // tile_slot(tok, P % 72)) of the slot's token tok.
-  int off[kLoadsPerLane];
+  // Slot loads: wave-wide load I of a slot fills LDS bytes [1024 I,
+  // 1024 (I + 1)) of the ring position; waves 0..1 issue loads 10w .. 10w + 9,
+  // waves 2..7 loads 2 + 9w .. + 8.  Lane position P = 64 I + lane (16-byte
+  // units) is chunk P % 74 of the slot's token P / 74; chunks 72 and 73 are
+  // the row's pad and repeat chunks 0 and 1.  off[i]: the chunk's byte offset
+  // in the slot's cache rows (the same for every slot).
+  const bool wide = wave < kWide;
+  const int i0 = wide ? 10 * wave : kWide + 9 * wave;
+  uint32_t off[10];
 #pragma unroll
-  for (int i = 0; i < kLoadsPerLane; ++i) {
-    const int P = (wave * kLoadsPerLane + i) * 64 + lane;
-    const int tok = P / kChunksPerRow;
-    const int c = tile_slot(tok, P - tok * kChunksPerRow);
-    off[i] = tok * kRowBytes + c * 16;
+  for (int i = 0; i < 10; ++i) {
+    const int P = (i0 + i) * 64 + lane;
+    const int tok = P / (kRowLds / 16);
+    const int c = P - tok * (kRowLds / 16);
+    off[i] = (uint32_t)(tok * kRowBytes + (c < kChunksPerRow ? c : c - kChunksPerRow) * 16);
   }
   const uint32_t ring_lds = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)ring);
 
@@ -151,8 +179,8 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode(DecodeParams p) {
   const int nslot = (t_end - t_begin + kSlotTok - 1) / kSlotTok;
 
   // Enqueue the split's slot `ts` (absolute slot index) into ring slot
-  // `r`.  Every lane issues exactly kLoadsPerLane loads; rows past the end of
-  // the split come from the zero row, so masked tokens multiply zeros.
+  // `r`; rows past the end of the split come from the zero row, so masked
+  // tokens multiply zeros.
   auto issue = [&](int ts, int r) {
     const uint8_t* src;
     if constexpr (PAGED) {
@@ -162,13 +190,15 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode(DecodeParams p) {
       src = p.cache + ((size_t)b * p.stride_tokens + (size_t)ts * kSlotTok) * kRowBytes;
     }
     const int nval = min(kSlotTok, t_end - ts * kSlotTok);
-    const uint32_t dst = ring_lds + r * kSlotBytes + wave * kLoadsPerLane * 1024;
+    const uint32_t dst = ring_lds + r * kSlotLds + i0 * 1024;
     if (nval == kSlotTok) {
 #pragma unroll
-      for (int i = 0; i < kLoadsPerLane; ++i) dma16(src + off[i], dst + i * 1024);
+      for (int i = 0; i < 9; ++i) dma16s(src, off[i], dst + i * 1024);
+      if (wide) dma16s(src, off[9], dst + 9 * 1024);
     } else {
 #pragma unroll
-      for (int i = 0; i < kLoadsPerLane; ++i) {
+      for (int i = 0; i < 10; ++i) {
+        if (i == 9 && !wide) break;
         const int tok = off[i] / kRowBytes;
         const uint8_t* a = (tok < nval) ? src + off[i] : p.zero_row + (off[i] - tok * kRowBytes);
         dma16(a, dst + i * 1024);
@@ -176,57 +206,47 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode(DecodeParams p) {
     }
   };
 
-  // Offsets of the score reads within a 16-row block of a slot (or of the
-  // query rows): row n16, chunk 4*ks + g sits at position (4ks + g) ^ n16 =
-  // 16*(ks/4) + ((4*(ks%4)) ^ (g ^ n16)); rope chunks 64 + ((4kk + g) ^ (n16 >> 1)).
-  int qk_off[4];
+  // ---- prologue: the query rows (row r of the group as "token" r, 1,152-byte
+  // rows, chunk c at tile_slot(r, c)) into the second ring position, by the
+  // waves 0 .. ROWS * 72 / 576 - 1 (9 loads each), the first slot into the first
+  if (wave * kQLoads * 64 < ROWS * kChunksPerRow) {
+    const uint32_t dst = ring_lds + kSlotLds + wave * kQLoads * 1024;
 #pragma unroll
-  for (int bb = 0; bb < 4; ++bb) qk_off[bb] = n16 * kRowBytes + (((4 * bb) ^ (g ^ n16)) << 4);
-  int rope_off[2];
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk) rope_off[kk] = n16 * kRowBytes + ((64 + ((4 * kk + g) ^ (n16 >> 1))) << 4);
-  auto row_chunk = [&](int ks) -> int { return ks < 16 ? qk_off[ks & 3] + (ks >> 2) * 256 : rope_off[ks - 16]; };
-
-  // ---- prologue: the query rows (row r of the group as "token" r) into the
-  // second ring position, the first slot into the first
-  if (wave * kLoadsPerLane * 64 < ROWS * kChunksPerRow) {
-    const uint32_t dst = ring_lds + kSlotBytes + wave * kLoadsPerLane * 1024;
-#pragma unroll
-    for (int i = 0; i < kLoadsPerLane; ++i) {
-      const int r = off[i] / kRowBytes;
+    for (int i = 0; i < kQLoads; ++i) {
+      const int P = (wave * kQLoads + i) * 64 + lane;
+      const int r = P / kChunksPerRow;
+      const int c = tile_slot(r, P - r * kChunksPerRow);
       const int jj = min(QG * grp + (r >> 5), p.Sq - 1);
-      const uint8_t* src = (const uint8_t*)p.qabs + (((size_t)b * p.Sq + jj) * 32 + (r & 31)) * kRowBytes +
-                           (off[i] - r * kRowBytes);
+      const uint8_t* src = (const uint8_t*)p.qabs + (((size_t)b * p.Sq + jj) * 32 + (r & 31)) * kRowBytes + c * 16;
       dma16(src, dst + i * 1024);
     }
   }
   issue(s0, 0);
-  wait_slots_ahead<kLoadsPerLane>(1);   // the query rows (older than the first slot) have landed
+  wait_slots_ahead(wide, 1);   // the query rows (older than the first slot) have landed
   lds_barrier();
   bf16x8 q[18];   // this wave's 16 query rows as MFMA B operands: lane holds row n16, 8 dims
   {
-    const uint8_t* qb = ring + kSlotBytes + rg * 16 * kRowBytes;
+    // row n16, chunk 4*ks + g at position (4ks + g) ^ n16 = 16*(ks/4) +
+    // ((4*(ks%4)) ^ (g ^ n16)); rope chunks 64 + ((4kk + g) ^ (n16 >> 1))
+    const uint8_t* qb = ring + kSlotLds + (rg * 16 + n16) * kRowBytes;
 #pragma unroll
-    for (int ks = 0; ks < 18; ++ks) q[ks] = *(const bf16x8*)(qb + row_chunk(ks));
+    for (int ks = 0; ks < 18; ++ks) {
+      const int pos = ks < 16 ? 16 * (ks >> 2) + ((4 * (ks & 3)) ^ (g ^ n16)) : 64 + ((4 * (ks - 16) + g) ^ (n16 >> 1));
+      q[ks] = *(const bf16x8*)(qb + pos * 16);
+    }
   }
   lds_barrier();   // every wave has its query rows before the second slot overwrites them
   if (nslot > 1) issue(s0 + 1, 1);
 
+  // Score reads of a slot: token n16 of a 16-token block, chunk 4*ks + g
+  // (rope chunks 64 + 4kk + g follow the latent ones): one base per lane.
+  const int qk_lane = n16 * kRowLds + g * 16;
   // Value reads (transposed, 8 bytes): token 4g + (n16 >> 2) (+16 for the
   // upper half of a 32-token step, +32 for the second step), columns
-  // 16*cb + 4*(n16 & 3); chunk 2cb + ((n16 >> 1) & 1) sits at position
-  // 16*(cb/8) + ((2*(cb%8)) ^ v).  This wave's blocks: cb = 4*wave + c.
-  int pv_off[kCbPerWave];
-  {
-    const int pv_tok = 4 * g + (n16 >> 2);
-    const int pv_v = ((n16 >> 1) & 1) ^ (pv_tok & 15);
-    const int pv_row = pv_tok * kRowBytes + (n16 & 1) * 8;
-#pragma unroll
-    for (int c = 0; c < kCbPerWave; ++c) {
-      const int cb = kCbPerWave * wave + c;
-      pv_off[c] = pv_row + (((2 * (cb & 7)) ^ pv_v) << 4) + (cb >> 3) * 256;
-    }
-  }
+  // 16*cb + 4*(n16 & 3) (chunk 2cb + ((n16 >> 1) & 1), bytes 8 (n16 & 1)).
+  // This wave's blocks: cb = 4*wave + c.
+  const int pv_lane = (4 * g + (n16 >> 2)) * kRowLds + (n16 & 1) * 8 + ((n16 >> 1) & 1) * 16 +
+                      kCbPerWave * wave * 32;
   // P reads: row n16 of a row group, one 32-token step: 16 bytes at k = 8g.
   const int pb_rd = n16 * 64 + g * 16;
 
@@ -249,7 +269,7 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode(DecodeParams p) {
     constexpr int NQK = NBLK * 18;
     auto qk_src = [&](int i) -> lds_bf16x8_t* {
       const int blk = i % NBLK, ks = i / NBLK;
-      return (lds_bf16x8_t*)(T + (tok0 + blk * 16) * kRowBytes + row_chunk(ks));
+      return (lds_bf16x8_t*)(T + (tok0 + blk * 16) * kRowLds + qk_lane + ks * 64);
     };
     f32x4 s[NBLK];
 #pragma unroll
@@ -323,9 +343,9 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode(DecodeParams p) {
       s16x4 lo[kCbPerWave], hi[kCbPerWave];
 #pragma unroll
       for (int c = 0; c < kCbPerWave; ++c) {
-        lds_cu8* a = T + pv_off[c] + ks * 32 * kRowBytes;
+        lds_cu8* a = T + pv_lane + c * 32 + ks * 32 * kRowLds;
         lo[c] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)a);
-        hi[c] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(a + 16 * kRowBytes));
+        hi[c] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(a + 16 * kRowLds));
       }
 #pragma unroll
       for (int c = 0; c < kCbPerWave; ++c) {
@@ -344,10 +364,10 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode(DecodeParams p) {
   // its reference by kTau.
   for (;;) {
     for (int it = 0; it < nslot; ++it) {
-      wait_slots_ahead<kLoadsPerLane>((it == 0 && nslot > 1) ? 1 : 0);
+      wait_slots_ahead(wide, (it == 0 && nslot > 1) ? 1 : 0);
       lds_barrier();
       if (it >= 1 && it + 1 < nslot) issue(s0 + it + 1, (it + 1) % kSlots);
-      process(slot_base(ring_lds + (it % kSlots) * kSlotBytes), s0 + it, it == 0);
+      process(slot_base(ring_lds + (it % kSlots) * kSlotLds), s0 + it, it == 0);
     }
     // row sums and true maxima of each score wave's token share
     float lsum = l_part;
