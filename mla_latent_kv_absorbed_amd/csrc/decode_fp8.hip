@@ -10,8 +10,8 @@
 // E4M3 values are exact in bf16, so both products stay on bf16 MFMA.  The
 // work is split as in the bf16 kernel (8 waves, two per SIMD; scores by row
 // group and token share, the value product by latent columns, P through LDS):
-//  * scores: the codes of 32 latent columns are read as 8 bytes per lane
-//    (ds_read_b64) and widened to bf16 exactly; each 128-column group has its
+//  * scores: the codes of 64 latent columns are read as 16 bytes per lane
+//    (ds_read_b128), two MFMA steps, and widened to bf16 exactly; each 128-column group has its
 //    own score accumulator, and the four are combined with the tokens'
 //    scales (the rope part has its own accumulator, unscaled);
 //  * values: O^T = C^T P'^T with P'_g = bf16(p * scale_{t,g}) for the
@@ -51,7 +51,9 @@ constexpr int kCbPerWave = kLatent / 16 / kWaves;          // 4 column blocks of
 
 typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2_t;
+typedef __attribute__((address_space(3))) const i32x4 lds_i32x4_t;
 typedef __attribute__((address_space(3))) const uint8_t lds_cu8;
 typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8_t;
 typedef __attribute__((address_space(3))) const f32x4 lds_f32x4_t;
@@ -124,7 +126,9 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode_fp8(DecodeParams p
   static_assert(ROWS * kRowBytes <= (kSlots - 1) * kSlotLds, "query rows fit in ring positions 1..2");
 
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kSlots * kSlotLds];
-  // p in fp32, [row group][32-token step][row][32 tokens in MFMA k order]
+  // p in fp32, [row group][32-token step][row][32 tokens in MFMA k order];
+  // 16-byte granule q of row r is stored at granule q ^ ((r % 16) >> 1), so the
+  // 16 lanes of a row block touch 16 different bank groups
   __shared__ __attribute__((aligned(16))) uint8_t pbuf[RG * 2 * 16 * 128];
   __shared__ float stat[3][TPW][ROWS];   // per score wave and row: slot max, sum, true max
   __shared__ int flags[kWaves];
@@ -190,11 +194,13 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode_fp8(DecodeParams p
     }
   };
 
-  // Score reads of the bf16 query rows (swizzled like bf16 cache tiles):
-  // row n16, chunk 4*ks + g at 16*(ks/4) + ((4*(ks%4)) ^ (g ^ n16)); rope
-  // chunks 64 + ((4kk + g) ^ (n16 >> 1)).
+  // Score reads of the bf16 query rows (swizzled like bf16 cache tiles): the
+  // codes of a row are read 16 bytes a lane, lane g taking latent columns
+  // 64m + 16g .. 64m + 16g + 15 of 64-column block m, whose halves are MFMA
+  // steps 2m and 2m + 1; so step ks needs query chunk c = 8(ks/2) + 2g + ks%2,
+  // stored at c ^ n16.  Rope chunks 64 + ((4kk + g) ^ (n16 >> 1)).
   auto q_chunk = [&](int ks) -> int {
-    return n16 * kRowBytes + (ks < 16 ? ((((4 * (ks & 3)) ^ (g ^ n16)) << 4) + (ks >> 2) * 256)
+    return n16 * kRowBytes + (ks < 16 ? (((8 * (ks >> 1) + 2 * g + (ks & 1)) ^ n16) << 4)
                                       : ((64 + ((4 * (ks - 16) + g) ^ (n16 >> 1))) << 4));
   };
 
@@ -233,7 +239,9 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode_fp8(DecodeParams p
   const int vtok = (r8 < 4) ? 4 * g + r8 : 12 + 4 * g + r8;
   const int v_off = vtok * kF8Row + (lane & 1) * 8 + kCbPerWave * wave * 16;
   const int pgrp = wave >> 1;
-  const int pb_rd = n16 * 128 + g * 32;
+  // the two 16-byte granules of lane (n16, g) in P row n16, granule ^ (n16 >> 1)
+  const int pb_rd0 = n16 * 128 + ((2 * g) ^ (n16 >> 1)) * 16;
+  const int pb_rd1 = n16 * 128 + ((2 * g + 1) ^ (n16 >> 1)) * 16;
   // scale of group pgrp of the tokens behind k = 8g + i of a 32-token step
   int sc_off[8];
 #pragma unroll
@@ -262,32 +270,35 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode_fp8(DecodeParams p
 #pragma unroll
     for (int blk = 0; blk < NBLK; ++blk) {
       __builtin_amdgcn_sched_barrier(0);
-      lds_cu8* rowb = T + (tok0 + 16 * blk + n16) * kF8Row + g * 8;
+      lds_cu8* rowb = T + (tok0 + 16 * blk + n16) * kF8Row + g * 16;
       f32x4 sg[5];
 #pragma unroll
       for (int k = 0; k < 5; ++k) sg[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-      i32x2 cur[4], nxt[4];
+      i32x4 cur[2], nxt[2];   // 64-column blocks 2k, 2k + 1 of group k
 #pragma unroll
-      for (int i = 0; i < 4; ++i) cur[i] = *(const lds_i32x2_t*)(rowb + i * 32);
+      for (int i = 0; i < 2; ++i) cur[i] = *(const lds_i32x4_t*)(rowb + i * 64);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         if (k < 3) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) nxt[i] = *(const lds_i32x2_t*)(rowb + (4 * (k + 1) + i) * 32);
+          for (int i = 0; i < 2; ++i) nxt[i] = *(const lds_i32x4_t*)(rowb + (2 * (k + 1) + i) * 64);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sg[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(cur[i]), q[4 * k + i], sg[k], 0, 0, 0);
+        for (int i = 0; i < 4; ++i) {
+          const i32x4 w = cur[i >> 1];
+          const i32x2 h = (i & 1) ? i32x2{w[2], w[3]} : i32x2{w[0], w[1]};
+          sg[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(h), q[4 * k + i], sg[k], 0, 0, 0);
+        }
         __builtin_amdgcn_sched_barrier(0);
         if (k < 3) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) cur[i] = nxt[i];
+          for (int i = 0; i < 2; ++i) cur[i] = nxt[i];
         }
       }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8 rp = *(lds_bf16x8_t*)(rowb - g * 8 + kF8RopeOff + kk * 64 + g * 16);
+        const bf16x8 rp = *(lds_bf16x8_t*)(rowb + kF8RopeOff + kk * 64);
         sg[4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rp, q[16 + kk], sg[4], 0, 0, 0);
       }
       // combine the groups with the tokens' scales, scale, mask
@@ -332,7 +343,7 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode_fp8(DecodeParams p
       }
       const int t16 = tok0 + blk * 16;
       const int ks = t16 >> 5, bb = (t16 >> 4) & 1;
-      *(f32x4*)(pbuf + ((rg * 2 + ks) * 16 + n16) * 128 + (8 * g + 4 * bb) * 4) = pf;
+      *(f32x4*)(pbuf + ((rg * 2 + ks) * 16 + n16) * 128 + ((2 * g + bb) ^ (n16 >> 1)) * 16) = pf;
     }
     lds_barrier();
 
@@ -351,8 +362,8 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode_fp8(DecodeParams p
       bf16x8 pb[RG];
 #pragma unroll
       for (int r2 = 0; r2 < RG; ++r2) {
-        const uint8_t* pr = pbuf + (r2 * 2 + ks) * 2048 + pb_rd;
-        const f32x4 p0 = *(const f32x4*)pr, p1 = *(const f32x4*)(pr + 16);
+        const uint8_t* pr = pbuf + (r2 * 2 + ks) * 2048;
+        const f32x4 p0 = *(const f32x4*)(pr + pb_rd0), p1 = *(const f32x4*)(pr + pb_rd1);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           pb[r2][i] = (__bf16)(p0[i] * scl[i]);
