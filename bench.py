@@ -19,6 +19,13 @@ sequence (batch 32, log-uniform contexts in [4096, 131072], paged) and one
 sequence of 524288 tokens, all with the device-balanced split; "prefill" the
 chunked prefill (un-absorbed form) of 4096 new tokens on 32K and 128K
 contexts, in TFLOP/s against the 2.5 PFLOP/s bf16 matrix peak.
+"ctx1k_one_layer" times one decode call on a 1024-token context (one layer)
+hot and after a 512 MiB write that flushes the caches; "read_ceiling" is
+the best rate of the library's streaming-read probe over 1 and 4 GiB, the
+practical HBM read ceiling on the same device; "kernel_tflops" fields are
+algorithmic flops (69,632 per visible token and query token) over the
+split-KV kernel's duration.  "cpu_baseline" also carries the absorbed fp64
+CPU reference timed on the same layers.
 
 Output: one JSON line.  "value" is decode tokens/s (batch * query tokens per
 step / step time, timed over --steps replays of a HIP graph of the step).
@@ -44,6 +51,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MLA decode tokens/s + latent-KV GB/s (% HBM peak) at 32K and 256K ctx, 1 GPU"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
 MFMA_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 matrix peak, 2.5 PFLOP/s
+FLOPS_PER_TOKEN_QUERY = 2 * 32 * 576 + 2 * 32 * 512   # scores + value product per (visible token, query token)
 BYTES_PER_TOKEN_LAYER = 1152    # 576 bf16 cached values per token per layer
 BYTES_PER_TOKEN_LAYER_FP8 = 656  # 512 E4M3 codes + 4 fp32 scales + 64 bf16 rope values
 COUNTERS = os.path.join(ROOT, "profiles", "splitkv_decode_counters.json")
@@ -134,6 +142,9 @@ def run_workload(k: int, steps: int, warmup: int, use_graph: bool, kv_chunk=None
     tokens_ctx = sum(dw.lens)
     bytes_per_launch = tokens_ctx * (BYTES_PER_TOKEN_LAYER_FP8 if cache_dtype == "fp8" else BYTES_PER_TOKEN_LAYER)
     avg_kernel_s = kern_ms / 1e3 / launches
+    # query token j of sequence b sees L_b - Sq + j + 1 tokens
+    visible = sum(L * Sq - Sq * (Sq - 1) // 2 for L in dw.lens)
+    flops_per_launch = FLOPS_PER_TOKEN_QUERY * visible
     step_bytes = bytes_per_launch * len(layers)
     res = dict(
         workload=wl.name, batch=B, query_tokens=Sq, context=list(dw.lens) if B <= 4 else f"{B} seqs, sum {tokens_ctx}",
@@ -143,10 +154,87 @@ def run_workload(k: int, steps: int, warmup: int, use_graph: bool, kv_chunk=None
         step_latent_gbps=step_bytes / (ms_per_step / 1e3) / 1e9,
         kernel_avg_us=avg_kernel_s * 1e6, kernel_bytes_per_launch=bytes_per_launch,
         kernel_latent_gbps=bytes_per_launch / avg_kernel_s / 1e9,
+        kernel_tflops=flops_per_launch / avg_kernel_s / 1e12,
     )
     del layers, outs, lses, ref, graph
     torch.cuda.empty_cache()
     return res
+
+
+def run_latency(k: int, kv_chunk: int, reps: int = 50, flush_mb: int = 512):
+    """One decode call of the one-layer workload k, in a HIP graph: microseconds per call hot
+    (200 back-to-back replays) and cold (median over `reps` replays, each after a
+    flush_mb MiB write that evicts the 256 MB Infinity Cache and the L2s)."""
+    import statistics
+    import torch
+    from mla_latent_kv_absorbed_amd.workload import DeviceWorkload
+    from synth.configs import workload
+
+    wl = workload(k)
+    dw = DeviceWorkload(wl, kv_chunk=kv_chunk)
+    li = dw.build_layer(0)
+    out = torch.empty((dw.B, dw.Sq, 32, 128), dtype=torch.bfloat16, device=dw.dev)
+    lse = torch.empty((dw.B, dw.Sq, 32), dtype=torch.float32, device=dw.dev)
+    dw.step(li, out=out, lse=lse)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dw.step(li, out=out, lse=lse)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dw.step(li, out=out, lse=lse)
+    for _ in range(5):
+        graph.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(200):
+        graph.replay()
+    b.record()
+    torch.cuda.synchronize()
+    hot_us = a.elapsed_time(b) / 200 * 1e3
+    scratch = torch.empty(flush_mb << 20, dtype=torch.uint8, device=dw.dev)
+    cold = []
+    for r in range(reps):
+        scratch.fill_(r & 255)
+        a.record()
+        graph.replay()
+        b.record()
+        torch.cuda.synchronize()
+        cold.append(a.elapsed_time(b) * 1e3)
+    res = dict(workload=wl.name, context=list(dw.lens), kv_chunk=dw.chunk_used, hot_us_per_call=hot_us,
+               cold_us_per_call=statistics.median(cold), flush_mb=flush_mb)
+    del li, dw, out, lse, graph, scratch
+    torch.cuda.empty_cache()
+    return res
+
+
+def read_ceiling(sizes=(1 << 30, 4 << 30), reps: int = 10):
+    """GB/s of the library's streaming-read probe over device buffers of the given sizes
+    (each read `reps` times back to back); the ceiling is the best of them."""
+    import torch
+    import mla_latent_kv_absorbed_amd as M
+
+    sink = torch.zeros(M.READ_PROBE_SINK_INTS, dtype=torch.int32, device="cuda")
+    rates = {}
+    for nbytes in sizes:
+        buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        buf.fill_(7)
+        for _ in range(2):
+            M.mla_read_probe(buf, sink)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            M.mla_read_probe(buf, sink)
+        b.record()
+        torch.cuda.synchronize()
+        rates[f"{nbytes >> 20}MiB"] = nbytes / (a.elapsed_time(b) / reps * 1e-3) / 1e9
+        del buf
+        torch.cuda.empty_cache()
+    return dict(kernel="read_probe", gbps_by_size=rates, gbps=max(rates.values()))
 
 
 def run_prefill(L: int, Tq: int, steps: int, warmup: int, seed: int = 8):
@@ -199,7 +287,7 @@ def cpu_baseline(k: int, budget_s: float = 15.0):
     f = O.bf16_bits_to_float
     inv = O.yarn_inv_freq()
     scale = O.softmax_scale()
-    layers, spent = 0, 0.0
+    layers, spent, spent_abs = 0, 0.0, 0.0
     while layers < wl.layers and spent < budget_s:
         c = f(synth.latent_bits(seed, layers, 0, 0, L))
         kk = O.round_to_bf16(O.rope_rotate(f(synth.kpe_bits(seed, layers, 0, 0, L)), np.arange(L), inv))
@@ -210,15 +298,22 @@ def cpu_baseline(k: int, budget_s: float = 15.0):
         t0 = time.perf_counter()
         O.mla_attention_unabsorbed(qn, qp, c, kk, w, scale)
         spent += time.perf_counter() - t0
+        t0 = time.perf_counter()
+        O.mla_attention_absorbed(qn, qp, c, kk, w, scale)
+        spent_abs += time.perf_counter() - t0
         layers += 1
     per_layer = spent / layers
     step_s = per_layer * wl.layers * wl.batch
+    abs_step_s = spent_abs / layers * wl.layers * wl.batch
     threads = sum(p.get("num_threads", 0) for p in threadpoolctl.threadpool_info() if p.get("user_api") == "blas")
     return {"value": wl.batch * Sq / step_s, "unit": "tokens/s", "cores": threads or os.cpu_count(),
             "kind": "oracle",
             "sample": (f"un-absorbed fp64 oracle, sequence 0 of {wl.name}, all 32 heads over the full {L}-token "
                        f"context, layers 0..{layers - 1}: {spent:.1f} s; {per_layer:.2f} s per layer scaled by "
-                       f"{wl.layers} layers x {wl.batch} sequence(s) to one step")}
+                       f"{wl.layers} layers x {wl.batch} sequence(s) to one step"),
+            "absorbed_reference": {"value": wl.batch * Sq / abs_step_s, "unit": "tokens/s",
+                                   "s_per_layer": spent_abs / layers,
+                                   "sample": "the absorbed fp64 CPU reference on the same layers and inputs"}}
 
 
 def traffic_from_counters(workload_name: str):
@@ -342,7 +437,7 @@ def main():
             r = run_workload(3, max(3, min(args.steps, 10)), 2, not args.no_graph, kv_chunk=chunk, label=f"256k-{name}")
             log(f"[256k {name}] {json.dumps(r)}")
             extra[name] = {k: r[k] for k in ("tokens_per_s", "ms_per_step", "step_latent_gbps", "kernel_avg_us",
-                                            "kernel_latent_gbps", "kv_chunk")}
+                                            "kernel_latent_gbps", "kernel_tflops", "kv_chunk")}
             extra[name]["kernel_hbm_frac"] = r["kernel_latent_gbps"] / HBM_PEAK_GBPS
     fp8 = None
     if not args.no_fp8:
@@ -354,7 +449,7 @@ def main():
                              cache_dtype="fp8")
             log(f"[fp8 {name}] {json.dumps(r)}")
             fp8[name] = {key: r[key] for key in ("workload", "tokens_per_s", "ms_per_step", "step_latent_gbps",
-                                               "kernel_avg_us", "kernel_latent_gbps", "kv_chunk")}
+                                               "kernel_avg_us", "kernel_latent_gbps", "kernel_tflops", "kv_chunk")}
             fp8[name]["kernel_hbm_frac"] = r["kernel_latent_gbps"] / HBM_PEAK_GBPS
     more = None
     if not args.no_more:
@@ -366,8 +461,9 @@ def main():
             log(f"[config{k}] {json.dumps(r)}")
             more[r["workload"]] = {key: r[key] for key in ("batch", "query_tokens", "layout", "tokens_per_s",
                                                          "ms_per_step", "step_latent_gbps", "kernel_avg_us",
-                                                         "kernel_latent_gbps", "kv_chunk")}
+                                                         "kernel_latent_gbps", "kernel_tflops", "kv_chunk")}
             more[r["workload"]]["kernel_hbm_frac"] = r["kernel_latent_gbps"] / HBM_PEAK_GBPS
+            more[r["workload"]]["kernel_mfma_frac"] = r["kernel_tflops"] / MFMA_PEAK_TFLOPS
     prefill = None
     if not args.no_more:
         prefill = {}
@@ -375,6 +471,18 @@ def main():
             r = run_prefill(L, Tq, 5, 2)
             log(f"[prefill {Tq}/{L}] {json.dumps(r)}")
             prefill[r["workload"]] = r
+    latency = None
+    if not args.no_more:
+        latency = {}
+        for name, chunk in (("kv_chunk_auto", 0), ("one_split", 1024)):
+            r = run_latency(0, chunk)
+            log(f"[config0 {name}] {json.dumps(r)}")
+            latency[name] = r
+    ceiling = None
+    if not args.no_more:
+        ceiling = read_ceiling()
+        ceiling["splitkv_frac_of_ceiling"] = main_res["kernel_latent_gbps"] / ceiling["gbps"]
+        log(f"[read ceiling] {json.dumps(ceiling)}")
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.config)
 
     bpl = main_res["kernel_bytes_per_launch"]
@@ -401,6 +509,9 @@ def main():
             "kernel": "splitkv_decode", "bytes_per_launch": bpl, "avg_launch_us": main_res["kernel_avg_us"],
         },
         "cpu_baseline": cpu,
+        "kernel_tflops": main_res["kernel_tflops"],
+        "read_ceiling": ceiling,
+        "ctx1k_one_layer": latency,
         "ctx256k": extra,
         "fp8_cache": fp8,
         "other_workloads": more,

@@ -274,6 +274,19 @@ mla_status mla_timing_enable(int32_t max_calls);
 mla_status mla_timing_collect(double* total_ms /* host */, int32_t* launches /* host */);
 mla_status mla_timing_disable(void);
 
+/* Streaming-read ceiling, a measurement aid (not needed to compute anything):
+ * one launch reads all `bytes` of device buffer `buf` once (2048 workgroups,
+ * each a contiguous share, streamed with 16-byte direct global->LDS loads as
+ * the decode kernels stream the cache) and stores one XOR digest per wave to
+ * `sink`, device int32 [MLA_READ_PROBE_SINK_INTS]; the XOR of the digests is
+ * the XOR of the buffer's 32-bit words.  Timed by the caller (events on `stream`),
+ * it gives the HBM read rate a plain streaming kernel reaches on this device,
+ * against which the decode kernels' rates can be read.  `buf` 16-byte
+ * aligned, bytes a non-zero multiple of 16 (MLA_ERR_ALIGN / MLA_ERR_RANGE
+ * otherwise); the caller owns both buffers. */
+#define MLA_READ_PROBE_SINK_INTS 8192
+mla_status mla_read_probe(const void* buf, size_t bytes, int32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

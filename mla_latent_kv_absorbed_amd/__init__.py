@@ -21,7 +21,7 @@ __all__ = [
     "mla_rope_yarn", "mla_cache_append", "mla_decode", "mla_decode_paged", "mla_decode_step",
     "mla_decode_workspace_size", "mla_decode_auto_chunk", "mla_status_string",
     "mla_prefill", "mla_prefill_workspace_size",
-    "mla_timing_enable", "mla_timing_collect", "mla_timing_disable",
+    "mla_timing_enable", "mla_timing_collect", "mla_timing_disable", "mla_read_probe", "READ_PROBE_SINK_INTS",
 ]
 
 
@@ -83,6 +83,7 @@ def library() -> ctypes.CDLL:
             "mla_timing_enable": [_I32],
             "mla_timing_collect": [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I32)],
             "mla_timing_disable": [],
+            "mla_read_probe": [_P, ctypes.c_size_t, _P, _P],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
@@ -373,3 +374,18 @@ def mla_timing_collect():
 
 def mla_timing_disable():
     _check(library().mla_timing_disable(), "mla_timing_disable")
+
+
+READ_PROBE_SINK_INTS = 8192   # MLA_READ_PROBE_SINK_INTS
+
+
+def mla_read_probe(buf: torch.Tensor, sink: torch.Tensor, stream=None):
+    """One streaming read of all of `buf` (a contiguous device tensor, a multiple of 16 bytes);
+    `sink` is a device int32 tensor of READ_PROBE_SINK_INTS elements that receives the digests."""
+    if not (buf.is_cuda and buf.is_contiguous()):
+        raise MlaError("buf: contiguous device tensor required")
+    _need(sink, torch.int32, "sink")
+    if sink.numel() < READ_PROBE_SINK_INTS:
+        raise MlaError(f"sink: {READ_PROBE_SINK_INTS} int32 elements required")
+    _check(library().mla_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)),
+           "mla_read_probe")

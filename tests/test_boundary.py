@@ -145,10 +145,24 @@ def test_prefill_argument_errors_and_workspace():
     assert _prefill(lib, s, wsb=1000) == ERR_WORKSPACE
     f8 = M.default_shape(M.CACHE_FP8_E4M3)
     assert _prefill(lib, f8) == 7                                 # MLA_ERR_UNSUPPORTED
-    # expanded rows [8192 | 64 rope] bf16 per token, context rounded up to 128
+    # expanded rows [8192 | 64 rope] bf16 per token, context rounded up to 256
     assert M.mla_prefill_workspace_size(1024) == 1024 * 8256 * 2
     assert M.mla_prefill_workspace_size(1000) == 1024 * 8256 * 2
     assert M.mla_prefill_workspace_size(129) == 256 * 8256 * 2
     assert M.mla_prefill_workspace_size(300) == 512 * 8256 * 2
     with pytest.raises(M.MlaError):
         M.mla_prefill_workspace_size(0)
+
+
+def test_read_probe_argument_errors():
+    lib = M.library()
+    assert lib.mla_read_probe(None, 1024, FAKE, None) == ERR_NULL
+    assert lib.mla_read_probe(FAKE, 1024, None, None) == ERR_NULL
+    assert lib.mla_read_probe(FAKE, 0, FAKE, None) == ERR_RANGE
+    assert lib.mla_read_probe(FAKE, 1000, FAKE, None) == ERR_RANGE      # not a multiple of 16
+    assert lib.mla_read_probe(FAKE + 8, 1024, FAKE, None) == ERR_ALIGN
+
+
+def test_read_probe_sink_size_matches_the_header():
+    m = re.search(r"#define MLA_READ_PROBE_SINK_INTS (\d+)", open(HEADER).read())
+    assert m and int(m.group(1)) == M.READ_PROBE_SINK_INTS

@@ -293,3 +293,18 @@ def test_balanced_schedule_over_many_short_sequences():
     for b in range(0, len(lens), 10):
         ref_o, ref_l = expected(wl.seed, 0, lens[b], 1, b)
         compare(go[b], gl[b], ref_o, ref_l)
+
+
+# ---------------------------------------------------------------------------
+# streaming-read probe (a measurement aid): every word is read exactly once
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("nbytes", [16, 4096 + 48, 3 << 20])
+def test_read_probe_digests_xor_to_the_buffer_xor(nbytes):
+    g = torch.Generator().manual_seed(nbytes)
+    host = torch.randint(-2 ** 31, 2 ** 31 - 1, (nbytes // 4,), dtype=torch.int32, generator=g)
+    buf = host.to(DEV)
+    sink = torch.full((M.READ_PROBE_SINK_INTS,), -1, dtype=torch.int32, device=DEV)
+    M.mla_read_probe(buf, sink)
+    torch.cuda.synchronize()
+    assert np.bitwise_xor.reduce(sink.cpu().numpy()) == np.bitwise_xor.reduce(host.numpy())
