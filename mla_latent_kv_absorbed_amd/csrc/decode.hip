@@ -133,7 +133,8 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode(DecodeParams p) {
   static_assert(ROWS * kRowBytes <= kSlotLds, "query rows fit in a ring position");
 
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kSlots * kSlotLds];
-  // P in bf16, [row group][32-token step][row][32 tokens in MFMA k order]
+  // P in bf16, [row group][32-token step][row][32 tokens in MFMA k order];
+  // 16-byte granule q of row r is stored at granule q ^ ((r % 16) >> 2)
   __shared__ __attribute__((aligned(16))) uint8_t pbuf[RG * 2 * 16 * 64];
   __shared__ float stat[3][TPW][ROWS];   // per score wave and row: slot max, sum, true max
   __shared__ int flags[kWaves];
@@ -247,8 +248,9 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode(DecodeParams p) {
   // This wave's blocks: cb = 4*wave + c.
   const int pv_lane = (4 * g + (n16 >> 2)) * kRowLds + (n16 & 1) * 8 + ((n16 >> 1) & 1) * 16 +
                       kCbPerWave * wave * 32;
-  // P reads: row n16 of a row group, one 32-token step: 16 bytes at k = 8g.
-  const int pb_rd = n16 * 64 + g * 16;
+  // P reads: row n16 of a row group, one 32-token step: 16 bytes at k = 8g
+  // (granule g, swizzled).
+  const int pb_rd = n16 * 64 + ((g ^ (n16 >> 2)) * 16);
 
   f32x4 o[kCbPerWave][RG];
 #pragma unroll
@@ -330,7 +332,7 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode(DecodeParams p) {
       }
       const int t16 = tok0 + blk * 16;   // first token of the block (a multiple of 16)
       const int ks = t16 >> 5, bb = (t16 >> 4) & 1;
-      *(s16x4*)(pbuf + ((rg * 2 + ks) * 16 + n16) * 64 + (8 * g + 4 * bb) * 2) = pk;
+      *(s16x4*)(pbuf + ((rg * 2 + ks) * 16 + n16) * 64 + ((g ^ (n16 >> 2)) * 16) + bb * 8) = pk;
     }
     lds_barrier();
 
