@@ -268,6 +268,53 @@ def run_prefill(L: int, Tq: int, steps: int, warmup: int, seed: int = 8):
                 flops_per_call=flops_attn + flops_expand)
 
 
+def library_reference(reps: int = 10):
+    """Library rates on the prefill shapes, for context: torch.matmul (hipBLASLt) on the
+    expansion GEMM [L x 512] x [512 x 8192] for L = 32768 and 131072, and torch's fused
+    attention (flash and memory-efficient backends only; they need equal head dims, so V is
+    padded to 192) on 4096 queries over 32768 keys without a mask."""
+    import torch
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+
+    def timed(f, n):
+        for _ in range(3):
+            f()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            f()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    g = torch.Generator(device="cuda").manual_seed(0)
+    res = {}
+    for L in (32768, 131072):
+        c = torch.randn(L, 512, device="cuda", dtype=torch.bfloat16, generator=g)
+        wt = torch.randn(512, 8192, device="cuda", dtype=torch.bfloat16, generator=g)
+        out = torch.empty(L, 8192, device="cuda", dtype=torch.bfloat16)
+        ms = timed(lambda: torch.matmul(c, wt, out=out), reps)
+        res[f"matmul_{L}x512x8192"] = dict(us=ms * 1e3, tflops_per_s=2 * L * 512 * 8192 / (ms * 1e-3) / 1e12)
+        del c, wt, out
+    q = torch.randn(1, 32, 4096, 192, device="cuda", dtype=torch.bfloat16, generator=g)
+    k = torch.randn(1, 32, 32768, 192, device="cuda", dtype=torch.bfloat16, generator=g)
+    v = torch.randn(1, 32, 32768, 192, device="cuda", dtype=torch.bfloat16, generator=g)
+    for be in (SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION):
+        try:
+            with sdpa_kernel([be]):
+                ms = timed(lambda: torch.nn.functional.scaled_dot_product_attention(q, k, v), max(2, reps // 2))
+            # useful flops: scores over 192 dims, values over the model's 128
+            res[f"sdpa_{be.name.lower()}_q4096_k32768"] = dict(
+                us=ms * 1e3, tflops_per_s=2 * 4096 * 32768 * 32 * (192 + 128) / (ms * 1e-3) / 1e12,
+                note="V padded to 192; rate counts the 192 + 128 useful dims")
+        except RuntimeError as e:
+            res[f"sdpa_{be.name.lower()}_q4096_k32768"] = dict(unavailable=str(e)[:160])
+    del q, k, v
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(k: int, budget_s: float = 15.0):
     """The un-absorbed fp64 oracle on the host cores, on a bounded sample of workload k.
 
@@ -398,6 +445,8 @@ def main():
     ap.add_argument("--no-fp8", action="store_true", help="skip the 8-bit cache report")
     ap.add_argument("--no-more", action="store_true",
                     help="skip the report on the other workloads (batched paged, speculative verify, 512K)")
+    ap.add_argument("--library-reference", action="store_true",
+                    help="run only the library rates on the prefill shapes (hipBLASLt GEMM, torch fused attention) and print them")
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only the chunked-prefill report (4096 new tokens on 32K and 128K contexts) and print it")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -418,6 +467,9 @@ def main():
 
     import torch
     torch.cuda.init()
+    if args.library_reference:
+        print(json.dumps({"library_reference": library_reference()}), flush=True)
+        return
     if args.prefill_only:
         res = {}
         for L, Tq in ((32768, 4096), (131072, 4096)):
