@@ -60,7 +60,8 @@ int compute_units() {
 // Upper bound of the number of segments (splits) of a call: with a fixed
 // kv_chunk every sequence has at most ceil(max_ctx_len / kv_chunk); the
 // balanced schedule (kv_chunk = 0) chooses c >= ceil(T / target) tiles, so
-// sum_b ceil(tiles_b / c) <= T / c + B <= target + B.
+// sum_b ceil(tiles_b / c) <= T / c + B <= target + B, or else c = the longest
+// sequence's tiles, which makes every sequence one split (B segments).
 int64_t max_segments(int B, int max_ctx, int kv_chunk, int target) {
   if (kv_chunk > 0) return (int64_t)B * ((max_ctx + kv_chunk - 1) / kv_chunk);
   return (int64_t)target + B;
@@ -71,11 +72,13 @@ int64_t max_segments(int B, int max_ctx, int kv_chunk, int target) {
 int balanced_chunk(int B, int max_ctx, int target) {
   const int64_t tiles = (max_ctx + kPage - 1) / kPage;
   const int64_t T = tiles * B;
-  int64_t c = std::max<int64_t>(kMinTilesPerSplit, (T + target - 1) / target);
+  // never more than one sequence's tiles: from there on each sequence is one split
+  const int64_t cmax = std::max<int64_t>(kMinTilesPerSplit, tiles);
+  int64_t c = std::min(cmax, std::max<int64_t>(kMinTilesPerSplit, (T + target - 1) / target));
   for (int it = 0; it < 8; ++it) {
     const int64_t n = B * ((tiles + c - 1) / c);
-    if (n <= target) break;
-    c = std::max<int64_t>(c + 1, (c * n + target - 1) / target);
+    if (n <= target || c >= cmax) break;
+    c = std::min(cmax, std::max<int64_t>(c + 1, (c * n + target - 1) / target));
   }
   return (int)(c * kPage);
 }

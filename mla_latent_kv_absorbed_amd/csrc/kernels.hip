@@ -59,6 +59,17 @@ __device__ __forceinline__ int block_sum256(int v, int* red4) {
   return r;
 }
 
+__device__ __forceinline__ int block_max256(int v, int* red4) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v = max(v, __shfl_xor(v, d, 64));
+  if (lane == 0) red4[wv] = v;
+  __syncthreads();
+  const int r = max(max(red4[0], red4[1]), max(red4[2], red4[3]));
+  __syncthreads();
+  return r;
+}
+
 // Inclusive prefix sum over a 256-thread workgroup; *total gets the sum.
 __device__ __forceinline__ int block_scan256(int v, int* red4, int* total) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -98,16 +109,24 @@ __device__ void build_schedule(const PrepParams& p, int* lds) {
   }
   int c = p.fixed_tiles;
   if (c <= 0) {
-    int tsum = 0;
-    for (int b = t; b < p.B; b += 256) tsum += (len_of(b) + kPage - 1) / kPage;
+    int tsum = 0, tmax = 1;
+    for (int b = t; b < p.B; b += 256) {
+      const int tb = (len_of(b) + kPage - 1) / kPage;
+      tsum += tb;
+      tmax = max(tmax, tb);
+    }
     const int T = block_sum256(tsum, red4);
-    c = max(kMinTilesPerSplit, (T + p.target_segs - 1) / p.target_segs);
+    tmax = max(kMinTilesPerSplit, block_max256(tmax, red4));
+    // c never exceeds the longest sequence's tiles: from there on every
+    // sequence is a single split, and more sequences than the target cannot
+    // be helped by longer splits
+    c = min(tmax, max(kMinTilesPerSplit, (T + p.target_segs - 1) / p.target_segs));
     for (int it = 0; it < 8; ++it) {   // the last split of each sequence is short: grow c until it fits
       int n = 0;
       for (int b = t; b < p.B; b += 256) n += ((len_of(b) + kPage - 1) / kPage + c - 1) / c;
       n = block_sum256(n, red4);
-      if (n <= p.target_segs) break;
-      c = max(c + 1, (int)(((long long)c * n + p.target_segs - 1) / p.target_segs));
+      if (n <= p.target_segs || c >= tmax) break;
+      c = min(tmax, max(c + 1, (int)(((long long)c * n + p.target_segs - 1) / p.target_segs)));
     }
   }
   const int chunk = c * kPage;

@@ -121,6 +121,12 @@ def test_workspace_size_and_auto_chunk():
         assert fixed >= B * Sq * 32 * (576 * 2 + 512 * 4) + B * -(-L // 128) * Sq * 32 * (512 * 2 + 4)
     with pytest.raises(M.MlaError):
         M.mla_decode_workspace_size(1, 1, 100, kv_chunk=65)
+    # more sequences than compute units: every sequence is one split, so the
+    # split never grows past the longest sequence (it used to grow without bound)
+    assert M.mla_decode_auto_chunk(65535, 1, 100) == 128
+    assert M.mla_decode_auto_chunk(4095, 16, 200) == 256
+    assert M.mla_decode_auto_chunk(65535, 1, 1 << 20) == 1 << 20
+    assert M.mla_decode_auto_chunk(300, 1, 64) == 128
     # an empty batch needs no workspace and must not trip the split heuristic
     assert M.mla_decode_workspace_size(0, 1, 1024) == 0
     assert M.mla_decode_auto_chunk(0, 1, 1024) % 64 == 0

@@ -295,6 +295,31 @@ def test_balanced_schedule_over_many_short_sequences():
         compare(go[b], gl[b], ref_o, ref_l)
 
 
+def test_widest_batch_takes_the_schedules_serial_path():
+    # B * Sq = 4095 * 16 = 65,520 rows (the combine's grid allows 65,535) and
+    # B > 2,048 sequences, so the device schedule takes its serial path;
+    # short ragged contexts, the balanced and a fixed split; a sample of
+    # sequences (both sides of 2,048 among them) against the oracle.
+    rng = np.random.default_rng(11)
+    lens = tuple(int(x) for x in rng.integers(16, 200, 4095))
+    wl = Workload(98, "widest", len(lens), 16, 1, lens, True)
+    dw = DeviceWorkload(wl, paged=True, kv_chunk=0)
+    li = dw.build_layer(0)
+    print(f"built {len(lens)} sequences", flush=True)
+    picks = sorted({0, 1, 2047, 2048, 2049, 4094} | {int(x) for x in rng.integers(0, 4095, 6)})
+    idx = torch.tensor(picks, device=DEV)
+    for chunk, run in ((0, dw.step), (64, dw.step_unfused)):
+        lse = torch.empty((len(lens), 16, 32), dtype=torch.float32, device=DEV)
+        out, lse = run(li, lse=lse, kv_chunk=chunk)
+        torch.cuda.synchronize()
+        go, gl = gpu_out(out[idx]), lse[idx].cpu().numpy()
+        for i, b in enumerate(picks):
+            ref_o, ref_l = expected(wl.seed, 0, lens[b], 16, b)
+            compare(go[i], gl[i], ref_o, ref_l)
+        print(f"chunk {chunk}: {len(picks)} sequences match", flush=True)
+        del out, lse
+
+
 # ---------------------------------------------------------------------------
 # streaming-read probe (a measurement aid): every word is read exactly once
 # ---------------------------------------------------------------------------
