@@ -49,7 +49,7 @@ typedef int32_t mla_status;
 #define MLA_ERR_ALIGN        4   /* a pointer or leading dimension is misaligned     */
 #define MLA_ERR_WORKSPACE    5   /* workspace too small                              */
 #define MLA_ERR_DEVICE       6   /* a HIP runtime call failed                        */
-#define MLA_ERR_UNSUPPORTED  7   /* a valid request this build does not implement    */
+#define MLA_ERR_UNSUPPORTED  7   /* a valid request this library does not implement  */
 
 /* Cache row formats (mla_shape.kv_cache_dtype).
  *  MLA_CACHE_BF16      576 bf16 = 1152 bytes: [latent (512) | rope key (64)]

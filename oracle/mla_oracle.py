@@ -20,7 +20,7 @@ attention time kv_b_proj expands full per-head keys and values from the latent
 and ordinary softmax attention follows.  Every floating-point step runs in
 fp64 on the bf16 input values (which fp64 holds exactly).
 
-Readings of points the pages leave open (each also listed in the design doc):
+Readings of points the pages leave open:
 
 * kv_b_proj output rows of head h are [k_nope (128) | v (128)], heads in order
   (the declared out width num_heads * (qk_nope_head_dim + v_head_dim)).

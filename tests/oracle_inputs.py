@@ -42,16 +42,20 @@ def expected(seed, layer, length, sq, b, heads=None, absorbed=False):
     return fn(qn, qp, c, k, weights(seed, layer), O.softmax_scale(), heads)
 
 
-# Tolerances: outputs as stated for the path (bf16 outputs, fp32 accumulation);
-# LSE bound derived from bf16 rounding of the absorbed query.
+# Tolerances: outputs as stated for the path (bf16 outputs, fp32 accumulation).
+# LSE: rounding the absorbed query q_lat (std ~0.5) to bf16 moves a score by
+# rms ~0.145 * 0.5 * 1.1e-3 * sqrt(512) ~ 1.8e-3; the library corrects the LSE to
+# first order with the fp32 residual, leaving second-order terms (< 1e-5) and
+# fp32 rounding, so 5e-3 bounds the LSE with a wide margin.
 OUT_MAX_ABS = 2e-2
 OUT_REL_L2 = 5e-3
 LSE_MAX_ABS = 5e-3
 
 
 # Chunked prefill (un-absorbed form): the expanded keys and values are rounded
-# to bf16 before the attention, errors the decode path does not have (the design doc
-# derives both bounds): a score moves by up to ~5.5e-3 for one visible token
+# to bf16 before the attention, errors the decode path does not have: a score
+# (0.145 * q_nope . dK over 128 dims, dK of rms 2^-9 / sqrt(3) relative) moves by
+# up to ~5.5e-3 for one visible token
 # (rms 1.8e-3), an output by half a bf16 ulp of V plus half an ulp of the
 # output (< 3.2e-2 for |V|, |out| < 8).  rel-L2 keeps the path's 5e-3.
 PREFILL_LSE_MAX_ABS = 1e-2
