@@ -17,7 +17,7 @@ from synth.configs import Workload, workload
 import mla_latent_kv_absorbed_amd as M
 from mla_latent_kv_absorbed_amd.workload import DeviceWorkload
 
-from oracle_inputs import compare, expected
+from oracle_inputs import compare, expected, expected_fp8
 
 pytestmark = pytest.mark.gpu
 
@@ -318,6 +318,42 @@ def test_widest_batch_takes_the_schedules_serial_path():
             compare(go[i], gl[i], ref_o, ref_l)
         print(f"chunk {chunk}: {len(picks)} sequences match", flush=True)
         del out, lse
+
+
+@pytest.mark.parametrize("chunk", [0, 128])
+def test_host_length_bound_above_the_lengths_changes_nothing(chunk):
+    # max_ctx_len only sizes the workspace and the grid: a bound 8x the longest
+    # context, with the cache rows at 8x the stride, gives bitwise the same
+    # result (the schedule follows the actual lengths on the device)
+    wl = Workload(99, "bound", 3, 2, 1, (700, 130, 1500), False)
+    dw = DeviceWorkload(wl, paged=False, kv_chunk=chunk)
+    li = dw.build_layer(0)
+    ref, ref_lse = dw.step_unfused(li, lse=torch.empty((3, 2, 32), dtype=torch.float32, device=DEV))
+    torch.cuda.synchronize()
+    wide = torch.zeros((3, 8 * dw.stride, 576), dtype=torch.bfloat16, device=DEV)
+    wide[:, :dw.stride] = li.cache
+    out, lse = M.mla_decode(li.q_nope, li.q_pe, li.w_kv_b, wide, dw.ctx_lens, 8 * dw.max_ctx, chunk,
+                            lse=torch.empty((3, 2, 32), dtype=torch.float32, device=DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref) and torch.equal(lse, ref_lse)
+
+
+def test_fp8_batch_above_the_schedules_lds_capacity():
+    # 2,100 sequences (> 2,048: the serial schedule path) over the 8-bit cache
+    rng = np.random.default_rng(12)
+    lens = tuple(int(x) for x in rng.integers(1, 150, 2100))
+    wl = Workload(96, "wide8", len(lens), 1, 1, lens, True)
+    dw = DeviceWorkload(wl, paged=True, kv_chunk=0, cache_dtype="fp8")
+    li = dw.build_layer(0)
+    lse = torch.empty((len(lens), 1, 32), dtype=torch.float32, device=DEV)
+    out, lse = dw.step(li, lse=lse)
+    torch.cuda.synchronize()
+    picks = [0, 2047, 2048, 2099] + [int(x) for x in rng.integers(0, 2100, 4)]
+    idx = torch.tensor(picks, device=DEV)
+    go, gl = gpu_out(out[idx]), lse[idx].cpu().numpy()
+    for i, b in enumerate(picks):
+        ref_o, ref_l = expected_fp8(wl.seed, 0, lens[b], 1, b)
+        compare(go[i], gl[i], ref_o, ref_l)
 
 
 # ---------------------------------------------------------------------------
