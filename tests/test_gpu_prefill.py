@@ -69,3 +69,9 @@ def test_prefill_fullsize_chunk4k_ctx32k_sampled_rows():
 def test_prefill_long_chunk_from_scratch_sampled_rows():
     # a long chunk from an empty context: ragged last tiles, first rows seeing few tokens
     check_sampled_rows(83, 2100, 2100, (0, 1, 2, 63, 64, 255, 256, 1000, 2047, 2048, 2099))
+
+
+def test_prefill_longest_context_sampled_rows():
+    # the largest context the call accepts (2^20 tokens) with a 64-token chunk
+    print("prefill 64 / 2^20: building", flush=True)
+    check_sampled_rows(84, 1 << 20, 64, (0, 63))
