@@ -51,6 +51,7 @@ constexpr int kCbPerWave = kLatent / 16 / kWaves;          // 4 column blocks of
 
 typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2_t;
 typedef __attribute__((address_space(3))) const i32x4 lds_i32x4_t;
@@ -126,10 +127,10 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode_fp8(DecodeParams p
   static_assert(ROWS * kRowBytes <= (kSlots - 1) * kSlotLds, "query rows fit in ring positions 1..2");
 
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kSlots * kSlotLds];
-  // p in fp32, [row group][32-token step][row][32 tokens in MFMA k order];
-  // 16-byte granule q of row r is stored at granule q ^ ((r % 16) >> 1), so the
-  // 16 lanes of a row block touch 16 different bank groups
-  __shared__ __attribute__((aligned(16))) uint8_t pbuf[RG * 2 * 16 * 128];
+  // P'_G = bf16(p * scale_G) for the four latent groups G, [G][row group]
+  // [32-token step][row][32 tokens in MFMA k order]; 16-byte granule q of row
+  // r is stored at granule q ^ ((r % 16) >> 2)
+  __shared__ __attribute__((aligned(16))) uint8_t pbuf[4 * RG * 2 * 16 * 64];
   __shared__ float stat[3][TPW][ROWS];   // per score wave and row: slot max, sum, true max
   __shared__ int flags[kWaves];
 
@@ -239,13 +240,8 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode_fp8(DecodeParams p
   const int vtok = (r8 < 4) ? 4 * g + r8 : 12 + 4 * g + r8;
   const int v_off = vtok * kF8Row + (lane & 1) * 8 + kCbPerWave * wave * 16;
   const int pgrp = wave >> 1;
-  // the two 16-byte granules of lane (n16, g) in P row n16, granule ^ (n16 >> 1)
-  const int pb_rd0 = n16 * 128 + ((2 * g) ^ (n16 >> 1)) * 16;
-  const int pb_rd1 = n16 * 128 + ((2 * g + 1) ^ (n16 >> 1)) * 16;
-  // scale of group pgrp of the tokens behind k = 8g + i of a 32-token step
-  int sc_off[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) sc_off[i] = ((i < 4) ? 4 * g + i : 12 + 4 * g + i) * kF8Row + kF8ScaleOff + 4 * pgrp;
+  // lane (n16, g) of a value wave reads granule g of P' row n16 of its group
+  const int pb_rd = pgrp * (RG * 2 * 16 * 64) + n16 * 64 + ((g ^ (n16 >> 2)) * 16);
 
   f32x4 o[kCbPerWave][RG];
 #pragma unroll
@@ -330,8 +326,9 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode_fp8(DecodeParams p
     }
     overflow = overflow || (__builtin_amdgcn_ballot_w64(mt > m_ref + kTau) != 0);
 
-    // ---- p = 2^(s - m_ref) (fp32) into LDS in the value product's B-operand
-    // layout: token t of the slot is step t/32, k = 8*((t%16)/4) + 4*((t/16)%2) + t%4
+    // ---- p = 2^(s - m_ref), and P'_G = bf16(p * scale_G) of every group into
+    // LDS in the value product's B-operand layout: token t of the slot is step
+    // t/32, k = 8*((t%16)/4) + 4*((t/16)%2) + t%4
     const float mref = (m_ref == kNegInf) ? 0.f : m_ref;
 #pragma unroll
     for (int blk = 0; blk < NBLK; ++blk) {
@@ -343,12 +340,22 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode_fp8(DecodeParams p
       }
       const int t16 = tok0 + blk * 16;
       const int ks = t16 >> 5, bb = (t16 >> 4) & 1;
-      *(f32x4*)(pbuf + ((rg * 2 + ks) * 16 + n16) * 128 + ((2 * g + bb) ^ (n16 >> 1)) * 16) = pf;
+      f32x4 sc[4];   // the four group scales of token 4g + i of the block
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[i] = *(lds_f32x4_t*)(T + (t16 + 4 * g + i) * kF8Row + kF8ScaleOff);
+      uint8_t* pw = pbuf + ((rg * 2 + ks) * 16 + n16) * 64 + ((g ^ (n16 >> 2)) * 16) + bb * 8;
+#pragma unroll
+      for (int G = 0; G < 4; ++G) {
+        bf16x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = (__bf16)(pf[i] * sc[i][G]);
+        *(bf16x4*)(pw + G * (RG * 2 * 16 * 64)) = v;
+      }
     }
     lds_barrier();
 
     // ---- O^T += C^T . P'^T over this wave's 4 column blocks and all rows,
-    // P'_g = bf16(p * scale_g) of this wave's group g
+    // with P' of this wave's latent group
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       __builtin_amdgcn_sched_barrier(0);
@@ -356,20 +363,9 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode_fp8(DecodeParams p
 #pragma unroll
       for (int c = 0; c < kCbPerWave; ++c)
         cv[c] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)(T + ks * 32 * kF8Row + v_off + c * 16));
-      float scl[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) scl[i] = *(lds_f32_t*)(T + ks * 32 * kF8Row + sc_off[i]);
       bf16x8 pb[RG];
 #pragma unroll
-      for (int r2 = 0; r2 < RG; ++r2) {
-        const uint8_t* pr = pbuf + (r2 * 2 + ks) * 2048;
-        const f32x4 p0 = *(const f32x4*)(pr + pb_rd0), p1 = *(const f32x4*)(pr + pb_rd1);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pb[r2][i] = (__bf16)(p0[i] * scl[i]);
-          pb[r2][4 + i] = (__bf16)(p1[i] * scl[4 + i]);
-        }
-      }
+      for (int r2 = 0; r2 < RG; ++r2) pb[r2] = *(const bf16x8*)(pbuf + pb_rd + (r2 * 2 + ks) * (16 * 64));
 #pragma unroll
       for (int c = 0; c < kCbPerWave; ++c) {
         const bf16x8 av = e4m3x8_to_bf16(cv[c]);
