@@ -1,0 +1,32 @@
+"""Host behaviour of bench.py that needs no GPU: more than one GPU is refused with a
+message, and the counters summary keeps its calibration arithmetic."""
+import json
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_committed_counters_record_is_consistent():
+    # the record bench.py reads for "traffic": bytes = KiB per dispatch x 1024 x scale, summed
+    with open(os.path.join(ROOT, "profiles", "splitkv_decode_counters.json")) as fh:
+        c = json.load(fh)
+    k = c["kernels"]["splitkv_decode"]
+    f, w = k["fetch"], k["write"]
+    assert abs(f["bytes_scaled"] - f["kib_per_dispatch"] * 1024 * c["FETCH_SIZE_scale"]) < 1e-3 * f["bytes_scaled"]
+    assert abs(w["bytes_scaled"] - w["kib_per_dispatch"] * 1024 * c["WRITE_SIZE_scale"]) < 1e-3 * w["bytes_scaled"]
+    assert abs(k["hbm_bytes_per_launch"] - f["bytes_scaled"] - w["bytes_scaled"]) < 1.0
+    # the calibration copy of copy_bytes reads and writes exactly that many bytes
+    assert abs(c["FETCH_SIZE_copy_kib"] * c["FETCH_SIZE_scale"] * 1024 - c["copy_bytes"]) < 1e-6 * c["copy_bytes"]
+    assert abs(c["WRITE_SIZE_copy_kib"] * c["WRITE_SIZE_scale"] * 1024 - c["copy_bytes"]) < 1e-6 * c["copy_bytes"]
+    # at least the cache itself is read (37,748,736 B at 32K)
+    assert f["bytes_scaled"] >= 37748736
