@@ -64,6 +64,7 @@ RAGGED = [
     (2, (2, 3, 64, 65, 129, 333)),
     (3, (3, 70, 200)),
     (4, (4, 100, 500)),
+    (16, (16, 40, 300)),
 ]
 
 
