@@ -15,8 +15,9 @@ reported alongside under "ctx256k", and the 32K and 256K workloads over the
 8-bit latent cache (E4M3 codes with per-128 fp32 scales, 656 bytes per token
 and layer) under "fp8_cache".  "other_workloads" reports the batched paged
 decode (16 x 65536), speculative verify of 2, 3 and 4 query tokens per
-sequence (batch 32, log-uniform contexts in [4096, 131072], paged) and one
-sequence of 524288 tokens, all with the device-balanced split; "prefill" the
+sequence (batch 32, log-uniform contexts in [4096, 131072], paged), verify
+of 2 tokens over the 8-bit cache, and one sequence of 524288 tokens, all
+with the device-balanced split; "prefill" the
 chunked prefill (un-absorbed form) of 4096 new tokens on 32K and 128K
 contexts, in TFLOP/s against the 2.5 PFLOP/s bf16 matrix peak.
 "ctx1k_one_layer" times one decode call on a 1024-token context (one layer)
@@ -516,6 +517,18 @@ def main():
                                                          "kernel_latent_gbps", "kernel_tflops", "kv_chunk")}
             more[r["workload"]]["kernel_hbm_frac"] = r["kernel_latent_gbps"] / HBM_PEAK_GBPS
             more[r["workload"]]["kernel_mfma_frac"] = r["kernel_tflops"] / MFMA_PEAK_TFLOPS
+        if not args.no_fp8:
+            # speculative verify over the 8-bit cache (656 B per token and layer)
+            r = run_workload(4, max(3, min(args.steps, 10)), 2, not args.no_graph, kv_chunk=0, label="fp8-config4",
+                             cache_dtype="fp8")
+            log(f"[fp8 config4] {json.dumps(r)}")
+            key = r["workload"] + "-fp8"
+            more[key] = {k: r[k] for k in ("batch", "query_tokens", "layout", "tokens_per_s", "ms_per_step",
+                                           "step_latent_gbps", "kernel_avg_us", "kernel_latent_gbps",
+                                           "kernel_tflops", "kv_chunk")}
+            more[key]["cache_dtype"] = "fp8"
+            more[key]["kernel_hbm_frac"] = r["kernel_latent_gbps"] / HBM_PEAK_GBPS
+            more[key]["kernel_mfma_frac"] = r["kernel_tflops"] / MFMA_PEAK_TFLOPS
     prefill = None
     if not args.no_more:
         prefill = {}
