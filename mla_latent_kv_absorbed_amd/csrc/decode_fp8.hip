@@ -11,14 +11,15 @@
 // work is split as in the bf16 kernel (8 waves, two per SIMD; scores by row
 // group and token share, the value product by latent columns, P through LDS):
 //  * scores: the codes of 64 latent columns are read as 16 bytes per lane
-//    (ds_read_b128), two MFMA steps, and widened to bf16 exactly; each 128-column group has its
-//    own score accumulator, and the four are combined with the tokens'
-//    scales (the rope part has its own accumulator, unscaled);
+//    (ds_read_b128), two MFMA steps, and widened to bf16 exactly; each
+//    128-column group has its own score accumulator, and the four are
+//    combined with the tokens' scales (the rope part has its own
+//    accumulator, unscaled);
 //  * values: O^T = C^T P'^T with P'_g = bf16(p * scale_{t,g}) for the
-//    columns of group g: the score waves write p (fp32) to LDS, and each
-//    value wave (its 64 columns lie in one group) forms P'_g from p and the
-//    tokens' scales of its group; the codes are fetched column-wise with the
-//    8-bit transposing read ds_read_b64_tr_b8
+//    columns of group g: the score waves write P'_g of all four groups to
+//    LDS, and each value wave (its 64 columns lie in one group) reads its
+//    group's; the codes are fetched column-wise with the 8-bit transposing
+//    read ds_read_b64_tr_b8
 //    (lanes 2r, 2r+1 of a 16-lane group supply the two halves of row r's 16
 //    bytes; lane i receives byte i of rows 0..7), which gives each lane 8
 //    tokens of one column in the MFMA k order, and widened to bf16 exactly.
