@@ -30,8 +30,12 @@ Readings of points the pages leave open:
   [MLA-arch] names yarn_get_mscale without printing it).
 * rope base 10000 and half-split pairing (i, i + 32): not printed for this
   model; they shape the prepared inputs only.
-* YaRN frequencies: NTK-by-parts (Peng et al., 2023) with a linear ramp over
-  the dimension index between floor(d(beta_fast)) and ceil(d(beta_slow)).
+* YaRN frequencies: NTK-by-parts (Peng et al., 2023) in the form of the
+  authors' public implementation, which the MLA model code that defines
+  yarn_get_mscale follows: a blend weight linear in the PAIR INDEX between
+  floor(d(beta_fast)) = 10 and ceil(d(beta_slow)) = 23.  (The paper's
+  equation writes the ramp as linear in the rotation count r instead; the
+  pages print only the parameters, and the two forms differ inside the ramp.)
 * query j of Sq new tokens sits at position L - Sq + j and sees cache tokens
   0 .. L - Sq + j (its own latent is already cached).
 """
@@ -160,16 +164,6 @@ def float_to_bf16_bits(x: np.ndarray) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # Cache rows and paging
 # ---------------------------------------------------------------------------
-
-def cache_row(c_kv: np.ndarray, k_pe_rotated: np.ndarray) -> np.ndarray:
-    """Per-token cache row [latent (512) | rope key (64)].
-
-    [MLA-arch]: kv_a_proj_with_mqa produces kv_lora_rank + qk_rope_head_dim
-    values per token; only this compressed latent and the rope component are
-    cached, with no per-head keys or values.
-    """
-    return np.concatenate([c_kv, k_pe_rotated], axis=-1)
-
 
 def paged_slot(block_table_row: np.ndarray, t: np.ndarray, page_size: int = PAGE_SIZE) -> np.ndarray:
     """Physical slot of logical token t: page block_table[t // P] * P + t % P."""
@@ -370,17 +364,6 @@ def lse_combine(parts):
     tot = wts.sum()
     o = sum(wt * p[0] for wt, p in zip(wts, parts)) / tot
     return o, big + math.log(tot)
-
-
-def mla_decode_batch(q_nope, q_pe, c_kv_list, k_pe_list, w_kv_b, scale, heads=None, absorbed=False):
-    """Loop the single-sequence oracle over a batch (lists of per-sequence caches)."""
-    fn = mla_attention_absorbed if absorbed else mla_attention_unabsorbed
-    outs, lses = [], []
-    for b in range(len(c_kv_list)):
-        o, l = fn(q_nope[b], q_pe[b], c_kv_list[b], k_pe_list[b], w_kv_b, scale, heads)
-        outs.append(o)
-        lses.append(l)
-    return np.stack(outs), np.stack(lses)
 
 
 # ---------------------------------------------------------------------------

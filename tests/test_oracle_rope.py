@@ -4,7 +4,9 @@ Each check compares with something other than the oracle's own formula: the
 textbook RoPE frequencies, YaRN's wavelength thresholds, complex-number
 rotation, group properties of rotations, or torch's own bf16 conversion.
 """
+import json
 import math
+import os
 
 import numpy as np
 import pytest
@@ -49,6 +51,41 @@ def test_yarn_frequency_regions_follow_the_wavelength_thresholds():
     assert np.all(f[mid] < base[mid]) and np.all(f[mid] > base[mid] / 64)
     assert np.all(np.diff(f) < 0)
     assert O.yarn_correction_range() == (10, 23)
+
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "yarn_ramp_page1.json")
+
+
+def _interp_weight(f):
+    """Weight w_i of the interpolated frequency in f_i = base_i (1 - w_i) + base_i / 64 w_i."""
+    base = np.array([10000.0 ** (-2.0 * i / 64) for i in range(32)])
+    return (base - f) / (base - base / 64)
+
+
+def test_yarn_ramp_interior_is_linear_in_the_pair_index():
+    # Fixture: the interpolation weights of the index-linear reading at ramp
+    # pairs, as exact fractions (i - 10) / 13; the ramp ends 10 and 23 follow
+    # from the printed beta_fast / beta_slow (see the region test above).
+    with open(GOLDEN) as fh:
+        g = json.load(fh)
+    w = _interp_weight(O.yarn_inv_freq())
+    for pair, (num, den) in g["interpolated_weight"].items():
+        assert w[int(pair)] == pytest.approx(num / den, abs=1e-12), pair
+
+
+def test_a_ramp_over_the_rotation_count_fails_the_ramp_pin():
+    # The same blend with the weight written over the rotation count r (the
+    # paper's gamma(r)) agrees at the region ends and disagrees inside: the pin
+    # above tells the two forms apart.
+    with open(GOLDEN) as fh:
+        g = json.load(fh)
+    base = np.array([10000.0 ** (-2.0 * i / 64) for i in range(32)])
+    r = 4096 * base / (2 * math.pi)
+    gamma = np.clip((r - 1.0) / (32.0 - 1.0), 0.0, 1.0)
+    f_r = base * gamma + base / 64 * (1.0 - gamma)
+    w_r = _interp_weight(f_r)
+    wrong = [p for p, (num, den) in g["interpolated_weight"].items() if abs(w_r[int(p)] - num / den) > 1e-3]
+    assert {"13", "16", "20"} <= set(wrong)
 
 
 def _rot_complex(x, pos, inv_freq):
