@@ -19,15 +19,24 @@
  *  - Every pointer argument is a DEVICE pointer unless marked "host".
  *  - bf16 is bfloat16 (1-8-7), passed as raw 16-bit values.
  *  - The caller owns every buffer.  The library allocates nothing, keeps no
- *    pointer after a call returns and holds no state between calls (the
- *    opt-in kernel timing at the end of this header aside).
+ *    pointer after a call returns and holds no state between calls, except
+ *    a static fault word per device (below) and the opt-in kernel timing at
+ *    the end of this header.
  *  - All work is enqueued on `stream` (a hipStream_t; NULL = the default
  *    stream).  MLA_OK means "enqueued"; device faults show up at the
  *    caller's next synchronisation.  No call synchronises the host.
  *  - Arguments are validated on the host before anything is enqueued; a bad
  *    argument returns an error code and enqueues nothing.  Contents of device
  *    arrays (block tables, context lengths, slot mappings) are not read by
- *    the host, so out-of-range values there are the caller's responsibility.
+ *    the host; the kernels check them instead: a slot at or beyond num_slots
+ *    is skipped, a block-table page outside [0, num_pages) is read as zero
+ *    rows (and not written by the fused step), a context length outside
+ *    [Sq, max_ctx_len] is clamped into it, so every access stays inside the
+ *    caller's buffers.  Each such event sets a bit of the device's sticky
+ *    fault word (MLA_FAULT_*), which mla_device_faults() reads after the work
+ *    has finished; mla_check_decode_inputs() and mla_check_slot_mapping()
+ *    apply the same rules to host copies of those arrays (a debug check
+ *    before enqueueing).
  *  - The library is reentrant; concurrent calls on different streams must
  *    use different workspaces.
  */
@@ -50,6 +59,14 @@ typedef int32_t mla_status;
 #define MLA_ERR_WORKSPACE    5   /* workspace too small                              */
 #define MLA_ERR_DEVICE       6   /* a HIP runtime call failed                        */
 #define MLA_ERR_UNSUPPORTED  7   /* a valid request this library does not implement  */
+
+/* Bits of the per-device fault word (mla_device_faults). */
+#define MLA_FAULT_SLOT        1u /* a slot >= num_slots: the row was not written          */
+#define MLA_FAULT_PAGE        2u /* a block-table page outside [0, num_pages): its rows
+                                    were read as zeros and not written                   */
+#define MLA_FAULT_CTX_LEN     4u /* a context length outside [Sq, max_ctx_len]: clamped  */
+#define MLA_FAULT_FP16_RANGE  8u /* mla_prefill: a query or an expanded key/value beyond
+                                    the fp16 range (|x| > 65504); results not reliable  */
 
 /* Cache row formats (mla_shape.kv_cache_dtype).
  *  MLA_CACHE_BF16      576 bf16 = 1152 bytes: [latent (512) | rope key (64)]
@@ -131,6 +148,8 @@ mla_status mla_rope_yarn(const mla_rope_params* params /* host */, const void* s
  *                 b * stride + t
  *   c_kv, ld_c    bf16 latent rows [n][ld_c] (ld_c >= 512)
  *   k_pe, ld_k    bf16 rope rows [n][ld_k] (ld_k >= 64), already rotated
+ *   num_slots     rows the cache holds; a slot >= num_slots is skipped and
+ *                 sets MLA_FAULT_SLOT
  *   slot_mapping  int64 [n]; a negative slot skips the row
  * Requires 16-byte aligned cache, c_kv and k_pe and ld_c, ld_k multiples
  * of 8 (MLA_ERR_ALIGN otherwise). */
@@ -151,8 +170,9 @@ mla_status mla_cache_append(const mla_shape* shape /* host */, void* cache, int6
  *   q_pe         bf16 [B][Sq][32][64], already rotated
  *   w_kv_b       bf16 [8192][512] (nn.Linear storage: out x in)
  *   cache        [B][stride_tokens] rows of the shape's format
- *   ctx_lens     int32 [B], Sq <= L_b <= min(max_ctx_len, stride_tokens)
- *   max_ctx_len  host upper bound of ctx_lens
+ *   ctx_lens     int32 [B], Sq <= L_b <= max_ctx_len (a value outside is
+ *                clamped into that range and sets MLA_FAULT_CTX_LEN)
+ *   max_ctx_len  host upper bound of ctx_lens, <= stride_tokens
  *   kv_chunk     tokens per split, a multiple of 64, or 0 to let the
  *                library choose (splits sized from the actual ctx_lens on the
  *                device, about one workgroup per compute unit)
@@ -174,8 +194,10 @@ mla_status mla_decode(const mla_shape* shape /* host */, const void* q_nope, con
 /* Decode attention against a paged cache: as mla_decode, but token t of
  * sequence b lives in slot block_table[b][t / 64] * 64 + t % 64 of
  *   cache        [num_pages][64] rows of the shape's format
- *   block_table  int32 [B][max_pages_per_seq]
- * Every page a sequence uses must be in [0, num_pages). */
+ *   block_table  int32 [B][max_pages_per_seq], max_pages_per_seq >=
+ *                ceil(max_ctx_len / 64)
+ * Every page a sequence uses must be in [0, num_pages); a page outside is
+ * read as 64 zero rows and sets MLA_FAULT_PAGE. */
 mla_status mla_decode_paged(const mla_shape* shape /* host */, const void* q_nope, const void* q_pe,
                             const void* w_kv_b, const void* cache, int64_t num_pages,
                             const int32_t* block_table, int32_t max_pages_per_seq,
@@ -200,7 +222,9 @@ mla_status mla_decode_paged(const mla_shape* shape /* host */, const void* q_nop
  *   k_pe_new      bf16 [B*Sq][ld_k] rope rows, NOT rotated (ld_k >= 64)
  *   cache         written at the new tokens' slots, read by the decode
  * Every other argument as in mla_decode.  c_kv_new and k_pe_new must be
- * 16-byte aligned with ld_c, ld_k multiples of 8. */
+ * 16-byte aligned with ld_c, ld_k multiples of 8.  In the paged form a new
+ * token whose page lies outside [0, num_pages) is not written
+ * (MLA_FAULT_PAGE). */
 mla_status mla_decode_step(const mla_shape* shape /* host */, const mla_rope_params* rope /* host */,
                            const void* q_nope, const void* q_pe, const void* c_kv_new, int64_t ld_c,
                            const void* k_pe_new, int64_t ld_k, const void* w_kv_b, void* cache,
@@ -241,7 +265,7 @@ mla_status mla_prefill_workspace_size(const mla_shape* shape /* host */, int32_t
  * are already written, e.g. by mla_rope_yarn + mla_cache_append) and each sees
  * tokens 0..p.  kv_b_proj expands every cached latent into per-head keys and
  * values ([MLA-arch]: "实时展开"):
- *   K_nope[t][h] = W_UK[h] c_t,  V[t][h] = W_UV[h] c_t   (bf16, fp32 sums)
+ *   K_nope[t][h] = W_UK[h] c_t,  V[t][h] = W_UV[h] c_t   (fp16, fp32 sums)
  *   s_jt = softmax_scale * (q_nope[j][h] . K_nope[t][h] + q_pe[j][h] . k_pe_t)
  *   out[j][h] = sum_t softmax(s)_t V[t][h],  lse[j][h] = ln sum_t exp(s_jt)
  * which for many query tokens costs fewer flops than the absorbed form of
@@ -256,10 +280,34 @@ mla_status mla_prefill_workspace_size(const mla_shape* shape /* host */, int32_t
  *   workspace    device scratch of mla_prefill_workspace_size() bytes,
  *                16-byte aligned
  * Supports 1 <= Tq <= ctx_len <= 2^20 and the bf16 cache format only
- * (MLA_ERR_UNSUPPORTED for the 8-bit format). */
+ * (MLA_ERR_UNSUPPORTED for the 8-bit format).  The expanded keys and values
+ * and q_nope are held in fp16 on the matrix cores: magnitudes up to 65504;
+ * a larger one sets MLA_FAULT_FP16_RANGE. */
 mla_status mla_prefill(const mla_shape* shape /* host */, const void* q_nope, const void* q_pe,
                        const void* w_kv_b, const void* cache, int32_t ctx_len, int32_t Tq, void* out,
                        float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Reads the fault word of the current device (MLA_FAULT_* bits set by any
+ * kernel of this library since the word was last cleared) into *faults
+ * (host), after waiting for all work on the device; clear != 0 then resets
+ * it to zero.  A debugging aid: it synchronises the device, so it must not
+ * be called during graph capture. */
+mla_status mla_device_faults(uint32_t* faults /* host */, int32_t clear);
+
+/* Host-side debug check of decode inputs (host copies of the device
+ * arrays): *faults (host) receives the MLA_FAULT_* bits the kernels would
+ * set: MLA_FAULT_CTX_LEN for a length outside [Sq, max_ctx_len],
+ * MLA_FAULT_PAGE for a page outside [0, num_pages) among the first
+ * ceil(L_b / 64) entries of a row (L_b after clamping).  block_table may be
+ * NULL (contiguous layout). */
+mla_status mla_check_decode_inputs(int32_t B, int32_t Sq, int32_t max_ctx_len, const int32_t* ctx_lens /* host */,
+                                   const int32_t* block_table /* host */, int32_t max_pages_per_seq,
+                                   int64_t num_pages, uint32_t* faults /* host */);
+
+/* Host-side debug check of an append's slot mapping (host copy):
+ * MLA_FAULT_SLOT if any slot is >= num_slots (negative slots are skips). */
+mla_status mla_check_slot_mapping(const int64_t* slot_mapping /* host */, int64_t n, int64_t num_slots,
+                                  uint32_t* faults /* host */);
 
 /* Kernel timing, a profiling aid (not needed to compute anything).
  * After mla_timing_enable(n), each of the next n decode calls has its

@@ -22,6 +22,8 @@ __all__ = [
     "mla_decode_workspace_size", "mla_decode_auto_chunk", "mla_status_string",
     "mla_prefill", "mla_prefill_workspace_size",
     "mla_timing_enable", "mla_timing_collect", "mla_timing_disable", "mla_read_probe", "READ_PROBE_SINK_INTS",
+    "mla_device_faults", "mla_check_decode_inputs",
+    "mla_check_slot_mapping", "FAULT_SLOT", "FAULT_PAGE", "FAULT_CTX_LEN", "FAULT_FP16_RANGE",
 ]
 
 
@@ -37,6 +39,10 @@ class MlaShape(ctypes.Structure):
 
 
 CACHE_BF16 = 0          # rows of 576 bf16: [latent | rope key]
+FAULT_SLOT = 1          # MLA_FAULT_* bits of the device fault word
+FAULT_PAGE = 2
+FAULT_CTX_LEN = 4
+FAULT_FP16_RANGE = 8
 CACHE_FP8_E4M3 = 1      # rows of 656 bytes: [512 E4M3 codes | 4 fp32 scales | 64 bf16 rope key]
 
 
@@ -84,6 +90,9 @@ def library() -> ctypes.CDLL:
             "mla_timing_collect": [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I32)],
             "mla_timing_disable": [],
             "mla_read_probe": [_P, ctypes.c_size_t, _P, _P],
+            "mla_device_faults": [ctypes.POINTER(ctypes.c_uint32), _I32],
+            "mla_check_decode_inputs": [_I32, _I32, _I32, _P, _P, _I32, _I64, ctypes.POINTER(ctypes.c_uint32)],
+            "mla_check_slot_mapping": [_P, _I64, _I64, ctypes.POINTER(ctypes.c_uint32)],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
@@ -118,9 +127,9 @@ def cache_row_width(shape: MlaShape) -> tuple:
     return torch.bfloat16, 576
 
 
-def _check_cache(cache, shape, name="cache"):
+def _check_cache(cache, shape, name="cache", gpu=True):
     dtype, width = cache_row_width(shape)
-    _need(cache, dtype, name)
+    _need(cache, dtype, name, gpu=gpu)
     if cache.shape[-1] != width:
         raise MlaError(f"{name} rows must hold {width} {dtype} values for this cache format")
     return width
@@ -141,15 +150,21 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _need(t, dtype, name, last_contig=True):
+def _need(t, dtype, name, last_contig=True, shape=None, device=None, gpu=True):
+    """Type, contiguity, (optionally) exact shape and device of a tensor argument; ``gpu=False``
+    leaves the GPU check to the caller (which then checks the common device once)."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
-        raise MlaError(f"{name} must be on the GPU (got {t.device})")
     if t.dtype != dtype:
         raise MlaError(f"{name} must be {dtype} (got {t.dtype})")
     if last_contig and not t.is_contiguous():
         raise MlaError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise MlaError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if device is not None and t.device != device:
+        raise MlaError(f"{name} is on {t.device}, the other arguments on {device}")
+    if gpu and t.device.type != "cuda":
+        raise MlaError(f"{name} must be on the GPU (got {t.device})")
 
 
 def _rows2d(x, name):
@@ -188,10 +203,12 @@ def mla_cache_append(cache: torch.Tensor, c_kv: torch.Tensor, k_pe: torch.Tensor
     fp8 rows); slot < 0 skips."""
     s = shape if shape is not None else default_shape()
     width = _check_cache(cache, s)
-    _need(slot_mapping, torch.int64, "slot_mapping")
+    _need(slot_mapping, torch.int64, "slot_mapping", device=cache.device)
     for t, name in ((c_kv, "c_kv"), (k_pe, "k_pe")):
         if t.dtype != torch.bfloat16 or t.device.type != "cuda" or t.dim() != 2 or t.stride(1) != 1:
             raise MlaError(f"{name} must be a 2-D bf16 GPU tensor with unit column stride")
+        if t.device != cache.device:
+            raise MlaError(f"{name} is on {t.device}, the cache on {cache.device}")
     n = c_kv.shape[0]
     if k_pe.shape[0] != n or slot_mapping.numel() != n:
         raise MlaError("c_kv, k_pe and slot_mapping need the same number of rows")
@@ -216,28 +233,29 @@ def mla_decode_auto_chunk(B: int, Sq: int, max_ctx_len: int) -> int:
     return out.value
 
 
-def _decode_io(q_nope, q_pe, w_kv_b, ctx_lens, out, lse, workspace, B, Sq, max_ctx_len, kv_chunk, shape):
-    _need(q_nope, torch.bfloat16, "q_nope")
-    _need(q_pe, torch.bfloat16, "q_pe")
-    _need(w_kv_b, torch.bfloat16, "w_kv_b")
-    _need(ctx_lens, torch.int32, "ctx_lens")
-    if tuple(q_nope.shape) != (B, Sq, 32, 128) or tuple(q_pe.shape) != (B, Sq, 32, 64):
-        raise MlaError("q_nope must be [B, Sq, 32, 128] and q_pe [B, Sq, 32, 64]")
-    if tuple(w_kv_b.shape) != (8192, 512):
-        raise MlaError("w_kv_b must be [8192, 512]")
-    if ctx_lens.numel() != B:
-        raise MlaError("ctx_lens must have B entries")
+def _decode_io(q_nope, q_pe, w_kv_b, ctx_lens, out, lse, workspace, B, Sq, max_ctx_len, kv_chunk, shape,
+               cache=None, block_table=None):
+    _need(q_nope, torch.bfloat16, "q_nope", shape=(B, Sq, 32, 128), gpu=False)
     dev = q_nope.device
+    _need(q_pe, torch.bfloat16, "q_pe", shape=(B, Sq, 32, 64), device=dev, gpu=False)
+    _need(w_kv_b, torch.bfloat16, "w_kv_b", shape=(8192, 512), device=dev, gpu=False)
+    _need(ctx_lens, torch.int32, "ctx_lens", shape=(B,), device=dev, gpu=False)
+    for t, name in ((cache, "cache"), (block_table, "block_table")):
+        if t is not None and t.device != dev:
+            raise MlaError(f"{name} is on {t.device}, q_nope on {dev}")
+    if out is not None:
+        _need(out, torch.bfloat16, "out", shape=(B, Sq, 32, 128), device=dev, gpu=False)
+    if lse is not None:
+        _need(lse, torch.float32, "lse", shape=(B, Sq, 32), device=dev, gpu=False)
+    if dev.type != "cuda":
+        raise MlaError(f"the arguments must be on the GPU (got {dev})")
     if out is None:
         out = torch.empty((B, Sq, 32, 128), dtype=torch.bfloat16, device=dev)
-    _need(out, torch.bfloat16, "out")
-    if lse is not None:
-        _need(lse, torch.float32, "lse")
     s = shape if shape is not None else default_shape()
     need = mla_decode_workspace_size(B, Sq, max_ctx_len, kv_chunk, s)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    _need(workspace, torch.uint8, "workspace")
+    _need(workspace, torch.uint8, "workspace", device=dev)
     return out, lse, workspace, s
 
 
@@ -245,11 +263,11 @@ def mla_decode(q_nope, q_pe, w_kv_b, cache, ctx_lens, max_ctx_len: int, kv_chunk
                out=None, lse=None, workspace=None, shape: MlaShape | None = None, stream=None):
     """Decode against a contiguous cache [B, stride, row]; returns (out, lse)."""
     B, Sq = q_nope.shape[0], q_nope.shape[1]
-    width = _check_cache(cache, shape if shape is not None else default_shape())
+    width = _check_cache(cache, shape if shape is not None else default_shape(), gpu=False)
     if cache.dim() != 3 or cache.shape[0] != B:
         raise MlaError(f"cache must be [B, stride, {width}]")
     out, lse, workspace, s = _decode_io(q_nope, q_pe, w_kv_b, ctx_lens, out, lse, workspace, B, Sq,
-                                        max_ctx_len, kv_chunk, shape)
+                                        max_ctx_len, kv_chunk, shape, cache=cache)
     _check(library().mla_decode(ctypes.byref(s), _ptr(q_nope), _ptr(q_pe), _ptr(w_kv_b), _ptr(cache),
                                 cache.shape[1], _ptr(ctx_lens), max_ctx_len, B, Sq, kv_chunk, _ptr(out),
                                 _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream)),
@@ -261,15 +279,15 @@ def mla_decode_paged(q_nope, q_pe, w_kv_b, cache, block_table, ctx_lens, max_ctx
                      kv_chunk: int = 0, out=None, lse=None, workspace=None,
                      shape: MlaShape | None = None, stream=None):
     """Decode against a paged cache [num_pages, 64, row]; returns (out, lse)."""
-    width = _check_cache(cache, shape if shape is not None else default_shape())
-    _need(block_table, torch.int32, "block_table")
+    width = _check_cache(cache, shape if shape is not None else default_shape(), gpu=False)
+    _need(block_table, torch.int32, "block_table", gpu=False)
     B, Sq = q_nope.shape[0], q_nope.shape[1]
     if cache.dim() != 3 or cache.shape[1] != 64:
         raise MlaError(f"cache must be [num_pages, 64, {width}]")
     if block_table.dim() != 2 or block_table.shape[0] != B:
         raise MlaError("block_table must be [B, max_pages_per_seq]")
     out, lse, workspace, s = _decode_io(q_nope, q_pe, w_kv_b, ctx_lens, out, lse, workspace, B, Sq,
-                                        max_ctx_len, kv_chunk, shape)
+                                        max_ctx_len, kv_chunk, shape, cache=cache, block_table=block_table)
     _check(library().mla_decode_paged(ctypes.byref(s), _ptr(q_nope), _ptr(q_pe), _ptr(w_kv_b), _ptr(cache),
                                       cache.shape[0], _ptr(block_table), block_table.shape[1],
                                       _ptr(ctx_lens), max_ctx_len, B, Sq, kv_chunk, _ptr(out), _ptr(lse),
@@ -285,15 +303,18 @@ def mla_decode_step(q_nope, q_pe, c_kv_new, k_pe_new, w_kv_b, cache, ctx_lens, m
     tokens' rows [c_kv_new | rot(k_pe_new)] into the cache, then decode.  q_pe and k_pe_new are
     NOT rotated.  ``block_table`` selects the paged layout [num_pages, 64, 576]; otherwise the
     cache is contiguous [B, stride, row].  Returns (out, lse)."""
-    width = _check_cache(cache, shape if shape is not None else default_shape())
+    width = _check_cache(cache, shape if shape is not None else default_shape(), gpu=False)
     B, Sq = q_nope.shape[0], q_nope.shape[1]
     for t, name, width in ((c_kv_new, "c_kv_new", 512), (k_pe_new, "k_pe_new", 64)):
         if t.dtype != torch.bfloat16 or t.device.type != "cuda" or t.dim() != 2 or t.stride(1) != 1:
             raise MlaError(f"{name} must be a 2-D bf16 GPU tensor with unit column stride")
         if t.shape[0] != B * Sq or t.shape[1] < width:
             raise MlaError(f"{name} must have B*Sq rows of at least {width} values")
+    for t, name in ((c_kv_new, "c_kv_new"), (k_pe_new, "k_pe_new")):
+        if t.device != q_nope.device:
+            raise MlaError(f"{name} is on {t.device}, q_nope on {q_nope.device}")
     out, lse, workspace, s = _decode_io(q_nope, q_pe, w_kv_b, ctx_lens, out, lse, workspace, B, Sq,
-                                        max_ctx_len, kv_chunk, shape)
+                                        max_ctx_len, kv_chunk, shape, cache=cache, block_table=block_table)
     r = rope if rope is not None else default_rope()
     lib = library()
     if block_table is None:
@@ -332,28 +353,29 @@ def mla_prefill(q_nope, q_pe, w_kv_b, cache, ctx_len: int, out=None, lse=None, w
                 shape: MlaShape | None = None, stream=None):
     """Chunked prefill of one sequence: q_nope [Tq, 32, 128], q_pe [Tq, 32, 64] (rotated) at
     positions ctx_len - Tq + j, cache [>= ctx_len, 576] bf16 rows; returns (out, lse)."""
-    _need(q_nope, torch.bfloat16, "q_nope")
-    _need(q_pe, torch.bfloat16, "q_pe")
-    _need(w_kv_b, torch.bfloat16, "w_kv_b")
-    Tq = q_nope.shape[0]
-    if tuple(q_nope.shape) != (Tq, 32, 128) or tuple(q_pe.shape) != (Tq, 32, 64):
-        raise MlaError("q_nope must be [Tq, 32, 128] and q_pe [Tq, 32, 64]")
-    if tuple(w_kv_b.shape) != (8192, 512):
-        raise MlaError("w_kv_b must be [8192, 512]")
+    Tq = q_nope.shape[0] if isinstance(q_nope, torch.Tensor) and q_nope.dim() > 0 else 0
+    _need(q_nope, torch.bfloat16, "q_nope", shape=(Tq, 32, 128), gpu=False)
+    dev = q_nope.device
+    _need(q_pe, torch.bfloat16, "q_pe", shape=(Tq, 32, 64), device=dev, gpu=False)
+    _need(w_kv_b, torch.bfloat16, "w_kv_b", shape=(8192, 512), device=dev, gpu=False)
     s = shape if shape is not None else default_shape()
-    width = _check_cache(cache, s)
+    width = _check_cache(cache, s, gpu=False)
+    if cache.device != dev:
+        raise MlaError(f"cache is on {cache.device}, q_nope on {dev}")
     if cache.dim() != 2 or cache.shape[0] < ctx_len:
         raise MlaError(f"cache must be [>= ctx_len, {width}]")
-    dev = q_nope.device
+    if out is not None:
+        _need(out, torch.bfloat16, "out", shape=(Tq, 32, 128), device=dev, gpu=False)
+    if lse is not None:
+        _need(lse, torch.float32, "lse", shape=(Tq, 32), device=dev, gpu=False)
+    if dev.type != "cuda":
+        raise MlaError(f"the arguments must be on the GPU (got {dev})")
     if out is None:
         out = torch.empty((Tq, 32, 128), dtype=torch.bfloat16, device=dev)
-    _need(out, torch.bfloat16, "out")
-    if lse is not None:
-        _need(lse, torch.float32, "lse")
     need = mla_prefill_workspace_size(ctx_len, s)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    _need(workspace, torch.uint8, "workspace")
+    _need(workspace, torch.uint8, "workspace", device=dev)
     _check(library().mla_prefill(ctypes.byref(s), _ptr(q_nope), _ptr(q_pe), _ptr(w_kv_b), _ptr(cache), ctx_len,
                                  Tq, _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream)),
            "mla_prefill")
@@ -389,3 +411,40 @@ def mla_read_probe(buf: torch.Tensor, sink: torch.Tensor, stream=None):
         raise MlaError(f"sink: {READ_PROBE_SINK_INTS} int32 elements required")
     _check(library().mla_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)),
            "mla_read_probe")
+
+
+def mla_device_faults(clear: bool = False) -> int:
+    """The current device's fault word (FAULT_* bits raised by the kernels since it was last
+    cleared), read after all work on the device has finished; ``clear`` resets it."""
+    v = ctypes.c_uint32()
+    _check(library().mla_device_faults(ctypes.byref(v), 1 if clear else 0), "mla_device_faults")
+    return v.value
+
+
+def mla_check_decode_inputs(ctx_lens, Sq: int, max_ctx_len: int, block_table=None, num_pages: int = 0) -> int:
+    """FAULT_* bits the decode kernels would raise for these host arrays (numpy or CPU tensors):
+    ctx_lens int32 [B], block_table int32 [B, max_pages] or None (contiguous layout)."""
+    import numpy as np
+    lens = np.ascontiguousarray(np.asarray(ctx_lens, dtype=np.int32))
+    B = lens.shape[0]
+    bt, mp = None, 0
+    if block_table is not None:
+        bt = np.ascontiguousarray(np.asarray(block_table, dtype=np.int32))
+        if bt.ndim != 2 or bt.shape[0] != B:
+            raise MlaError("block_table must be [B, max_pages_per_seq]")
+        mp = bt.shape[1]
+    v = ctypes.c_uint32()
+    _check(library().mla_check_decode_inputs(B, Sq, max_ctx_len, lens.ctypes.data_as(_P),
+                                             None if bt is None else bt.ctypes.data_as(_P), mp, num_pages,
+                                             ctypes.byref(v)), "mla_check_decode_inputs")
+    return v.value
+
+
+def mla_check_slot_mapping(slot_mapping, num_slots: int) -> int:
+    """FAULT_SLOT if a slot of this host array (int64) is at or beyond num_slots, else 0."""
+    import numpy as np
+    sm = np.ascontiguousarray(np.asarray(slot_mapping, dtype=np.int64))
+    v = ctypes.c_uint32()
+    _check(library().mla_check_slot_mapping(sm.ctypes.data_as(_P), sm.size, num_slots, ctypes.byref(v)),
+           "mla_check_slot_mapping")
+    return v.value

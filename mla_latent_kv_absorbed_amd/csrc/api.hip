@@ -3,6 +3,7 @@
 // workspace carving and kernel launches on the caller's stream.
 #include <math.h>
 #include <algorithm>
+#include <mutex>
 #include <string.h>
 
 #include "mla.h"   // include/mla.h (on the include path)
@@ -10,7 +11,32 @@
 
 using namespace mla;
 
+// Per-device fault word: the kernels OR MLA_FAULT_* bits into it when they
+// meet an index outside its range (mla_device_faults reads and clears it).
+__device__ uint32_t g_fault_word = 0;
+
 namespace {
+
+// Device address of the fault word, looked up once per device (with that
+// device current) by hipGetSymbolAddress: in host code its name is a
+// host-side stand-in, never a device address.
+constexpr int kMaxDevices = 64;
+struct DeviceSymbols {
+  std::once_flag once;
+  hipError_t err = hipSuccess;
+  uint32_t* faults = nullptr;
+};
+DeviceSymbols g_symbols[kMaxDevices];
+
+const DeviceSymbols* device_symbols() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  DeviceSymbols& d = g_symbols[dev];
+  std::call_once(d.once, [&d] {
+    d.err = hipGetSymbolAddress((void**)&d.faults, HIP_SYMBOL(g_fault_word));
+  });
+  return d.err == hipSuccess ? &d : nullptr;
+}
 
 constexpr int kMaxSq = 16;
 constexpr int64_t kMaxRows = 65535;   // B * Sq: one grid dimension of the combine
@@ -168,6 +194,8 @@ mla_status decode_common(const mla_shape* shape, const StepInputs& step, const v
   if (((segs + kXcds - 1) / kXcds) * kXcds * groups > (int64_t)(0xFFFFFFFFu / 256)) return MLA_ERR_RANGE;
   const WorkspaceLayout wl = workspace_layout(B, Sq, (int)segs);
   if (workspace_bytes < wl.total) return MLA_ERR_WORKSPACE;
+  const DeviceSymbols* sym = device_symbols();
+  if (sym == nullptr) return MLA_ERR_DEVICE;
 
   uint8_t* ws = (uint8_t*)workspace;
   uint16_t* qabs = (uint16_t*)(ws + wl.qabs);
@@ -187,6 +215,9 @@ mla_status decode_common(const mla_shape* shape, const StepInputs& step, const v
   pp.rows = rows;
   pp.Sq = Sq;
   pp.ctx_lens = ctx_lens;
+  pp.max_ctx_len = max_ctx_len;
+  pp.num_pages = num_pages;
+  pp.faults = sym->faults;
   pp.rotate = step.rope != nullptr;
   memset(&pp.inv, 0, sizeof(pp.inv));
   if (step.rope != nullptr) yarn_frequencies(*step.rope, pp.inv.v);
@@ -222,6 +253,8 @@ mla_status decode_common(const mla_shape* shape, const StepInputs& step, const v
   p.part_o = (uint16_t*)(ws + wl.part_o);
   p.part_lse = (float*)(ws + wl.part_lse);
   p.zero_row = zero_row;
+  p.num_pages = num_pages;
+  p.faults = sym->faults;
   const bool timed = g_timing.on && g_timing.used < g_timing.capacity;
   {
     hipEvent_t ev0 = timed ? g_timing.ev[2 * g_timing.used] : nullptr;
@@ -323,13 +356,15 @@ mla_status mla_cache_append(const mla_shape* shape, void* cache, int64_t num_slo
       ((uintptr_t)slot_mapping & 7u) != 0)
     return MLA_ERR_ALIGN;
   if (n > (int64_t)1 << 40) return MLA_ERR_RANGE;
+  const DeviceSymbols* sym = device_symbols();
+  if (sym == nullptr) return MLA_ERR_DEVICE;
   if (shape->kv_cache_dtype == MLA_CACHE_FP8_E4M3)
-    return launch_append_fp8((uint8_t*)cache, (const uint16_t*)c_kv, ld_c, (const uint16_t*)k_pe, ld_k,
-                             slot_mapping, n, (hipStream_t)stream) == hipSuccess
+    return launch_append_fp8((uint8_t*)cache, num_slots, (const uint16_t*)c_kv, ld_c, (const uint16_t*)k_pe, ld_k,
+                             slot_mapping, n, sym->faults, (hipStream_t)stream) == hipSuccess
                ? MLA_OK
                : MLA_ERR_DEVICE;
   return launch_append((uint8_t*)cache, num_slots, (const uint16_t*)c_kv, ld_c, (const uint16_t*)k_pe,
-                       ld_k, slot_mapping, n, (hipStream_t)stream) == hipSuccess
+                       ld_k, slot_mapping, n, sym->faults, (hipStream_t)stream) == hipSuccess
              ? MLA_OK
              : MLA_ERR_DEVICE;
 }
@@ -402,9 +437,11 @@ mla_status mla_prefill(const mla_shape* shape, const void* q_nope, const void* q
     return MLA_ERR_ALIGN;
   if (lse != nullptr && ((uintptr_t)lse & 3u) != 0) return MLA_ERR_ALIGN;
   if (workspace_bytes < prefill_workspace_bytes(ctx_len)) return MLA_ERR_WORKSPACE;
+  const DeviceSymbols* sym = device_symbols();
+  if (sym == nullptr) return MLA_ERR_DEVICE;
   const float scale_log2 = shape->softmax_scale * 1.44269504088896340736f;
   if (launch_prefill((const uint16_t*)q_nope, (const uint16_t*)q_pe, (const uint16_t*)w_kv_b, (const uint8_t*)cache,
-                     ctx_len, Tq, scale_log2, (uint16_t*)workspace, (uint16_t*)out, lse,
+                     ctx_len, Tq, scale_log2, (uint16_t*)workspace, (uint16_t*)out, lse, sym->faults,
                      (hipStream_t)stream) != hipSuccess)
     return MLA_ERR_DEVICE;
   return MLA_OK;
@@ -425,6 +462,51 @@ mla_status mla_decode_workspace_size(const mla_shape* shape, int32_t B, int32_t 
   const int64_t segs = max_segments(B, max_ctx_len, kv_chunk, compute_units());
   if (segs > 0x7FFFFFFF) return MLA_ERR_RANGE;
   *bytes = workspace_layout(B, Sq, (int)segs).total;
+  return MLA_OK;
+}
+
+mla_status mla_device_faults(uint32_t* faults, int32_t clear) {
+  if (faults == nullptr) return MLA_ERR_NULL;
+  const DeviceSymbols* sym = device_symbols();
+  if (sym == nullptr) return MLA_ERR_DEVICE;
+  if (hipDeviceSynchronize() != hipSuccess) return MLA_ERR_DEVICE;
+  if (hipMemcpy(faults, sym->faults, sizeof(uint32_t), hipMemcpyDeviceToHost) != hipSuccess) return MLA_ERR_DEVICE;
+  if (clear) {
+    if (hipMemset(sym->faults, 0, sizeof(uint32_t)) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+      return MLA_ERR_DEVICE;
+  }
+  return MLA_OK;
+}
+
+mla_status mla_check_decode_inputs(int32_t B, int32_t Sq, int32_t max_ctx_len, const int32_t* ctx_lens,
+                                   const int32_t* block_table, int32_t max_pages_per_seq, int64_t num_pages,
+                                   uint32_t* faults) {
+  if (faults == nullptr || (B > 0 && ctx_lens == nullptr)) return MLA_ERR_NULL;
+  if (B < 0 || Sq < 1 || Sq > kMaxSq || max_ctx_len < Sq) return MLA_ERR_RANGE;
+  if (block_table != nullptr && (num_pages < 1 || max_pages_per_seq < (max_ctx_len + kPage - 1) / kPage))
+    return MLA_ERR_RANGE;
+  uint32_t f = 0;
+  for (int b = 0; b < B; ++b) {
+    bool bad;
+    const int L = clamp_ctx_len(ctx_lens[b], Sq, max_ctx_len, &bad);
+    if (bad) f |= kFaultCtxLen;
+    if (block_table != nullptr) {
+      const int32_t* row = block_table + (size_t)b * max_pages_per_seq;
+      for (int k = 0; k < (L + kPage - 1) / kPage; ++k)
+        if (!page_ok(row[k], num_pages)) f |= kFaultPage;
+    }
+  }
+  *faults = f;
+  return MLA_OK;
+}
+
+mla_status mla_check_slot_mapping(const int64_t* slot_mapping, int64_t n, int64_t num_slots, uint32_t* faults) {
+  if (faults == nullptr || (n > 0 && slot_mapping == nullptr)) return MLA_ERR_NULL;
+  if (n < 0 || num_slots < 0) return MLA_ERR_RANGE;
+  uint32_t f = 0;
+  for (int64_t i = 0; i < n; ++i)
+    if (slot_fault(slot_mapping[i], num_slots)) f |= kFaultSlot;
+  *faults = f;
   return MLA_OK;
 }
 

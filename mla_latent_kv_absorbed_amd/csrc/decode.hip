@@ -184,13 +184,18 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode(DecodeParams p) {
   // tokens multiply zeros.
   auto issue = [&](int ts, int r) {
     const uint8_t* src;
+    int nval = min(kSlotTok, t_end - ts * kSlotTok);
     if constexpr (PAGED) {
       const int page = p.block_table[(size_t)b * p.max_pages + ts];
       src = p.cache + (size_t)page * kTileBytes;
+      if (!page_ok(page, p.num_pages)) {   // a page outside the pool: its rows are read as zeros
+        if (tid == 0) raise_fault(p.faults, kFaultPage);
+        src = p.cache;
+        nval = 0;
+      }
     } else {
       src = p.cache + ((size_t)b * p.stride_tokens + (size_t)ts * kSlotTok) * kRowBytes;
     }
-    const int nval = min(kSlotTok, t_end - ts * kSlotTok);
     const uint32_t dst = ring_lds + r * kSlotLds + i0 * 1024;
     if (nval == kSlotTok) {
 #pragma unroll

@@ -165,13 +165,18 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode_fp8(DecodeParams p
   auto issue = [&](int ts, int r) {
     if (!dma_wave) return;
     const uint8_t* src;
+    int nval = min(kSlotTok, t_end - ts * kSlotTok);
     if constexpr (PAGED) {
       const int page = p.block_table[(size_t)b * p.max_pages + ts];
       src = p.cache + (size_t)page * kF8Tile;
+      if (!page_ok(page, p.num_pages)) {   // a page outside the pool: its rows are read as zeros
+        if (tid == 0) raise_fault(p.faults, kFaultPage);
+        src = p.cache;
+        nval = 0;
+      }
     } else {
       src = p.cache + ((size_t)b * p.stride_tokens + (size_t)ts * kSlotTok) * kF8Row;
     }
-    const int nval = min(kSlotTok, t_end - ts * kSlotTok);
     const uint32_t dst = ring_lds + r * kSlotLds + wave * kLoadsPerLane * 1024;
     if (nval == kSlotTok) {
       // a whole slot: byte offset 16 P from the slot's (wave-uniform) start;

@@ -102,9 +102,18 @@ __device__ void build_schedule(const PrepParams& p, int* lds) {
   const bool in_lds = p.B <= kSchedLds;
   int* lens = lds;                    // [kSchedLds]
   int* starts = lds + kSchedLds;      // [kSchedLds + 1]
-  auto len_of = [&](int b) { return in_lds ? lens[b] : p.ctx_lens[b]; };
+  // lengths clamped into [Sq, max_ctx_len]; a clamped length raises the fault
+  // bit once (the first thread that meets one in this workgroup's pass)
+  bool bad_len = false;
+  auto read_len = [&](int b) {
+    bool bad;
+    const int L = clamp_ctx_len(p.ctx_lens[b], p.Sq, p.max_ctx_len, &bad);
+    bad_len |= bad;
+    return L;
+  };
+  auto len_of = [&](int b) { return in_lds ? lens[b] : read_len(b); };
   if (in_lds) {
-    for (int b = t; b < p.B; b += 256) lens[b] = p.ctx_lens[b];
+    for (int b = t; b < p.B; b += 256) lens[b] = read_len(b);
     __syncthreads();
   }
   int c = p.fixed_tiles;
@@ -163,6 +172,7 @@ __device__ void build_schedule(const PrepParams& p, int* lds) {
     }
   }
   for (int w = carry + t; w < p.max_segs; w += 256) p.seg_desc[w] = make_int4(-1, 0, 0, 0);
+  if (bad_len) raise_fault(p.faults, kFaultCtxLen);
 }
 
 // ---------------------------------------------------------------------------
@@ -242,7 +252,8 @@ __global__ void __launch_bounds__(256) prep_query(PrepParams p) {
   p.qres[hrow * kLatent + cblk * 64 + col] = acc - bf16_to_f32(qb);
 
   const int b = r / p.Sq;
-  const int pos = p.ctx_lens[b] - p.Sq + (r - b * p.Sq);
+  bool bad_len;   // raised by the schedule
+  const int pos = clamp_ctx_len(p.ctx_lens[b], p.Sq, p.max_ctx_len, &bad_len) - p.Sq + (r - b * p.Sq);
   const int half = kRope / 2;
   if (cblk == 0) {
     const uint16_t* src = p.q_pe + hrow * kRope;
@@ -259,8 +270,16 @@ __global__ void __launch_bounds__(256) prep_query(PrepParams p) {
     // 8-bit row: latent group cblk (128 values, 2 per lane of this row's wave)
     // quantised with its own scale; the rope key rotated into bf16 at byte 528
     int64_t slot;
-    if (p.paged) slot = (int64_t)p.block_table[(size_t)b * p.max_pages + pos / kPage] * kPage + pos % kPage;
-    else slot = (int64_t)b * p.stride_tokens + pos;
+    if (p.paged) {
+      const int page = p.block_table[(size_t)b * p.max_pages + pos / kPage];
+      if (!page_ok(page, p.num_pages)) {   // no row is written for a page outside the pool
+        if (col == 0) raise_fault(p.faults, kFaultPage);
+        return;
+      }
+      slot = (int64_t)page * kPage + pos % kPage;
+    } else {
+      slot = (int64_t)b * p.stride_tokens + pos;
+    }
     uint8_t* row = p.cache + slot * kF8Row;
     if (h == 0) {
       const uint32_t two = *(const uint32_t*)(p.c_new + r * p.ld_c + cblk * kF8Group + 2 * col);
@@ -288,8 +307,16 @@ __global__ void __launch_bounds__(256) prep_query(PrepParams p) {
   }
   if (p.c_new != nullptr && !p.fp8 && pos >= 0 && (h == 0 || (h == 1 && cblk == 0))) {
     int64_t slot;
-    if (p.paged) slot = (int64_t)p.block_table[(size_t)b * p.max_pages + pos / kPage] * kPage + pos % kPage;
-    else slot = (int64_t)b * p.stride_tokens + pos;
+    if (p.paged) {
+      const int page = p.block_table[(size_t)b * p.max_pages + pos / kPage];
+      if (!page_ok(page, p.num_pages)) {   // no row is written for a page outside the pool
+        if (col == 0) raise_fault(p.faults, kFaultPage);
+        return;
+      }
+      slot = (int64_t)page * kPage + pos % kPage;
+    } else {
+      slot = (int64_t)b * p.stride_tokens + pos;
+    }
     uint16_t* crow = (uint16_t*)(p.cache + slot * kRowBytes);
     if (h == 0) {
       crow[cblk * 64 + col] = p.c_new[r * p.ld_c + cblk * 64 + col];
@@ -498,13 +525,18 @@ __global__ void __launch_bounds__(256) rope_rotate(const uint16_t* src, int64_t 
 __global__ void __launch_bounds__(256) cache_append(uint8_t* __restrict__ cache,
                                                     const uint16_t* __restrict__ c_kv, int64_t ld_c,
                                                     const uint16_t* __restrict__ k_pe, int64_t ld_k,
-                                                    const int64_t* __restrict__ slots, int64_t n) {
+                                                    const int64_t* __restrict__ slots, int64_t n,
+                                                    int64_t num_slots, uint32_t* faults) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= n * kChunksPerRow) return;
   const int64_t t = idx / kChunksPerRow;
   const int c = (int)(idx - t * kChunksPerRow);
   const int64_t slot = slots[t];
   if (slot < 0) return;
+  if (slot_fault(slot, num_slots)) {   // outside the cache: the row is skipped
+    if (c == 0) raise_fault(faults, kFaultSlot);
+    return;
+  }
   const uint4 v = (c < 64) ? *(const uint4*)(c_kv + t * ld_c + c * 8)
                            : *(const uint4*)(k_pe + t * ld_k + (c - 64) * 8);
   *(uint4*)(cache + slot * kRowBytes + c * 16) = v;
@@ -519,12 +551,17 @@ __global__ void __launch_bounds__(256) cache_append(uint8_t* __restrict__ cache,
 __global__ void __launch_bounds__(256) cache_append_fp8(uint8_t* __restrict__ cache,
                                                         const uint16_t* __restrict__ c_kv, int64_t ld_c,
                                                         const uint16_t* __restrict__ k_pe, int64_t ld_k,
-                                                        const int64_t* __restrict__ slots, int64_t n) {
+                                                        const int64_t* __restrict__ slots, int64_t n,
+                                                        int64_t num_slots, uint32_t* faults) {
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (t >= n) return;
   const int64_t slot = slots[t];
   if (slot < 0) return;
+  if (slot_fault(slot, num_slots)) {   // outside the cache: the row is skipped
+    if (lane == 0) raise_fault(faults, kFaultSlot);
+    return;
+  }
   const uint4 v = *(const uint4*)(c_kv + t * ld_c + 8 * lane);
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
   float x[8];
@@ -552,10 +589,12 @@ __global__ void __launch_bounds__(256) cache_append_fp8(uint8_t* __restrict__ ca
 
 }  // namespace
 
-hipError_t launch_append_fp8(uint8_t* cache, const uint16_t* c_kv, int64_t ld_c, const uint16_t* k_pe,
-                             int64_t ld_k, const int64_t* slots, int64_t n, hipStream_t stream) {
+hipError_t launch_append_fp8(uint8_t* cache, int64_t num_slots, const uint16_t* c_kv, int64_t ld_c,
+                             const uint16_t* k_pe, int64_t ld_k, const int64_t* slots, int64_t n,
+                             uint32_t* faults, hipStream_t stream) {
   const unsigned blocks = (unsigned)((n + 3) / 4);
-  hipLaunchKernelGGL(cache_append_fp8, dim3(blocks), dim3(256), 0, stream, cache, c_kv, ld_c, k_pe, ld_k, slots, n);
+  hipLaunchKernelGGL(cache_append_fp8, dim3(blocks), dim3(256), 0, stream, cache, c_kv, ld_c, k_pe, ld_k, slots, n,
+                     num_slots, faults);
   return hipGetLastError();
 }
 
@@ -588,12 +627,11 @@ hipError_t launch_rope(const uint16_t* src, int64_t ld_src, uint16_t* dst, int64
 
 hipError_t launch_append(uint8_t* cache, int64_t num_slots, const uint16_t* c_kv, int64_t ld_c,
                          const uint16_t* k_pe, int64_t ld_k, const int64_t* slots, int64_t n,
-                         hipStream_t stream) {
-  (void)num_slots;
+                         uint32_t* faults, hipStream_t stream) {
   const int64_t total = n * kChunksPerRow;
   const unsigned blocks = (unsigned)((total + 255) / 256);
   hipLaunchKernelGGL(cache_append, dim3(blocks), dim3(256), 0, stream, cache, c_kv, ld_c, k_pe, ld_k,
-                     slots, n);
+                     slots, n, num_slots, faults);
   return hipGetLastError();
 }
 

@@ -32,6 +32,31 @@ constexpr int kF8Group = 128;
 constexpr int kF8Tile = kPage * kF8Row;         // 41984 bytes per page
 constexpr float kE4M3Max = 448.0f;
 
+// Fault bits of the per-device fault word (values as MLA_FAULT_* in mla.h).
+// A kernel that meets an index outside its documented range skips or clamps
+// that item, so that every access stays inside the caller's buffers, and ORs
+// the bit into the word.
+constexpr uint32_t kFaultSlot = 1u;        // append: slot >= num_slots (row skipped)
+constexpr uint32_t kFaultPage = 2u;        // block-table page outside [0, num_pages)
+constexpr uint32_t kFaultCtxLen = 4u;      // ctx_lens[b] outside [Sq, max_ctx_len] (clamped)
+constexpr uint32_t kFaultFp16Range = 8u;   // prefill: a value beyond the fp16 range
+
+// The range rules, shared by the kernels and the host-side validator.
+// A context length is clamped into [Sq, max_ctx_len]; a page must lie in
+// [0, num_pages); a slot below 0 means "skip" (no fault), one at or above
+// num_slots is a fault.
+__host__ __device__ inline int clamp_ctx_len(int L, int Sq, int max_ctx_len, bool* bad) {
+  const bool lo = L < Sq, hi = L > max_ctx_len;
+  *bad = lo || hi;
+  return lo ? Sq : (hi ? max_ctx_len : L);
+}
+__host__ __device__ inline bool page_ok(int64_t page, int64_t num_pages) { return page >= 0 && page < num_pages; }
+__host__ __device__ inline bool slot_fault(int64_t slot, int64_t num_slots) { return slot >= num_slots; }
+
+__device__ __forceinline__ void raise_fault(uint32_t* faults, uint32_t bit) {
+  if (faults != nullptr) __hip_atomic_fetch_or(faults, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
@@ -102,6 +127,8 @@ struct DecodeParams {
   uint16_t* part_o;             // bf16 normalised partial rows
   float* part_lse;
   const uint8_t* zero_row;      // kRowBytes zero bytes
+  int64_t num_pages;            // paged layout: pages of the pool (block-table entries are checked)
+  uint32_t* faults;             // the device's fault word
 };
 
 // Query tokens per split-KV workgroup, and the number of such query groups
@@ -170,7 +197,10 @@ struct PrepParams {
   int32_t rows;                 // B * Sq
   int32_t B;
   int32_t Sq;
-  const int32_t* ctx_lens;
+  const int32_t* ctx_lens;      // read clamped into [Sq, max_ctx_len]
+  int32_t max_ctx_len;
+  int64_t num_pages;
+  uint32_t* faults;
   int32_t rotate;               // q_pe and k_new are rotated here when non-zero
   InvFreq inv;
   const uint16_t* c_new;        // bf16 [rows][ld_c] latent rows of the new tokens, or null
@@ -220,15 +250,17 @@ hipError_t launch_rope(const uint16_t* src, int64_t ld_src, uint16_t* dst, int64
                        hipStream_t stream);
 hipError_t launch_append(uint8_t* cache, int64_t num_slots, const uint16_t* c_kv, int64_t ld_c,
                          const uint16_t* k_pe, int64_t ld_k, const int64_t* slots, int64_t n,
-                         hipStream_t stream);
-hipError_t launch_append_fp8(uint8_t* cache, const uint16_t* c_kv, int64_t ld_c, const uint16_t* k_pe,
-                             int64_t ld_k, const int64_t* slots, int64_t n, hipStream_t stream);
+                         uint32_t* faults, hipStream_t stream);
+hipError_t launch_append_fp8(uint8_t* cache, int64_t num_slots, const uint16_t* c_kv, int64_t ld_c,
+                             const uint16_t* k_pe, int64_t ld_k, const int64_t* slots, int64_t n,
+                             uint32_t* faults, hipStream_t stream);
 // Chunked prefill (prefill.hip): expand the L context rows through kv_b_proj
-// into kv (bf16 rows [8192 expanded | 64 rope key], L rounded up to 256 rows,
-// prefill_workspace_bytes), then causal attention of the Tq chunk tokens.
+// into kv (rows [8192 expanded values, fp16 | 64 rope key, bf16], L rounded
+// up to 256 rows, prefill_workspace_bytes), then causal attention of the Tq
+// chunk tokens.
 hipError_t launch_prefill(const uint16_t* q_nope, const uint16_t* q_pe, const uint16_t* w_kv_b, const uint8_t* cache,
                           int32_t L, int32_t Tq, float scale_log2, uint16_t* kv, uint16_t* out, float* lse,
-                          hipStream_t stream);
+                          uint32_t* faults, hipStream_t stream);
 size_t prefill_workspace_bytes(int32_t L);
 hipError_t launch_decode_fp8(const DecodeParams& p, int segments, bool paged, hipStream_t stream,
                              hipEvent_t ev_start, hipEvent_t ev_stop);

@@ -14,19 +14,23 @@
 // the expansion (2*512*8192 flops per cached token, once) pays for itself.
 //
 // Two kernels:
-//  * expand_kv: KV[t][o] = bf16(sum_k W[o][k] c_t[k]) for the 8192 rows o of
+//  * expand_kv: KV[t][o] = fp16(sum_k W[o][k] c_t[k]) for the 8192 rows o of
 //    kv_b_proj (per head [k_nope 128 | v 128]); 256 persistent workgroups of
 //    8 waves walk 256 x 256 output tiles with one pipeline of 64-wide k stages
 //    (double-buffered in LDS through direct global->LDS loads), on
-//    v_mfma_f32_16x16x32_bf16.
+//    v_mfma_f32_16x16x32_bf16.  The expanded values are kept in fp16, whose
+//    11-bit significand rounds a key 8 times more finely than bf16 at the same
+//    matrix-core rate: a row that sees one or two tokens has no other tokens
+//    to average that rounding out of its log-sum-exp.
 //  * prefill_attention: flash attention (rescaling only when a row's maximum
 //    outgrows its reference by 2^8); a workgroup of 8 waves takes 256 query
 //    rows of one head, each wave 32 rows (two row groups of 16, so every LDS
 //    read of a key or value tile feeds two MFMAs); 64-token tiles of
 //    [K_nope | k_pe] and V stream through a three-tile LDS ring.
-//    S^T = K . Q^T with the keys as the A operand; the S^T accumulator layout
-//    is the B-operand layout of P in O^T += V^T P^T, with V^T fetched by
-//    ds_read_b64_tr_b16, so P stays in registers.  The query tiles of a head
+//    S^T = K . Q^T with the keys as the A operand (fp16 products over the
+//    128 nope dims, bf16 over the 64 rope dims, one fp32 accumulator); the
+//    S^T accumulator layout is the B-operand layout of P in O^T += V^T P^T
+//    (fp16), with V^T fetched by ds_read_b64_tr_b16, so P stays in registers.  The query tiles of a head
 //    are placed on one XCD (workgroups x, x + 8, ...), where they read the
 //    head's key and value tiles from the same L2.
 #include "mla_internal.h"
@@ -36,10 +40,13 @@ namespace {
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kKvRow = kHeads * kWRowsPerHead;   // 8192 expanded values per token
-constexpr int kKvStride = kKvRow + kRope;         // workspace row: [8192 expanded | 64 rope key]
+constexpr int kKvStride = kKvRow + kRope;         // workspace row: [8192 expanded (fp16) | 64 rope key (bf16)]
+constexpr float kF16Max = 65504.0f;              // largest finite fp16
 
 typedef __attribute__((__vector_size__(8 * sizeof(float)))) float f32x8;
-typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+typedef __attribute__((address_space(3))) const f16x8 lds_f16x8_t;
 typedef __attribute__((__vector_size__(2 * sizeof(unsigned)))) unsigned u32x2;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 typedef __attribute__((address_space(3))) const uint8_t lds_cu8;
@@ -76,7 +83,7 @@ __device__ __forceinline__ lds_cu8* lds_base(uint32_t lds) {
 }
 
 // ---------------------------------------------------------------------------
-// expand_kv.  KV[t][o] = bf16(W[o][:] . c_t) for the 8192 rows o of kv_b_proj.
+// expand_kv.  KV[t][o] = fp16(W[o][:] . c_t) for the 8192 rows o of kv_b_proj.
 // Output tiles of 256 rows x 256 tokens; one workgroup of 8 waves per compute
 // unit walks its tiles with one pipeline of 64-wide k stages across tile
 // boundaries (the next tile's first stages load while the current tile
@@ -100,7 +107,7 @@ constexpr int kExpOTiles = kKvRow / kExpTile;                    // 32
 static_assert(kExpOTiles == 4 * kXcds && kExpGrid == kExpOTiles * kXcds, "tile placement");
 
 __global__ void __launch_bounds__(512, 2) expand_kv(const uint16_t* __restrict__ w, const uint8_t* __restrict__ cache,
-                                                 int32_t L, uint16_t* __restrict__ kv) {
+                                                 int32_t L, uint16_t* __restrict__ kv, uint32_t* faults) {
   __shared__ __attribute__((aligned(1024))) uint8_t st[2 * kExpStageBytes];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -197,14 +204,18 @@ __global__ void __launch_bounds__(512, 2) expand_kv(const uint16_t* __restrict__
       // Every row of the tile is written (rows past L repeat row L - 1), so
       // that the attention's last tile reads defined values.
       const int t0 = (tt0 + kXcds * (s / kExpStages)) * kExpTile;
+      float amax = 0.f;   // largest magnitude in this lane's share (fp16 range check)
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
         const int t = t0 + 64 * wt + 16 * tb + n16;
         uint16_t* krow = kv + (size_t)t * kKvStride + o0 + 128 * wo + 16 * (g & 1) + 8 * (g >> 1);
 #pragma unroll
         for (int pr = 0; pr < 4; ++pr) {
-          const u32x2 a = __builtin_bit_cast(u32x2, __builtin_convertvector(acc[2 * pr][tb], bf16x4));
-          const u32x2 b = __builtin_bit_cast(u32x2, __builtin_convertvector(acc[2 * pr + 1][tb], bf16x4));
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            amax = fmaxf(amax, fmaxf(fabsf(acc[2 * pr][tb][i]), fabsf(acc[2 * pr + 1][tb][i])));
+          const u32x2 a = __builtin_bit_cast(u32x2, __builtin_convertvector(acc[2 * pr][tb], f16x4));
+          const u32x2 b = __builtin_bit_cast(u32x2, __builtin_convertvector(acc[2 * pr + 1][tb], f16x4));
           const auto lo = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
           const auto hi = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
           *(uint4*)(krow + 32 * pr) = make_uint4(lo[0], hi[0], lo[1], hi[1]);
@@ -212,6 +223,8 @@ __global__ void __launch_bounds__(512, 2) expand_kv(const uint16_t* __restrict__
           acc[2 * pr + 1][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
       }
+      // values past the largest finite fp16 (65504) or not finite: flagged
+      if (__builtin_amdgcn_ballot_w64(!(amax <= kF16Max)) != 0 && lane == 0) raise_fault(faults, kFaultFp16Range);
     }
     if (s + 2 < nst) issue(s + 2, s & 1);
   }
@@ -258,6 +271,7 @@ struct PrefillParams {
   float scale_log2;
   uint16_t* out;            // bf16 [Tq][32][128]
   float* lse;               // fp32 [Tq][32] or null
+  uint32_t* faults;         // the device's fault word
 };
 
 // Maxima of finite or infinite scores (no NaN handling needed; written as
@@ -307,24 +321,39 @@ __global__ void __launch_bounds__(kPfWaves * 64, 2) prefill_attention(PrefillPar
   const int base = p.L - p.Tq;                     // position of query row 0
   const uint32_t ring_lds = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)ring);
 
-  // this wave's rows: q0 + kRowsW wave + 16 rg + n16 (rows past Tq repeat Tq - 1, never stored)
-  bf16x8 q[RG][6];
+  // this wave's rows: q0 + kRowsW wave + 16 rg + n16 (rows past Tq repeat Tq - 1, never stored).
+  // The nope part meets the fp16 keys, so it is widened to fp16 (exact for
+  // bf16 values of magnitude 2^-14 .. 65504; smaller ones round to the fp16
+  // subnormal grid, an absolute error below 2^-25); the rope part stays bf16.
+  f16x8 qn16[RG][4];
+  bf16x8 qr[RG][2];
+  float qmax = 0.f;
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) {
     const int j = min(q0 + kRowsW * wave + 16 * rg + n16, p.Tq - 1);
     const uint16_t* qn = p.q_nope + ((size_t)j * kHeads + h) * kNope + 8 * g;
     const uint16_t* qp = p.q_pe + ((size_t)j * kHeads + h) * kRope + 8 * g;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) q[rg][ks] = *(const bf16x8*)(qn + 32 * ks);
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 v = *(const bf16x8*)(qn + 32 * ks);
+      const f32x8 w = __builtin_convertvector(v, f32x8);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) q[rg][4 + ks] = *(const bf16x8*)(qp + 32 * ks);
+      for (int i = 0; i < 8; ++i) qmax = fmaxf(qmax, fabsf(w[i]));
+      qn16[rg][ks] = __builtin_convertvector(w, f16x8);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) qr[rg][ks] = *(const bf16x8*)(qp + 32 * ks);
   }
+  if (__builtin_amdgcn_ballot_w64(!(qmax <= kF16Max)) != 0 && lane == 0) raise_fault(p.faults, kFaultFp16Range);
   // settle the query loads before the direct loads start (a wait placed at
   // their first use would also drain the tiles in flight)
 #pragma unroll
-  for (int rg = 0; rg < RG; ++rg)
+  for (int rg = 0; rg < RG; ++rg) {
 #pragma unroll
-    for (int ks = 0; ks < 6; ++ks) asm volatile("" ::"v"(q[rg][ks]));
+    for (int ks = 0; ks < 4; ++ks) asm volatile("" ::"v"(qn16[rg][ks]));
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) asm volatile("" ::"v"(qr[rg][ks]));
+  }
 
   // key/value tiles of tokens [0, last visible of the workgroup's rows]
   const int last_row = min(q0 + kQRows, p.Tq) - 1;
@@ -417,16 +446,27 @@ __global__ void __launch_bounds__(kPfWaves * 64, 2) prefill_attention(PrefillPar
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) s[rg][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 6; ++ks) {
-        bf16x8 a[2];
+      for (int ks = 0; ks < 4; ++ks) {   // nope dims: fp16 keys
+        f16x8 a[2];
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
-          a[tb] = *(lds_bf16x8_t*)(T + k_lane + (32 * hb + 16 * tb) * kPfKRow + 16 * (ks < 4 ? 4 * ks : 16 + 4 * (ks - 4)));
+        for (int tb = 0; tb < 2; ++tb) a[tb] = *(lds_f16x8_t*)(T + k_lane + (32 * hb + 16 * tb) * kPfKRow + 64 * ks);
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
           for (int rg = 0; rg < RG; ++rg)
-            s[rg][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[tb], q[rg][ks], s[rg][tb], 0, 0, 0);
+            s[rg][tb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[tb], qn16[rg][ks], s[rg][tb], 0, 0, 0);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {   // rope dims: bf16 keys
+        bf16x8 a[2];
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+          a[tb] = *(lds_bf16x8_t*)(T + k_lane + (32 * hb + 16 * tb) * kPfKRow + 16 * (16 + 4 * ks));
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+          for (int rg = 0; rg < RG; ++rg)
+            s[rg][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[tb], qr[rg][ks], s[rg][tb], 0, 0, 0);
       }
       // causal mask, only on steps that reach past the wave's first row
       // (a wave-uniform branch; the empty asm keeps it a branch)
@@ -474,7 +514,7 @@ __global__ void __launch_bounds__(kPfWaves * 64, 2) prefill_attention(PrefillPar
             for (int i = 0; i < 4; ++i) o[rg][vb][i] *= alpha;
         }
       }
-      bf16x8 pa[RG];
+      f16x8 pa[RG];   // p <= 2^kPfTau: inside the fp16 range
 #pragma unroll
       for (int rg = 0; rg < RG; ++rg) {
         // k order of the 32-token step: tokens 4g+i of block 0, then of block 1
@@ -484,7 +524,7 @@ __global__ void __launch_bounds__(kPfWaves * 64, 2) prefill_attention(PrefillPar
 #pragma unroll
           for (int i = 0; i < 4; ++i) e[4 * tb + i] = __builtin_amdgcn_exp2f(fmaf(s[rg][tb][i], p.scale_log2, nsub[rg]));
         l[rg] += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
-        pa[rg] = __builtin_convertvector(e, bf16x8);
+        pa[rg] = __builtin_convertvector(e, f16x8);
       }
 
       // ---- O^T += V^T . P^T: 8 value blocks of 16 columns, this 32-token step
@@ -493,10 +533,10 @@ __global__ void __launch_bounds__(kPfWaves * 64, 2) prefill_attention(PrefillPar
         lds_cu8* a = T + v_lane + 32 * hb * kPfVRow + 32 * vb;
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)a);
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(a + 16 * kPfVRow));
-        const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        const f16x8 av = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int rg = 0; rg < RG; ++rg)
-          o[rg][vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pa[rg], o[rg][vb], 0, 0, 0);
+          o[rg][vb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pa[rg], o[rg][vb], 0, 0, 0);
       }
     }
   }
@@ -527,8 +567,8 @@ __global__ void __launch_bounds__(kPfWaves * 64, 2) prefill_attention(PrefillPar
 
 hipError_t launch_prefill(const uint16_t* q_nope, const uint16_t* q_pe, const uint16_t* w_kv_b, const uint8_t* cache,
                           int32_t L, int32_t Tq, float scale_log2, uint16_t* kv, uint16_t* out, float* lse,
-                          hipStream_t stream) {
-  hipLaunchKernelGGL(expand_kv, dim3(kExpGrid), dim3(512), 0, stream, w_kv_b, cache, L, kv);
+                          uint32_t* faults, hipStream_t stream) {
+  hipLaunchKernelGGL(expand_kv, dim3(kExpGrid), dim3(512), 0, stream, w_kv_b, cache, L, kv, faults);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   PrefillParams pp;
   pp.q_nope = q_nope;
@@ -539,6 +579,7 @@ hipError_t launch_prefill(const uint16_t* q_nope, const uint16_t* q_pe, const ui
   pp.scale_log2 = scale_log2;
   pp.out = out;
   pp.lse = lse;
+  pp.faults = faults;
   constexpr int kRows = 32 * kPfWaves;
   pp.qtiles = (Tq + kRows - 1) / kRows;
   hipLaunchKernelGGL(prefill_attention, dim3((unsigned)(pp.qtiles * kHeads)),

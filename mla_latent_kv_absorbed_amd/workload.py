@@ -64,6 +64,7 @@ class DeviceWorkload:
             bt, pool = synth.block_tables(self.seed, self.lens, 64, permute)
             self.block_table_host = bt
             self.block_table = torch.from_numpy(bt).to(self.dev)
+            self.block_table64 = torch.from_numpy(bt.astype("int64")).to(self.dev)   # for slot arithmetic
             self.num_pages = pool
             self.cache_shape = (pool, 64, self.row_width)
         else:
@@ -81,16 +82,16 @@ class DeviceWorkload:
         self.q_pos = torch.tensor(qpos, dtype=torch.int32, device=self.dev)
         self.new_pos = torch.tensor(npos, dtype=torch.int32, device=self.dev)
         self.new_slots = self.slots_of(torch.arange(B, device=self.dev).repeat_interleave(Sq),
-                                       self.new_pos.to(torch.int64))
+                                       torch.tensor(npos, dtype=torch.int64, device=self.dev))
         self.workspace_bytes = mla_decode_workspace_size(B, Sq, self.max_ctx, self.kv_chunk, self.shape)
         self.workspace = torch.empty(self.workspace_bytes, dtype=torch.uint8, device=self.dev)
         self.chunk_used = self.kv_chunk or mla_decode_auto_chunk(B, Sq, self.max_ctx)
 
     # ---- addressing
-    def slots_of(self, b: torch.Tensor, t: torch.Tensor) -> torch.Tensor:
-        """Cache slot of token t of sequence b (int64 tensors)."""
+    def slots_of(self, b, t: torch.Tensor) -> torch.Tensor:
+        """Cache slot of token t of sequence b (t an int64 tensor, b an int or an int64 tensor)."""
         if self.paged:
-            pages = self.block_table.to(torch.int64)[b, t // 64]
+            pages = self.block_table64[b, t // 64]
             return pages * 64 + t % 64
         return b * self.stride + t
 
@@ -115,8 +116,7 @@ class DeviceWorkload:
                 sgpu.kpe(k, seed, layer, b, t0)
                 pos = torch.arange(t0, t0 + n, dtype=torch.int32, device=dev)
                 mla_rope_yarn(k, pos)
-                slots = self.slots_of(torch.full((n,), b, dtype=torch.int64, device=dev),
-                                      pos.to(torch.int64))
+                slots = self.slots_of(b, torch.arange(t0, t0 + n, dtype=torch.int64, device=dev))
                 mla_cache_append(cache, c, k, slots, shape=self.shape)
                 del c, k
         w = torch.empty((8192, 512), dtype=torch.bfloat16, device=dev)
@@ -198,7 +198,7 @@ class DevicePrefill:
             sgpu.kpe(k, seed, layer, 0, t0)
             pos = torch.arange(t0, t0 + n, dtype=torch.int32, device=dev)
             mla_rope_yarn(k, pos)
-            mla_cache_append(cache, c, k, pos.to(torch.int64))
+            mla_cache_append(cache, c, k, torch.arange(t0, t0 + n, dtype=torch.int64, device=dev))
             del c, k
         w = torch.empty((8192, 512), dtype=torch.bfloat16, device=dev)
         sgpu.wkvb(w, seed, layer)

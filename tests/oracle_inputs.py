@@ -52,16 +52,6 @@ OUT_REL_L2 = 5e-3
 LSE_MAX_ABS = 5e-3
 
 
-# Chunked prefill (un-absorbed form): the expanded keys and values are rounded
-# to bf16 before the attention, errors the decode path does not have: a score
-# (0.145 * q_nope . dK over 128 dims, dK of rms 2^-9 / sqrt(3) relative) moves by
-# up to ~5.5e-3 for one visible token
-# (rms 1.8e-3), an output by half a bf16 ulp of V plus half an ulp of the
-# output (< 3.2e-2 for |V|, |out| < 8).  rel-L2 keeps the path's 5e-3.
-PREFILL_LSE_MAX_ABS = 1e-2
-PREFILL_OUT_MAX_ABS = 4e-2
-
-
 def compare(out_gpu, lse_gpu, out_ref, lse_ref, lse_tol=LSE_MAX_ABS, abs_tol=OUT_MAX_ABS):
     """Returns (max_abs, rel_l2, lse_max_abs); asserts the tolerances."""
     og = np.asarray(out_gpu, dtype=np.float64)

@@ -172,3 +172,71 @@ def test_read_probe_argument_errors():
 def test_read_probe_sink_size_matches_the_header():
     m = re.search(r"#define MLA_READ_PROBE_SINK_INTS (\d+)", open(HEADER).read())
     assert m and int(m.group(1)) == M.READ_PROBE_SINK_INTS
+
+
+def _header_define(name):
+    m = re.search(r"#define %s\s+\(?(\d+)u?(?:\s*<<\s*(\d+))?\)?" % name, open(HEADER).read())
+    assert m, name
+    return int(m.group(1)) << int(m.group(2) or 0)
+
+
+def test_fault_bits_match_the_header():
+    assert _header_define("MLA_FAULT_SLOT") == M.FAULT_SLOT
+    assert _header_define("MLA_FAULT_PAGE") == M.FAULT_PAGE
+    assert _header_define("MLA_FAULT_CTX_LEN") == M.FAULT_CTX_LEN
+    assert _header_define("MLA_FAULT_FP16_RANGE") == M.FAULT_FP16_RANGE
+
+
+def test_host_checks_of_lengths_and_pages():
+    # the range rules the kernels apply, run on host copies of the arrays
+    assert M.mla_check_decode_inputs([5, 64, 100], 1, 100) == 0
+    assert M.mla_check_decode_inputs([5, 101], 1, 100) == M.FAULT_CTX_LEN        # above max_ctx_len
+    assert M.mla_check_decode_inputs([1, 100], 2, 100) == M.FAULT_CTX_LEN        # below Sq
+    assert M.mla_check_decode_inputs([0], 1, 100) == M.FAULT_CTX_LEN
+    bt = [[3, 0], [1, 2]]
+    assert M.mla_check_decode_inputs([128, 65], 1, 128, bt, num_pages=4) == 0
+    assert M.mla_check_decode_inputs([128, 65], 1, 128, bt, num_pages=3) == M.FAULT_PAGE   # page 3 of 3
+    assert M.mla_check_decode_inputs([128, 64], 1, 128, [[0, 1], [2, -1]], num_pages=4) == 0  # entry unused
+    assert M.mla_check_decode_inputs([128, 65], 1, 128, [[0, 1], [2, -1]], num_pages=4) == M.FAULT_PAGE
+    # a clamped length decides which entries count: 200 tokens clamp to 128 (two pages)
+    assert M.mla_check_decode_inputs([200], 1, 128, [[0, 1]], num_pages=2) == M.FAULT_CTX_LEN
+    assert M.mla_check_decode_inputs([200], 1, 128, [[0, 9]], num_pages=2) == M.FAULT_CTX_LEN | M.FAULT_PAGE
+    with pytest.raises(M.MlaError):
+        M.mla_check_decode_inputs([10], 1, 128, [[0]], num_pages=2)               # table narrower than 128 tokens
+    assert M.mla_check_slot_mapping([0, 5, -1, 9], 10) == 0
+    assert M.mla_check_slot_mapping([0, 10], 10) == M.FAULT_SLOT
+    assert M.mla_check_slot_mapping([], 0) == 0
+
+
+def test_binding_checks_shapes_and_devices_before_the_gpu():
+    # shape, dtype and same-device checks of the Python binding come before
+    # the GPU check, so they run here on CPU tensors
+    import torch
+    B, Sq = 2, 1
+    q = torch.zeros(B, Sq, 32, 128, dtype=torch.bfloat16)
+    qp = torch.zeros(B, Sq, 32, 64, dtype=torch.bfloat16)
+    w = torch.zeros(8192, 512, dtype=torch.bfloat16)
+    lens = torch.full((B,), 64, dtype=torch.int32)
+    cache = torch.zeros(B, 64, 576, dtype=torch.bfloat16)
+    with pytest.raises(M.MlaError, match="out must have shape"):
+        M.mla_decode(q, qp, w, cache, lens, 64, out=torch.zeros(B, Sq, 32, 64, dtype=torch.bfloat16))
+    with pytest.raises(M.MlaError, match="lse must have shape"):
+        M.mla_decode(q, qp, w, cache, lens, 64, out=torch.zeros(B, Sq, 32, 128, dtype=torch.bfloat16),
+                     lse=torch.zeros(B, Sq, 16, dtype=torch.float32))
+    with pytest.raises(M.MlaError, match="ctx_lens must have shape"):
+        M.mla_decode(q, qp, w, cache, lens[:1], 64)
+    with pytest.raises(M.MlaError, match="q_pe must have shape"):
+        M.mla_decode(q, qp[:, :, :16].contiguous(), w, cache, lens, 64)
+    with pytest.raises(M.MlaError, match="is on meta"):
+        M.mla_decode(q, qp.to("meta"), w, cache, lens, 64)
+    with pytest.raises(M.MlaError, match="must be on the GPU"):
+        M.mla_decode(q, qp, w, cache, lens, 64, out=torch.zeros(B, Sq, 32, 128, dtype=torch.bfloat16))
+    Tq = 4
+    with pytest.raises(M.MlaError, match="out must have shape"):
+        M.mla_prefill(torch.zeros(Tq, 32, 128, dtype=torch.bfloat16), torch.zeros(Tq, 32, 64, dtype=torch.bfloat16),
+                      w, torch.zeros(64, 576, dtype=torch.bfloat16), 64,
+                      out=torch.zeros(Tq - 1, 32, 128, dtype=torch.bfloat16))
+    with pytest.raises(M.MlaError, match="lse must have shape"):
+        M.mla_prefill(torch.zeros(Tq, 32, 128, dtype=torch.bfloat16), torch.zeros(Tq, 32, 64, dtype=torch.bfloat16),
+                      w, torch.zeros(64, 576, dtype=torch.bfloat16), 64,
+                      out=torch.zeros(Tq, 32, 128, dtype=torch.bfloat16), lse=torch.zeros(Tq, dtype=torch.float32))

@@ -99,7 +99,7 @@ def test_fp8_config0_all_heads(chunk):
 
 @pytest.mark.parametrize("paged", [False, True])
 def test_fp8_fused_step_equals_separate_calls_and_is_deterministic(paged):
-    lens = (1, 65, 700, 130)
+    lens = (2, 65, 700, 130)      # the shortest context the contract allows: Sq tokens
     wl = Workload(99, "fp8-fused", len(lens), 2, 1, lens, True)
     res = []
     for fused in (True, False, True):
@@ -162,3 +162,33 @@ def test_fp8_fullsize_ctx32k():
     ref_o, ref_l = expected_fp8(wl.seed, 0, 32768, 1, 0, absorbed=True)
     s = compare(gpu_out(out[0]), lse[0].cpu().numpy(), ref_o, ref_l)
     print(f"fp8 32K: max_abs={s[0]:.3e} rel_l2={s[1]:.3e} lse={s[2]:.3e}")
+
+
+def _fp8_step(k):
+    wl = workload(k)
+    dw = DeviceWorkload(wl, kv_chunk=0, cache_dtype="fp8")   # the benchmark's launch configuration
+    li = dw.build_layer(0)
+    lse = torch.empty((dw.B, dw.Sq, 32), dtype=torch.float32, device=DEV)
+    out, lse = dw.step(li, lse=lse)
+    torch.cuda.synchronize()
+    go, gl = gpu_out(out), lse.cpu().numpy()
+    del li, dw
+    torch.cuda.empty_cache()
+    return wl, go, gl
+
+
+def test_fp8_fullsize_ctx256k_balanced():
+    wl, go, gl = _fp8_step(3)
+    ref_o, ref_l = expected_fp8(wl.seed, 0, wl.lens[0], 1, 0, absorbed=True)
+    s = compare(go[0], gl[0], ref_o, ref_l)
+    print(f"fp8 256K: max_abs={s[0]:.3e} rel_l2={s[1]:.3e} lse={s[2]:.3e}", flush=True)
+
+
+def test_fp8_fullsize_verify_b32_sq2():
+    wl, go, gl = _fp8_step(4)
+    lens = np.array(wl.lens)
+    for b in sorted({int(lens.argmin()), int(lens.argmax()), 5, 17}):
+        ref_o, ref_l = expected_fp8(wl.seed, 0, wl.lens[b], wl.sq, b, absorbed=True)
+        s = compare(go[b], gl[b], ref_o, ref_l)
+        print(f"fp8 verify 32x2 seq {b} (L={wl.lens[b]}): max_abs={s[0]:.3e} rel_l2={s[1]:.3e} lse={s[2]:.3e}",
+              flush=True)
