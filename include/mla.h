@@ -20,8 +20,9 @@
  *  - bf16 is bfloat16 (1-8-7), passed as raw 16-bit values.
  *  - The caller owns every buffer.  The library allocates nothing, keeps no
  *    pointer after a call returns and holds no state between calls, except
- *    a static fault word per device (below) and the opt-in kernel timing at
- *    the end of this header.
+ *    two static device arrays per device (the fault word below and the
+ *    scratch of mla_decode_step_paged_noalloc) and the opt-in kernel timing
+ *    at the end of this header.
  *  - All work is enqueued on `stream` (a hipStream_t; NULL = the default
  *    stream).  MLA_OK means "enqueued"; device faults show up at the
  *    caller's next synchronisation.  No call synchronises the host.
@@ -59,6 +60,8 @@ typedef int32_t mla_status;
 #define MLA_ERR_WORKSPACE    5   /* workspace too small                              */
 #define MLA_ERR_DEVICE       6   /* a HIP runtime call failed                        */
 #define MLA_ERR_UNSUPPORTED  7   /* a valid request this library does not implement  */
+#define MLA_ERR_SCRATCH      8   /* the no-allocation entry point needs more than its
+                                    static scratch (MLA_STATIC_SCRATCH_BYTES)          */
 
 /* Bits of the per-device fault word (mla_device_faults). */
 #define MLA_FAULT_SLOT        1u /* a slot >= num_slots: the row was not written          */
@@ -286,6 +289,25 @@ mla_status mla_prefill_workspace_size(const mla_shape* shape /* host */, int32_t
 mla_status mla_prefill(const mla_shape* shape /* host */, const void* q_nope, const void* q_pe,
                        const void* w_kv_b, const void* cache, int32_t ctx_len, int32_t Tq, void* out,
                        float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* mla_decode_step_paged for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops that forbid allocation): the same
+ * arguments without the workspace, which is taken from a static device
+ * array of MLA_STATIC_SCRATCH_BYTES that the library holds on every device it
+ * runs on until the process ends.  The call allocates nothing.  A request
+ * whose workspace (mla_decode_workspace_size) exceeds that size returns
+ * MLA_ERR_SCRATCH and enqueues nothing.  All calls on one device share its
+ * array: calls that may overlap on one device (different streams, or other
+ * host threads) race and must be serialised by the caller.  The first call on
+ * a device (or any other call of this library there) looks up the array's
+ * device address, so it must not be the first library call inside a capture. */
+#define MLA_STATIC_SCRATCH_BYTES (64u << 20)
+mla_status mla_decode_step_paged_noalloc(const mla_shape* shape /* host */, const mla_rope_params* rope /* host */,
+                                         const void* q_nope, const void* q_pe, const void* c_kv_new, int64_t ld_c,
+                                         const void* k_pe_new, int64_t ld_k, const void* w_kv_b, void* cache,
+                                         int64_t num_pages, const int32_t* block_table, int32_t max_pages_per_seq,
+                                         const int32_t* ctx_lens, int32_t max_ctx_len, int32_t B, int32_t Sq,
+                                         int32_t kv_chunk, void* out, float* lse, void* stream);
 
 /* Reads the fault word of the current device (MLA_FAULT_* bits set by any
  * kernel of this library since the word was last cleared) into *faults

@@ -22,7 +22,7 @@ __all__ = [
     "mla_decode_workspace_size", "mla_decode_auto_chunk", "mla_status_string",
     "mla_prefill", "mla_prefill_workspace_size",
     "mla_timing_enable", "mla_timing_collect", "mla_timing_disable", "mla_read_probe", "READ_PROBE_SINK_INTS",
-    "mla_device_faults", "mla_check_decode_inputs",
+    "mla_decode_step_paged_noalloc", "STATIC_SCRATCH_BYTES", "mla_device_faults", "mla_check_decode_inputs",
     "mla_check_slot_mapping", "FAULT_SLOT", "FAULT_PAGE", "FAULT_CTX_LEN", "FAULT_FP16_RANGE",
 ]
 
@@ -43,6 +43,7 @@ FAULT_SLOT = 1          # MLA_FAULT_* bits of the device fault word
 FAULT_PAGE = 2
 FAULT_CTX_LEN = 4
 FAULT_FP16_RANGE = 8
+STATIC_SCRATCH_BYTES = 64 << 20   # MLA_STATIC_SCRATCH_BYTES
 CACHE_FP8_E4M3 = 1      # rows of 656 bytes: [512 E4M3 codes | 4 fp32 scales | 64 bf16 rope key]
 
 
@@ -90,6 +91,9 @@ def library() -> ctypes.CDLL:
             "mla_timing_collect": [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I32)],
             "mla_timing_disable": [],
             "mla_read_probe": [_P, ctypes.c_size_t, _P, _P],
+            "mla_decode_step_paged_noalloc": [ctypes.POINTER(MlaShape), ctypes.POINTER(MlaRopeParams), _P, _P, _P,
+                                              _I64, _P, _I64, _P, _P, _I64, _P, _I32, _P, _I32, _I32, _I32, _I32,
+                                              _P, _P, _P],
             "mla_device_faults": [ctypes.POINTER(ctypes.c_uint32), _I32],
             "mla_check_decode_inputs": [_I32, _I32, _I32, _P, _P, _I32, _I64, ctypes.POINTER(ctypes.c_uint32)],
             "mla_check_slot_mapping": [_P, _I64, _I64, ctypes.POINTER(ctypes.c_uint32)],
@@ -234,7 +238,7 @@ def mla_decode_auto_chunk(B: int, Sq: int, max_ctx_len: int) -> int:
 
 
 def _decode_io(q_nope, q_pe, w_kv_b, ctx_lens, out, lse, workspace, B, Sq, max_ctx_len, kv_chunk, shape,
-               cache=None, block_table=None):
+               cache=None, block_table=None, need_workspace=True):
     _need(q_nope, torch.bfloat16, "q_nope", shape=(B, Sq, 32, 128), gpu=False)
     dev = q_nope.device
     _need(q_pe, torch.bfloat16, "q_pe", shape=(B, Sq, 32, 64), device=dev, gpu=False)
@@ -252,10 +256,11 @@ def _decode_io(q_nope, q_pe, w_kv_b, ctx_lens, out, lse, workspace, B, Sq, max_c
     if out is None:
         out = torch.empty((B, Sq, 32, 128), dtype=torch.bfloat16, device=dev)
     s = shape if shape is not None else default_shape()
-    need = mla_decode_workspace_size(B, Sq, max_ctx_len, kv_chunk, s)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    _need(workspace, torch.uint8, "workspace", device=dev)
+    if need_workspace:
+        need = mla_decode_workspace_size(B, Sq, max_ctx_len, kv_chunk, s)
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        _need(workspace, torch.uint8, "workspace", device=dev)
     return out, lse, workspace, s
 
 
@@ -411,6 +416,39 @@ def mla_read_probe(buf: torch.Tensor, sink: torch.Tensor, stream=None):
         raise MlaError(f"sink: {READ_PROBE_SINK_INTS} int32 elements required")
     _check(library().mla_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)),
            "mla_read_probe")
+
+
+def mla_decode_step_paged_noalloc(q_nope, q_pe, c_kv_new, k_pe_new, w_kv_b, cache, block_table, ctx_lens,
+                                  max_ctx_len: int, out, lse=None, kv_chunk: int = 0,
+                                  rope: MlaRopeParams | None = None, shape: MlaShape | None = None, stream=None):
+    """mla_decode_step on a paged cache with no workspace argument and no allocation: the library
+    takes the workspace from its static device scratch (STATIC_SCRATCH_BYTES); ``out`` (and
+    ``lse`` if wanted) must be given.  Calls that overlap on one device race on that scratch."""
+    if out is None:
+        raise MlaError("out must be given: the no-allocation entry point allocates nothing")
+    width = _check_cache(cache, shape if shape is not None else default_shape())
+    B, Sq = q_nope.shape[0], q_nope.shape[1]
+    for t, name, w in ((c_kv_new, "c_kv_new", 512), (k_pe_new, "k_pe_new", 64)):
+        if t.dtype != torch.bfloat16 or t.device.type != "cuda" or t.dim() != 2 or t.stride(1) != 1:
+            raise MlaError(f"{name} must be a 2-D bf16 GPU tensor with unit column stride")
+        if t.shape[0] != B * Sq or t.shape[1] < w:
+            raise MlaError(f"{name} must have B*Sq rows of at least {w} values")
+        if t.device != q_nope.device:
+            raise MlaError(f"{name} is on {t.device}, q_nope on {q_nope.device}")
+    _need(block_table, torch.int32, "block_table")
+    if cache.dim() != 3 or cache.shape[1] != 64:
+        raise MlaError(f"cache must be [num_pages, 64, {width}]")
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise MlaError("block_table must be [B, max_pages_per_seq]")
+    out, lse, _, s = _decode_io(q_nope, q_pe, w_kv_b, ctx_lens, out, lse, None, B, Sq, max_ctx_len, kv_chunk,
+                                shape, cache=cache, block_table=block_table, need_workspace=False)
+    r = rope if rope is not None else default_rope()
+    _check(library().mla_decode_step_paged_noalloc(
+        ctypes.byref(s), ctypes.byref(r), _ptr(q_nope), _ptr(q_pe), _ptr(c_kv_new), c_kv_new.stride(0),
+        _ptr(k_pe_new), k_pe_new.stride(0), _ptr(w_kv_b), _ptr(cache), cache.shape[0], _ptr(block_table),
+        block_table.shape[1], _ptr(ctx_lens), max_ctx_len, B, Sq, kv_chunk, _ptr(out), _ptr(lse), _stream(stream)),
+        "mla_decode_step_paged_noalloc")
+    return out, lse
 
 
 def mla_device_faults(clear: bool = False) -> int:

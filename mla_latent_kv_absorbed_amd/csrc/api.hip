@@ -15,16 +15,22 @@ using namespace mla;
 // meet an index outside its range (mla_device_faults reads and clears it).
 __device__ uint32_t g_fault_word = 0;
 
+// Scratch of mla_decode_step_paged_noalloc, in place of a caller's workspace:
+// each device the library runs on holds its own copy until the process ends.
+constexpr size_t kStaticScratchBytes = (size_t)MLA_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
 namespace {
 
-// Device address of the fault word, looked up once per device (with that
-// device current) by hipGetSymbolAddress: in host code its name is a
-// host-side stand-in, never a device address.
+// Device addresses of the two arrays above, looked up once per device (with
+// that device current) by hipGetSymbolAddress: in host code the arrays' names
+// are host-side stand-ins, never device addresses.
 constexpr int kMaxDevices = 64;
 struct DeviceSymbols {
   std::once_flag once;
   hipError_t err = hipSuccess;
   uint32_t* faults = nullptr;
+  uint8_t* scratch = nullptr;
 };
 DeviceSymbols g_symbols[kMaxDevices];
 
@@ -34,6 +40,7 @@ const DeviceSymbols* device_symbols() {
   DeviceSymbols& d = g_symbols[dev];
   std::call_once(d.once, [&d] {
     d.err = hipGetSymbolAddress((void**)&d.faults, HIP_SYMBOL(g_fault_word));
+    if (d.err == hipSuccess) d.err = hipGetSymbolAddress((void**)&d.scratch, HIP_SYMBOL(scratch));
   });
   return d.err == hipSuccess ? &d : nullptr;
 }
@@ -136,6 +143,10 @@ void yarn_frequencies(const mla_rope_params& p, double* out) {
   }
 }
 
+// Workspace argument meaning "use the device's static scratch" (the
+// no-allocation entry point); never a valid device address.
+void* const kUseStaticScratch = (void*)(uintptr_t)1;
+
 // Optional fused front end of a decode call: rotate q_pe (and the new
 // tokens' rope rows) at p = L_b - Sq + j and write the new tokens' cache rows.
 struct StepInputs {
@@ -175,8 +186,8 @@ mla_status decode_common(const mla_shape* shape, const StepInputs& step, const v
     if (stride_tokens < max_ctx_len) return MLA_ERR_RANGE;
   }
   if (kv_chunk < 0 || kv_chunk % kPage != 0) return MLA_ERR_RANGE;
-  if (!aligned16(q_nope) || !aligned16(q_pe) || !aligned16(w_kv_b) || !aligned16(cache) ||
-      !aligned16(out) || ((uintptr_t)workspace & 255u) != 0)
+  if (!aligned16(q_nope) || !aligned16(q_pe) || !aligned16(w_kv_b) || !aligned16(cache) || !aligned16(out) ||
+      (workspace != kUseStaticScratch && ((uintptr_t)workspace & 255u) != 0))
     return MLA_ERR_ALIGN;
   if (lse != nullptr && ((uintptr_t)lse & 3u) != 0) return MLA_ERR_ALIGN;
   if (step.rope != nullptr) {
@@ -193,9 +204,15 @@ mla_status decode_common(const mla_shape* shape, const StepInputs& step, const v
   // workgroups times 256 threads must fit in 32 bits
   if (((segs + kXcds - 1) / kXcds) * kXcds * groups > (int64_t)(0xFFFFFFFFu / 256)) return MLA_ERR_RANGE;
   const WorkspaceLayout wl = workspace_layout(B, Sq, (int)segs);
-  if (workspace_bytes < wl.total) return MLA_ERR_WORKSPACE;
+  const bool use_static = workspace == kUseStaticScratch;
+  if (use_static) {
+    if (wl.total > kStaticScratchBytes) return MLA_ERR_SCRATCH;
+  } else if (workspace_bytes < wl.total) {
+    return MLA_ERR_WORKSPACE;
+  }
   const DeviceSymbols* sym = device_symbols();
   if (sym == nullptr) return MLA_ERR_DEVICE;
+  if (use_static) workspace = sym->scratch;
 
   uint8_t* ws = (uint8_t*)workspace;
   uint16_t* qabs = (uint16_t*)(ws + wl.qabs);
@@ -323,6 +340,8 @@ const char* mla_status_string(mla_status s) {
     case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace too small";
     case MLA_ERR_DEVICE: return "MLA_ERR_DEVICE: a HIP runtime call failed";
     case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: not implemented";
+    case MLA_ERR_SCRATCH:
+      return "MLA_ERR_SCRATCH: the call needs more scratch than the static buffer of the no-allocation entry point";
     default: return "MLA_ERR_UNKNOWN";
   }
 }
@@ -463,6 +482,18 @@ mla_status mla_decode_workspace_size(const mla_shape* shape, int32_t B, int32_t 
   if (segs > 0x7FFFFFFF) return MLA_ERR_RANGE;
   *bytes = workspace_layout(B, Sq, (int)segs).total;
   return MLA_OK;
+}
+
+mla_status mla_decode_step_paged_noalloc(const mla_shape* shape, const mla_rope_params* rope, const void* q_nope,
+                                         const void* q_pe, const void* c_kv_new, int64_t ld_c, const void* k_pe_new,
+                                         int64_t ld_k, const void* w_kv_b, void* cache, int64_t num_pages,
+                                         const int32_t* block_table, int32_t max_pages_per_seq,
+                                         const int32_t* ctx_lens, int32_t max_ctx_len, int32_t B, int32_t Sq,
+                                         int32_t kv_chunk, void* out, float* lse, void* stream) {
+  if (rope == nullptr) return MLA_ERR_NULL;
+  return decode_common(shape, StepInputs{rope, c_kv_new, ld_c, k_pe_new, ld_k}, q_nope, q_pe, w_kv_b, cache,
+                       0, num_pages, block_table, max_pages_per_seq, ctx_lens, max_ctx_len, B, Sq, kv_chunk,
+                       out, lse, kUseStaticScratch, 0, stream, true);
 }
 
 mla_status mla_device_faults(uint32_t* faults, int32_t clear) {

@@ -40,8 +40,9 @@ def test_default_shape_and_scale():
 
 
 def test_status_strings():
-    for code in range(8):
+    for code in range(9):
         assert M.mla_status_string(code).startswith("MLA_")
+    assert "scratch" in M.mla_status_string(8)
 
 
 def _decode(lib, shape, **kw):
@@ -180,11 +181,12 @@ def _header_define(name):
     return int(m.group(1)) << int(m.group(2) or 0)
 
 
-def test_fault_bits_match_the_header():
+def test_fault_bits_and_static_scratch_size_match_the_header():
     assert _header_define("MLA_FAULT_SLOT") == M.FAULT_SLOT
     assert _header_define("MLA_FAULT_PAGE") == M.FAULT_PAGE
     assert _header_define("MLA_FAULT_CTX_LEN") == M.FAULT_CTX_LEN
     assert _header_define("MLA_FAULT_FP16_RANGE") == M.FAULT_FP16_RANGE
+    assert _header_define("MLA_STATIC_SCRATCH_BYTES") == M.STATIC_SCRATCH_BYTES == 64 << 20
 
 
 def test_host_checks_of_lengths_and_pages():
@@ -206,6 +208,30 @@ def test_host_checks_of_lengths_and_pages():
     assert M.mla_check_slot_mapping([0, 5, -1, 9], 10) == 0
     assert M.mla_check_slot_mapping([0, 10], 10) == M.FAULT_SLOT
     assert M.mla_check_slot_mapping([], 0) == 0
+
+
+def test_noalloc_entry_point_argument_errors():
+    lib = M.library()
+    s = M.default_shape()
+    r = M.default_rope()
+
+    def call(**kw):
+        a = dict(pages=100, bt=FAKE, maxpages=16, maxctx=1024, B=1, Sq=1, chunk=0, out=FAKE)
+        a.update(kw)
+        return lib.mla_decode_step_paged_noalloc(ctypes.byref(s), ctypes.byref(r), FAKE, FAKE, FAKE, 512, FAKE, 64,
+                                                 FAKE, FAKE, a["pages"], a["bt"], a["maxpages"], FAKE, a["maxctx"],
+                                                 a["B"], a["Sq"], a["chunk"], a["out"], None, None)
+    assert call(out=None) == ERR_NULL
+    assert call(bt=None) == ERR_NULL
+    assert call(maxpages=15) == ERR_RANGE
+    assert call(B=0) == OK
+    # a workspace beyond the static scratch: 4096 sequences x 16 query tokens
+    # need more than 64 MiB of query rows alone
+    assert call(B=4095, Sq=16, maxctx=1024) == 8                  # MLA_ERR_SCRATCH
+    assert M.mla_decode_workspace_size(4095, 16, 1024) > M.STATIC_SCRATCH_BYTES
+    # fixed 64-token splits over long contexts: many segments
+    assert call(B=16, maxctx=65536, maxpages=1024, chunk=64) == 8
+    assert M.mla_decode_workspace_size(16, 1, 65536, kv_chunk=64) > M.STATIC_SCRATCH_BYTES
 
 
 def test_binding_checks_shapes_and_devices_before_the_gpu():
