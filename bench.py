@@ -354,7 +354,11 @@ def cpu_baseline(k: int, budget_s: float = 15.0):
     step_s = per_layer * wl.layers * wl.batch
     abs_step_s = spent_abs / layers * wl.layers * wl.batch
     threads = sum(p.get("num_threads", 0) for p in threadpoolctl.threadpool_info() if p.get("user_api") == "blas")
-    return {"value": wl.batch * Sq / step_s, "unit": "tokens/s", "cores": threads or os.cpu_count(),
+    try:
+        host_cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        host_cores = os.cpu_count()
+    return {"value": wl.batch * Sq / step_s, "unit": "tokens/s", "cores": host_cores, "blas_threads": threads,
             "kind": "oracle",
             "sample": (f"un-absorbed fp64 oracle, sequence 0 of {wl.name}, all 32 heads over the full {L}-token "
                        f"context, layers 0..{layers - 1}: {spent:.1f} s; {per_layer:.2f} s per layer scaled by "
@@ -419,6 +423,79 @@ def summarize_counters(fetch_csv: str, write_csv: str, copy_bytes: int, workload
     print(json.dumps(res, indent=1))
 
 
+def counters_only(k: int, steps: int, layers: int, cache_dtype: str, kv_chunk):
+    """A short run for hardware-counter passes: `layers` layers of workload k are built, then
+    `steps` eager decode steps run over them (no graph, no timing).  The build needs few
+    dispatches (the slot tensors are made once per chunk with no dtype casts), and a counter
+    pass restricted to the decode kernels by name collects nothing while it runs."""
+    import torch
+    from mla_latent_kv_absorbed_amd.workload import DeviceWorkload
+    from synth.configs import workload
+
+    wl = workload(k)
+    dw = DeviceWorkload(wl, kv_chunk=kv_chunk, cache_dtype=cache_dtype)
+    lis = [dw.build_layer(l) for l in range(layers)]
+    torch.cuda.synchronize()
+    log(f"[counters] built {layers} layer(s) of {wl.name} ({cache_dtype}, chunk {dw.chunk_used})")
+    out = torch.empty((dw.B, dw.Sq, 32, 128), dtype=torch.bfloat16, device=dw.dev)
+    lse = torch.empty((dw.B, dw.Sq, 32), dtype=torch.float32, device=dw.dev)
+    for s in range(steps):
+        for li in lis:
+            dw.step(li, out=out, lse=lse)
+        torch.cuda.synchronize()
+        log(f"[counters] step {s + 1}/{steps} done")
+    print(json.dumps({"counters_run": wl.name, "cache_dtype": cache_dtype, "layers": layers, "steps": steps,
+                      "kv_chunk": dw.chunk_used, "tokens": sum(dw.lens), "query_tokens": dw.Sq,
+                      "visible_token_queries": sum(L * dw.Sq - dw.Sq * (dw.Sq - 1) // 2 for L in dw.lens)}),
+          flush=True)
+
+
+def _short_kernel(name: str) -> str:
+    n = name.replace("void ", "").replace("mla::(anonymous namespace)::", "")
+    return n.split("(")[0]
+
+
+def summarize_pmc(paths, title: str, command: str):
+    """Markdown table of rocprofv3 --pmc CSVs of one workload (several passes may be given): per
+    kernel, the mean of each counter per dispatch, and where the counters are present the MFMA
+    busy share SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x GRBM_GUI_ACTIVE / XCDs), GRBM_GUI_ACTIVE being
+    summed over the XCDs and the busy cycles over the SIMDs."""
+    import csv
+    import statistics
+    rows, dur = {}, {}
+    simds, xccs = None, None
+    for path in paths:
+        for (cn, kn), vals in _counter_rows(path).items():
+            rows.setdefault(_short_kernel(kn), {}).setdefault(cn, []).extend(vals)
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                dur.setdefault(_short_kernel(r["Kernel_Name"]), []).append(
+                    (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        info = os.path.join(os.path.dirname(path), "run_agent_info.csv")
+        if os.path.exists(info):
+            with open(info) as fh:
+                for r in csv.DictReader(fh):
+                    if r.get("Name", "").startswith("gfx"):
+                        simds, xccs = int(r["Simd_Count"]), int(r["Num_Xcc"])
+    lines = [f"# {title}", "", "Commands (repository root, one MI355X; one counter pass per run):", ""]
+    lines += ["    " + c for c in command.split(" ;; ")]
+    lines += ["", f"Device: {simds} SIMDs, {xccs} XCDs (run_agent_info.csv).", ""]
+    counters = sorted({cn for d in rows.values() for cn in d})
+    lines.append("| kernel | dispatches | median us | " + " | ".join(counters) + " | MFMA busy |")
+    lines.append("|---|---:|---:|" + "---:|" * len(counters) + "---:|")
+    for kn in sorted(rows):
+        d = rows[kn]
+        n = max(len(v) for v in d.values())
+        cells = [f"{statistics.mean(d[c]):,.0f}" if c in d else "" for c in counters]
+        busy = ""
+        if simds and xccs and "SQ_VALU_MFMA_BUSY_CYCLES" in d and "GRBM_GUI_ACTIVE" in d:
+            cyc = statistics.mean(d["GRBM_GUI_ACTIVE"]) / xccs
+            busy = f"{statistics.mean(d['SQ_VALU_MFMA_BUSY_CYCLES']) / (simds * cyc):.1%}"
+        lines.append(f"| {kn} | {n // max(1, len(paths))} | {statistics.median(dur[kn]):.1f} | " + " | ".join(cells)
+                     + f" | {busy} |")
+    print("\n".join(lines))
+
+
 def copy_calibration(nbytes: int):
     """A plain device-to-device copy of nbytes, three times (a known-size reference for counters)."""
     import torch
@@ -455,7 +532,18 @@ def main():
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/splitkv_decode_counters.json from two rocprofv3 --pmc runs and exit")
     ap.add_argument("--counters-command", default="", help="command line recorded with --summarize-counters")
+    ap.add_argument("--counters-only", action="store_true",
+                    help="build --counter-layers layers of --config and run --steps eager decode steps, nothing else "
+                         "(for hardware-counter passes)")
+    ap.add_argument("--counter-layers", type=int, default=1)
+    ap.add_argument("--cache-dtype", default="bf16", choices=("bf16", "fp8"), help="with --counters-only")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="CSV",
+                    help="print a markdown table (mean per dispatch, per kernel and counter) of rocprofv3 --pmc CSVs")
+    ap.add_argument("--pmc-title", default="rocprofv3 counters")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc, args.pmc_title, args.counters_command)
+        return
     if args.summarize_counters:
         from synth.configs import workload
         summarize_counters(args.summarize_counters[0], args.summarize_counters[1],
@@ -468,6 +556,9 @@ def main():
 
     import torch
     torch.cuda.init()
+    if args.counters_only:
+        counters_only(args.config, args.steps, args.counter_layers, args.cache_dtype, args.kv_chunk)
+        return
     if args.library_reference:
         print(json.dumps({"library_reference": library_reference()}), flush=True)
         return

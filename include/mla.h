@@ -178,7 +178,12 @@ mla_status mla_cache_append(const mla_shape* shape /* host */, void* cache, int6
  *   max_ctx_len  host upper bound of ctx_lens, <= stride_tokens
  *   kv_chunk     tokens per split, a multiple of 64, or 0 to let the
  *                library choose (splits sized from the actual ctx_lens on the
- *                device, about one workgroup per compute unit)
+ *                device, about one workgroup per compute unit).  When the
+ *                chunks of a call are fewer than the device's compute units
+ *                (per query group), each chunk is cut into 2^k equal
+ *                sub-splits of at least 128 tokens, within that count; the
+ *                LSE combine over the sub-splits equals combining each
+ *                chunk's sub-splits and then the chunks.
  *   out          bf16 [B][Sq][32][128]
  *   lse          fp32 [B][Sq][32] natural-log sum of exp(s_t), or NULL
  *   workspace    device scratch of mla_decode_workspace_size() bytes,

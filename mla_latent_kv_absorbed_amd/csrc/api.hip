@@ -91,12 +91,13 @@ int compute_units() {
 }
 
 // Upper bound of the number of segments (splits) of a call: with a fixed
-// kv_chunk every sequence has at most ceil(max_ctx_len / kv_chunk); the
-// balanced schedule (kv_chunk = 0) chooses c >= ceil(T / target) tiles, so
-// sum_b ceil(tiles_b / c) <= T / c + B <= target + B, or else c = the longest
-// sequence's tiles, which makes every sequence one split (B segments).
+// kv_chunk every sequence has at most ceil(max_ctx_len / kv_chunk) chunks,
+// and chunks are sub-split only while the segments stay within the target;
+// the balanced schedule (kv_chunk = 0) chooses c >= ceil(T / target) tiles,
+// so sum_b ceil(tiles_b / c) <= T / c + B <= target + B, or else c = the
+// longest sequence's tiles, which makes every sequence one split (B segments).
 int64_t max_segments(int B, int max_ctx, int kv_chunk, int target) {
-  if (kv_chunk > 0) return (int64_t)B * ((max_ctx + kv_chunk - 1) / kv_chunk);
+  if (kv_chunk > 0) return std::max<int64_t>((int64_t)B * ((max_ctx + kv_chunk - 1) / kv_chunk), target);
   return (int64_t)target + B;
 }
 
@@ -230,6 +231,7 @@ mla_status decode_common(const mla_shape* shape, const StepInputs& step, const v
   pp.qres = qres;
   pp.zero_row = zero_row;
   pp.rows = rows;
+  pp.rows_per_wg = prep_rows_per_wg(rows);
   pp.Sq = Sq;
   pp.ctx_lens = ctx_lens;
   pp.max_ctx_len = max_ctx_len;
@@ -289,6 +291,7 @@ mla_status decode_common(const mla_shape* shape, const StepInputs& step, const v
   cp.max_segs = (int)segs;
   cp.Sq = Sq;
   cp.hrows = rows * kHeads;
+  cp.rows_per_wg = combine_rows_per_wg(rows);
   cp.w_kv_b = (const uint16_t*)w_kv_b;
   cp.qres = qres;
   cp.scale_log2 = scale_log2;

@@ -88,8 +88,9 @@ __device__ __forceinline__ int block_scan256(int v, int* red4, int* total) {
 }
 
 // The split schedule of one call, built by one 256-thread workgroup: splits
-// of c tiles, c fixed or chosen here so that the segments of all sequences
-// number at most target_segs where the lengths allow; then the first
+// of c tiles, c fixed (and sub-split when the chunks leave compute units
+// idle) or chosen here so that the segments of all sequences number at most
+// target_segs where the lengths allow; then the first
 // segment of every sequence and the segment descriptors {b, first token, end
 // token, L_b} in sequence order.  Up to kSchedLds sequences, the lengths and
 // segment starts stay in LDS (`lds`, 2 * kSchedLds + 1 ints) and each
@@ -117,7 +118,21 @@ __device__ void build_schedule(const PrepParams& p, int* lds) {
     __syncthreads();
   }
   int c = p.fixed_tiles;
-  if (c <= 0) {
+  if (c > 0) {
+    // A fixed chunk that leaves compute units idle (fewer chunks than the
+    // target) has every chunk cut into k equal sub-splits, k a power of two
+    // dividing c, each of at least kMinTilesPerSplit tiles, while the
+    // segments stay within the target.  The sub-split boundaries include
+    // every chunk boundary, and the combine's LSE merge over the sub-splits
+    // equals merging each chunk's sub-splits first and then the chunks.
+    int n = 0;
+    for (int b = t; b < p.B; b += 256) n += ((len_of(b) + kPage - 1) / kPage + c - 1) / c;
+    n = block_sum256(n, red4);
+    while (c % 2 == 0 && c / 2 >= kMinTilesPerSplit && 2LL * n <= p.target_segs) {
+      c /= 2;
+      n *= 2;   // an upper bound of the segments with the halved split
+    }
+  } else {
     int tsum = 0, tmax = 1;
     for (int b = t; b < p.B; b += 256) {
       const int tb = (len_of(b) + kPage - 1) / kPage;
@@ -177,13 +192,14 @@ __device__ void build_schedule(const PrepParams& p, int* lds) {
 
 // ---------------------------------------------------------------------------
 // Preparation of one decode call.  Grid (8 latent blocks of 64 + 1, 32
-// heads, query-row blocks of 4); row r = b*Sq + j.
+// heads, blocks of rows_per_wg query rows, 4 or 16); row r = b*Sq + j.
 //  * Absorption: Q_abs[r][h][0:512] = bf16(W_UK[h]^T q_nope[r][h]) and the
 //    fp32 residual q_lat - bf16(q_lat) (for the first-order LSE correction).
 //    W_UK[h] = w_kv_b rows [h*256, h*256 + 128).  Thread (ng, c8) loads
-//    W_UK[h][4ng .. 4ng+3][c8*8 .. c8*8+7] as four 16-byte loads, forms the
-//    partial dot products of the block's 4 rows over those 4 nope dims, and
-//    the 32 partials of each output are summed through LDS in a fixed order.
+//    W_UK[h][4ng .. 4ng+3][c8*8 .. c8*8+7] as four 16-byte loads once, and
+//    in rounds of 4 rows forms the partial dot products of the round's rows
+//    over those 4 nope dims; the 32 partials of each output are summed
+//    through LDS in a fixed order.  Up to 16 rows share one load of W_UK.
 //  * Rope part: Q_abs[r][h][512:576] = q_pe[r][h], rotated at the query's
 //    position p = L_b - Sq + j when `rotate` is set (latent block 0).
 //  * New tokens (when c_new is given): cache row of token p of sequence b =
@@ -192,59 +208,14 @@ __device__ void build_schedule(const PrepParams& p, int* lds) {
 //  * Workgroup (8, 0, 0) zeroes the decode kernel's zero row and builds the
 //    split schedule (the other workgroups of that column exit at once).
 // ---------------------------------------------------------------------------
-constexpr int kPrepRows = 4;
+constexpr int kPrepRows = 4;        // rows of one reduction round
+constexpr int kPrepRowsMax = 16;    // rows of one workgroup (its W_UK block is loaded once)
 
-__global__ void __launch_bounds__(256) prep_query(PrepParams p) {
-  __shared__ float red[kPrepRows][32][64];
-  static_assert(sizeof(red) >= (2 * kSchedLds + 1) * sizeof(int), "schedule scratch");
-  const int cblk = blockIdx.x;
-  const int h = blockIdx.y;
-  const int r0 = blockIdx.z * kPrepRows;
-  const int t = threadIdx.x;
-  if (cblk == kLatent / 64) {           // the extra column: schedule and zero row
-    if (h == 0 && r0 == 0) {
-      if (t < kChunksPerRow) ((uint4*)p.zero_row)[t] = make_uint4(0, 0, 0, 0);
-      build_schedule(p, (int*)&red[0][0][0]);
-    }
-    return;
-  }
-  const int c8 = t & 7, ng = t >> 3;
-  const uint16_t* wk = p.w_kv_b + ((size_t)h * kWRowsPerHead + 4 * ng) * kLatent + cblk * 64 + c8 * 8;
-  uint4 w[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) w[k] = *(const uint4*)(wk + (size_t)k * kLatent);
-  uint2 q[kPrepRows];
-#pragma unroll
-  for (int rr = 0; rr < kPrepRows; ++rr) {
-    const int r = min(r0 + rr, p.rows - 1);
-    q[rr] = *(const uint2*)(p.q_nope + ((size_t)r * kHeads + h) * kNope + 4 * ng);
-  }
-#pragma unroll
-  for (int rr = 0; rr < kPrepRows; ++rr) {
-    const float qv[4] = {__uint_as_float(q[rr].x << 16), __uint_as_float(q[rr].x & 0xFFFF0000u),
-                         __uint_as_float(q[rr].y << 16), __uint_as_float(q[rr].y & 0xFFFF0000u)};
-    float acc[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t wd[4] = {w[k].x, w[k].y, w[k].z, w[k].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[2 * e] = fmaf(qv[k], __uint_as_float(wd[e] << 16), acc[2 * e]);
-        acc[2 * e + 1] = fmaf(qv[k], __uint_as_float(wd[e] & 0xFFFF0000u), acc[2 * e + 1]);
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) red[rr][ng][c8 * 8 + e] = acc[e];
-  }
-  __syncthreads();
-  const int rr = t >> 6, col = t & 63;
-  const int r = r0 + rr;
-  if (r >= p.rows) return;
-  float acc = 0.f;
-#pragma unroll
-  for (int k = 0; k < 32; ++k) acc += red[rr][k][col];
+// The outputs of query row r for head h and latent block cblk, from this
+// thread's column `col` of the absorbed query (acc, fp32): Q_abs and the
+// residual, the rope part, and the new token's cache row.  One wave per row,
+// so every branch below is uniform across a wave.
+__device__ __forceinline__ void prep_row(const PrepParams& p, int r, int h, int cblk, int col, float acc) {
   const size_t hrow = (size_t)r * kHeads + h;
   uint16_t* dst = p.qabs + hrow * kRow;
   const uint16_t qb = f32_to_bf16(acc);
@@ -334,36 +305,103 @@ __global__ void __launch_bounds__(256) prep_query(PrepParams p) {
   }
 }
 
+__global__ void __launch_bounds__(256) prep_query(PrepParams p) {
+  __shared__ float red[kPrepRows][32][64];
+  static_assert(sizeof(red) >= (2 * kSchedLds + 1) * sizeof(int), "schedule scratch");
+  const int cblk = blockIdx.x;
+  const int h = blockIdx.y;
+  const int r0 = blockIdx.z * p.rows_per_wg;
+  const int t = threadIdx.x;
+  if (cblk == kLatent / 64) {           // the extra column: schedule and zero row
+    if (h == 0 && r0 == 0) {
+      if (t < kChunksPerRow) ((uint4*)p.zero_row)[t] = make_uint4(0, 0, 0, 0);
+      build_schedule(p, (int*)&red[0][0][0]);
+    }
+    return;
+  }
+  const int c8 = t & 7, ng = t >> 3;
+  const uint16_t* wk = p.w_kv_b + ((size_t)h * kWRowsPerHead + 4 * ng) * kLatent + cblk * 64 + c8 * 8;
+  uint4 w[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) w[k] = *(const uint4*)(wk + (size_t)k * kLatent);
+  // rounds of kPrepRows rows; the W_UK block stays in registers
+  for (int rc = 0; rc < p.rows_per_wg; rc += kPrepRows) {
+    const int rb = r0 + rc;
+    if (rb >= p.rows) break;            // uniform across the workgroup
+    uint2 q[kPrepRows];
+#pragma unroll
+    for (int rr = 0; rr < kPrepRows; ++rr) {
+      const int r = min(rb + rr, p.rows - 1);
+      q[rr] = *(const uint2*)(p.q_nope + ((size_t)r * kHeads + h) * kNope + 4 * ng);
+    }
+#pragma unroll
+    for (int rr = 0; rr < kPrepRows; ++rr) {
+      const float qv[4] = {__uint_as_float(q[rr].x << 16), __uint_as_float(q[rr].x & 0xFFFF0000u),
+                           __uint_as_float(q[rr].y << 16), __uint_as_float(q[rr].y & 0xFFFF0000u)};
+      float acc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t wd[4] = {w[k].x, w[k].y, w[k].z, w[k].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] = fmaf(qv[k], __uint_as_float(wd[e] << 16), acc[2 * e]);
+          acc[2 * e + 1] = fmaf(qv[k], __uint_as_float(wd[e] & 0xFFFF0000u), acc[2 * e + 1]);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red[rr][ng][c8 * 8 + e] = acc[e];
+    }
+    __syncthreads();
+    const int rr = t >> 6, col = t & 63;
+    const int r = rb + rr;
+    if (r < p.rows) {
+      float acc = 0.f;
+#pragma unroll
+      for (int k = 0; k < 32; ++k) acc += red[rr][k][col];
+      prep_row(p, r, h, cblk, col, acc);
+    }
+    __syncthreads();                    // red is written again by the next round
+  }
+}
+
 // ---------------------------------------------------------------------------
 // LSE combine of the segment partials with this column block's share of the
-// W_UV up-projection.  Grid (8 latent blocks of 64 columns, 32 heads, rows);
-// a workgroup of 256 threads handles head row (r, h) on columns
-// [64 cb, 64 cb + 64):
-//  1. its 16 groups of 16 lanes take every 16th of the sequence's segments,
-//     16 per batch with every load in flight, each lane 4 columns, and keep
-//     a running max; the groups are merged in a fixed order:
+// W_UV up-projection.  Grid (8 latent blocks of 64 columns, 32 heads, blocks
+// of RB query rows); a workgroup of 256 threads handles head h of rows
+// r0 .. r0 + RB - 1 on columns [64 cb, 64 cb + 64), RB = rows_per_wg (a power
+// of two up to 16), so that the block's W_UV share is read once for RB rows:
+//  1. 16 groups of 16 lanes, 16 / RB groups per row; the groups of a row take
+//     every (16 / RB)-th of its sequence's segments, 16 per batch with every
+//     load in flight, each lane 4 columns, keeping a running max; a row's
+//     groups are then merged in a fixed order:
 //       o_lat = sum_i 2^(lse_i - M) O_i / W,   W = sum_i 2^(lse_i - M)
 //     (a segment whose row saw no token has lse_i = -inf and weight 0);
-//  2. share[v] = sum over the block's columns of W_UV[h][v][c] o_lat[c]
-//     (W_UV[h] = w_kv_b rows [h*256 + 128, h*256 + 256)) and the block's share
-//     of qres . o_lat go to the workspace; block 0 also stores (M, W).
+//  2. for every row, share[v] = sum over the block's columns of
+//     W_UV[h][v][c] o_lat[c] (W_UV[h] = w_kv_b rows [h*256 + 128, h*256 + 256))
+//     and the block's share of qres . o_lat go to the workspace; block 0
+//     also stores (M, W).
 // finalize_out then adds the 8 shares in block order.
 // ---------------------------------------------------------------------------
 constexpr int kCombGroups = 16;
 constexpr int kCombBatch = 16;
+constexpr int kCombRowsMax = 16;
 
 __global__ void __launch_bounds__(256) combine_blocks(CombineParams p) {
   __shared__ f32x4 red_acc[kCombGroups][16];
   __shared__ float red_m[kCombGroups], red_w[kCombGroups];
-  __shared__ float olat[64];
+  __shared__ float olat[kCombRowsMax][64];
   const int cb = blockIdx.x;
   const int h = blockIdx.y;
-  const int r = blockIdx.z;
-  const int b = r / p.Sq;
-  const int j = r - b * p.Sq;
-  const size_t hrow = (size_t)r * kHeads + h;
+  const int RB = p.rows_per_wg;
+  const int r0 = blockIdx.z * RB;
+  const int rows = p.hrows / kHeads;
   const int t = threadIdx.x;
   const int grp = t >> 4, c4 = t & 15;
+  const int gpr = kCombGroups / RB;     // lane groups per row
+  const int rr = grp / gpr, gi = grp - rr * gpr;
+  const int r = r0 + rr;
 
   // W_UV[h][v][64 cb + 32 half .. + 32): thread (v, half), requested first
   const int v = t >> 1, half = t & 1;
@@ -371,47 +409,52 @@ __global__ void __launch_bounds__(256) combine_blocks(CombineParams p) {
   uint4 wu[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) wu[k] = *(const uint4*)(wrow + 8 * k);
+  // qres of row t / 16 of the block, 4 columns
   float4 qr = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (t < 16) qr = *(const float4*)(p.qres + hrow * kLatent + cb * 64 + 4 * t);
-
-  const int seg0 = p.seg_start[b];
-  const int nseg = min(p.seg_start[b + 1], p.max_segs) - seg0;
-  const size_t unit_rows = (size_t)p.Sq * kHeads;
-  const uint16_t* obase = p.part_o + ((size_t)seg0 * unit_rows + j * kHeads + h) * kLatent + cb * 64 + 4 * c4;
-  const float* lbase = p.part_lse + (size_t)seg0 * unit_rows + j * kHeads + h;
-  const size_t ostride = unit_rows * kLatent;
+  if (t < 16 * RB && r0 + (t >> 4) < rows)
+    qr = *(const float4*)(p.qres + ((size_t)(r0 + (t >> 4)) * kHeads + h) * kLatent + cb * 64 + 4 * (t & 15));
 
   float m = kNegInf, wsum = 0.f;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int s0 = grp; s0 < nseg; s0 += kCombGroups * kCombBatch) {
-    float l[kCombBatch];
-    uint2 o4[kCombBatch];   // 4 bf16 values
+  if (r < rows) {
+    const int b = r / p.Sq;
+    const int j = r - b * p.Sq;
+    const int seg0 = p.seg_start[b];
+    const int nseg = min(p.seg_start[b + 1], p.max_segs) - seg0;
+    const size_t unit_rows = (size_t)p.Sq * kHeads;
+    const uint16_t* obase = p.part_o + ((size_t)seg0 * unit_rows + j * kHeads + h) * kLatent + cb * 64 + 4 * c4;
+    const float* lbase = p.part_lse + (size_t)seg0 * unit_rows + j * kHeads + h;
+    const size_t ostride = unit_rows * kLatent;
+    for (int s0 = gi; s0 < nseg; s0 += gpr * kCombBatch) {
+      float l[kCombBatch];
+      uint2 o4[kCombBatch];   // 4 bf16 values
 #pragma unroll
-    for (int k = 0; k < kCombBatch; ++k) {
-      const int s = min(s0 + k * kCombGroups, nseg - 1);   // past the end: re-read, weight 0 below
-      l[k] = lbase[s * unit_rows];
-      o4[k] = *(const uint2*)(obase + s * ostride);
-    }
-    __builtin_amdgcn_sched_barrier(0);   // every load of the batch in flight before the first use
+      for (int k = 0; k < kCombBatch; ++k) {
+        const int s = min(s0 + k * gpr, nseg - 1);   // past the end: re-read, weight 0 below
+        l[k] = lbase[s * unit_rows];
+        o4[k] = *(const uint2*)(obase + s * ostride);
+      }
+      __builtin_amdgcn_sched_barrier(0);   // every load of the batch in flight before the first use
 #pragma unroll
-    for (int k = 0; k < kCombBatch; ++k)
-      if (s0 + k * kCombGroups >= nseg) l[k] = kNegInf;
-    float bm = m;
+      for (int k = 0; k < kCombBatch; ++k)
+        if (s0 + k * gpr >= nseg) l[k] = kNegInf;
+      float bm = m;
 #pragma unroll
-    for (int k = 0; k < kCombBatch; ++k) bm = fmaxf(bm, l[k]);
-    const float sc = (m == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m - bm);
-    wsum *= sc;
+      for (int k = 0; k < kCombBatch; ++k) bm = fmaxf(bm, l[k]);
+      const float sc = (m == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m - bm);
+      wsum *= sc;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] *= sc;
-    m = bm;
+      for (int i = 0; i < 4; ++i) acc[i] *= sc;
+      m = bm;
 #pragma unroll
-    for (int k = 0; k < kCombBatch; ++k) {
-      const float wt = (l[k] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(l[k] - bm);
-      wsum += wt;
-      const float ov[4] = {__uint_as_float(o4[k].x << 16), __uint_as_float(o4[k].x & 0xFFFF0000u),
-                           __uint_as_float(o4[k].y << 16), __uint_as_float(o4[k].y & 0xFFFF0000u)};
+      for (int k = 0; k < kCombBatch; ++k) {
+        const float wt = (l[k] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(l[k] - bm);
+        wsum += wt;
+        const float ov[4] = {__uint_as_float(o4[k].x << 16), __uint_as_float(o4[k].x & 0xFFFF0000u),
+                             __uint_as_float(o4[k].y << 16), __uint_as_float(o4[k].y & 0xFFFF0000u)};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = fmaf(wt, ov[i], acc[i]);
+        for (int i = 0; i < 4; ++i) acc[i] = fmaf(wt, ov[i], acc[i]);
+      }
     }
   }
   red_acc[grp][c4] = acc;
@@ -420,34 +463,32 @@ __global__ void __launch_bounds__(256) combine_blocks(CombineParams p) {
     red_w[grp] = wsum;
   }
   __syncthreads();
-  if (t < 64) {   // wave 0: merge the groups, this block's o_lat and share of qres . o_lat
-    float M = red_m[0];
-#pragma unroll
-    for (int g2 = 1; g2 < kCombGroups; ++g2) M = fmaxf(M, red_m[g2]);
+  if (t < 16 * RB) {   // row t / 16 of the block: merge its groups; o_lat and the share of qres . o_lat
+    const int rr2 = t >> 4, g0 = rr2 * gpr, lane16 = t & 15;
+    float M = red_m[g0];
+    for (int g2 = 1; g2 < gpr; ++g2) M = fmaxf(M, red_m[g0 + g2]);
     float W = 0.f;
     f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int g2 = 0; g2 < kCombGroups; ++g2) {
-      const float sc = (red_m[g2] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(red_m[g2] - M);
-      W = fmaf(red_w[g2], sc, W);
-      const f32x4 a = red_acc[g2][t & 15];
+    for (int g2 = 0; g2 < gpr; ++g2) {
+      const float sc = (red_m[g0 + g2] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(red_m[g0 + g2] - M);
+      W = fmaf(red_w[g0 + g2], sc, W);
+      const f32x4 a = red_acc[g0 + g2][lane16];
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[i] = fmaf(a[i], sc, o[i]);
     }
     const float inv = (W > 0.f) ? 1.f / W : 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] *= inv;
-    float c = 0.f;
-    if (t < 16) {
-      *(f32x4*)(olat + 4 * t) = o;
-      c = qr.x * o[0];
-      c = fmaf(qr.y, o[1], c);
-      c = fmaf(qr.z, o[2], c);
-      c = fmaf(qr.w, o[3], c);
-    }
+    *(f32x4*)(&olat[rr2][4 * lane16]) = o;
+    float c = qr.x * o[0];
+    c = fmaf(qr.y, o[1], c);
+    c = fmaf(qr.z, o[2], c);
+    c = fmaf(qr.w, o[3], c);
 #pragma unroll
     for (int d = 8; d >= 1; d >>= 1) c += __shfl_xor(c, d, 16);
-    if (t == 0) {
+    const int r2 = r0 + rr2;
+    if (lane16 == 0 && r2 < rows) {
+      const size_t hrow = (size_t)r2 * kHeads + h;
       p.corr_part[hrow * 8 + cb] = c;
       if (cb == 0) {
         p.stat[2 * hrow] = M;
@@ -457,19 +498,23 @@ __global__ void __launch_bounds__(256) combine_blocks(CombineParams p) {
   }
   __syncthreads();
 
-  float up = 0.f;
+  for (int rr2 = 0; rr2 < RB; ++rr2) {
+    const int r2 = r0 + rr2;
+    if (r2 >= rows) break;
+    float up = 0.f;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint32_t wd[4] = {wu[k].x, wu[k].y, wu[k].z, wu[k].w};
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t wd[4] = {wu[k].x, wu[k].y, wu[k].z, wu[k].w};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int c = 32 * half + 8 * k + 2 * e;
-      up = fmaf(__uint_as_float(wd[e] << 16), olat[c], up);
-      up = fmaf(__uint_as_float(wd[e] & 0xFFFF0000u), olat[c + 1], up);
+      for (int e = 0; e < 4; ++e) {
+        const int c = 32 * half + 8 * k + 2 * e;
+        up = fmaf(__uint_as_float(wd[e] << 16), olat[rr2][c], up);
+        up = fmaf(__uint_as_float(wd[e] & 0xFFFF0000u), olat[rr2][c + 1], up);
+      }
     }
+    up += __shfl_xor(up, 1, 2);
+    if (half == 0) p.up_part[(((size_t)r2 * kHeads + h) * 8 + cb) * kVDim + v] = up;
   }
-  up += __shfl_xor(up, 1, 2);
-  if (half == 0) p.up_part[(hrow * 8 + cb) * kVDim + v] = up;
 }
 
 // ---------------------------------------------------------------------------
@@ -599,14 +644,15 @@ hipError_t launch_append_fp8(uint8_t* cache, int64_t num_slots, const uint16_t* 
 }
 
 hipError_t launch_prep(const PrepParams& p, hipStream_t stream) {
-  const unsigned rb = (unsigned)((p.rows + kPrepRows - 1) / kPrepRows);
+  const unsigned rb = (unsigned)((p.rows + p.rows_per_wg - 1) / p.rows_per_wg);
   hipLaunchKernelGGL(prep_query, dim3(kLatent / 64 + 1, kHeads, rb), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
 hipError_t launch_combine_upproject(const CombineParams& p, hipStream_t stream) {
   const unsigned rows = (unsigned)(p.hrows / kHeads);
-  hipLaunchKernelGGL(combine_blocks, dim3(kLatent / 64, kHeads, rows), dim3(256), 0, stream, p);
+  const unsigned rblocks = (rows + p.rows_per_wg - 1) / p.rows_per_wg;
+  hipLaunchKernelGGL(combine_blocks, dim3(kLatent / 64, kHeads, rblocks), dim3(256), 0, stream, p);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   hipLaunchKernelGGL(finalize_out, dim3((unsigned)((p.hrows + 1) / 2)), dim3(256), 0, stream, p);
   return hipGetLastError();

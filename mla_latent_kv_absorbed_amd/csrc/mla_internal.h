@@ -201,6 +201,7 @@ struct PrepParams {
   int32_t max_ctx_len;
   int64_t num_pages;
   uint32_t* faults;
+  int32_t rows_per_wg;          // query rows per workgroup (prep_rows_per_wg)
   int32_t rotate;               // q_pe and k_new are rotated here when non-zero
   InvFreq inv;
   const uint16_t* c_new;        // bf16 [rows][ld_c] latent rows of the new tokens, or null
@@ -228,6 +229,7 @@ struct CombineParams {
   int32_t max_segs;
   int32_t Sq;
   int32_t hrows;                // rows * 32
+  int32_t rows_per_wg;          // query rows per workgroup (combine_rows_per_wg)
   const uint16_t* w_kv_b;
   const float* qres;
   float scale_log2;
@@ -237,6 +239,17 @@ struct CombineParams {
   float* corr_part;             // fp32 [rows*32][8]: qres . o_lat shares
   float* stat;                  // fp32 [rows*32][2]: combined (M, W), log2 domain
 };
+
+// Query rows per workgroup of the preparation and combine kernels: enough
+// rows that W_UK and W_UV (4 MiB each) are not read once per query row from
+// L2 when a call has many rows, few enough that a call with few rows still
+// spreads over the compute units.  Powers of two up to 16.
+inline int prep_rows_per_wg(int rows) { return rows >= 32 ? 16 : 4; }
+inline int combine_rows_per_wg(int rows) {
+  int rb = 1;
+  while (rb < 16 && 8 * rb <= rows) rb *= 2;
+  return rb;
+}
 
 // Launchers (each enqueues on `stream`; return hipError_t of the launch).
 // ev_start / ev_stop (may be null): recorded by the dispatches themselves at
