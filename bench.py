@@ -496,6 +496,47 @@ def summarize_pmc(paths, title: str, command: str):
     print("\n".join(lines))
 
 
+def summarize_trace(path: str, title: str, command: str, splitkv: str):
+    """Markdown summary of a rocprofv3 --kernel-trace CSV: per kernel the calls and durations, and
+    the median durations over back-to-back layer sequences (prep_query -> the split-KV kernel whose
+    name starts with `splitkv` -> combine_blocks -> finalize_out, gaps under 2 us)."""
+    import csv
+    import statistics
+    ks = []
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            ks.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), _short_kernel(r["Kernel_Name"])))
+    ks.sort()
+    per = {}
+    for a, b, n in ks:
+        per.setdefault(n, []).append((b - a) / 1e3)
+    total = sum(sum(v) for v in per.values())
+    lines = [f"# {title}", "", "Command (repository root, one MI355X):", "", "    " + command, "",
+             "| kernel | calls | avg us | median us | min us | max us | share |", "|---|---:|---:|---:|---:|---:|---:|"]
+    for n, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| {n[:70]} | {len(v)} | {statistics.mean(v):.2f} | {statistics.median(v):.2f} | {min(v):.2f} | "
+                     f"{max(v):.2f} | {sum(v) / total:.1%} |")
+    seq = {"prep_query": [], "split": [], "combine_blocks": [], "finalize_out": [], "layer": []}
+    for i in range(len(ks) - 3):
+        names = [ks[i + k][2] for k in range(4)]
+        if names[0] != "prep_query" or not names[1].startswith(splitkv) or names[2] != "combine_blocks" \
+                or names[3] != "finalize_out":
+            continue
+        if any(ks[i + k + 1][0] - ks[i + k][1] > 2000 for k in range(3)):
+            continue
+        for k, key in enumerate(("prep_query", "split", "combine_blocks", "finalize_out")):
+            seq[key].append((ks[i + k][1] - ks[i + k][0]) / 1e3)
+        seq["layer"].append((ks[i + 3][1] - ks[i][0]) / 1e3)
+    if seq["layer"]:
+        lines += ["", f"Back-to-back layer sequences (prep_query -> {splitkv}* -> combine_blocks -> finalize_out, "
+                      f"gaps < 2 us; {len(seq['layer'])} found), median durations:", "", "| kernel | median us |",
+                  "|---|---:|"]
+        for key in ("prep_query", "split", "combine_blocks", "finalize_out"):
+            lines.append(f"| {splitkv if key == 'split' else key} | {statistics.median(seq[key]):.2f} |")
+        lines.append(f"| one layer, first start to last end | {statistics.median(seq['layer']):.2f} |")
+    print("\n".join(lines))
+
+
 def copy_calibration(nbytes: int):
     """A plain device-to-device copy of nbytes, three times (a known-size reference for counters)."""
     import torch
@@ -536,13 +577,19 @@ def main():
                     help="build --counter-layers layers of --config and run --steps eager decode steps, nothing else "
                          "(for hardware-counter passes)")
     ap.add_argument("--counter-layers", type=int, default=1)
-    ap.add_argument("--cache-dtype", default="bf16", choices=("bf16", "fp8"), help="with --counters-only")
+    ap.add_argument("--cache-dtype", default="bf16", choices=("bf16", "fp8"),
+                    help="cache format of the main workload (and of --counters-only)")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="CSV",
                     help="print a markdown table (mean per dispatch, per kernel and counter) of rocprofv3 --pmc CSVs")
     ap.add_argument("--pmc-title", default="rocprofv3 counters")
+    ap.add_argument("--summarize-trace", metavar="CSV", help="print a markdown summary of a rocprofv3 kernel trace")
+    ap.add_argument("--trace-splitkv", default="splitkv_decode<", help="split-KV kernel name prefix for the layer table")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc, args.pmc_title, args.counters_command)
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.pmc_title, args.counters_command, args.trace_splitkv)
         return
     if args.summarize_counters:
         from synth.configs import workload
@@ -572,7 +619,7 @@ def main():
     if args.copy_calibration_mb:
         copy_calibration(args.copy_calibration_mb << 20)
     main_res = run_workload(args.config, args.steps, args.warmup, not args.no_graph, kv_chunk=args.kv_chunk,
-                            label=f"config{args.config}")
+                            label=f"config{args.config}", cache_dtype=args.cache_dtype)
     log(f"[config{args.config}] {json.dumps(main_res)}")
     extra = None
     if not args.no_256k and args.config != 3:

@@ -191,115 +191,123 @@ __device__ void build_schedule(const PrepParams& p, int* lds) {
 }
 
 // ---------------------------------------------------------------------------
-// Preparation of one decode call.  Grid (8 latent blocks of 64 + 1, 32
+// Preparation of one decode call.  Grid (8 latent blocks of 64 + 2, 32
 // heads, blocks of rows_per_wg query rows, 4 or 16); row r = b*Sq + j.
-//  * Absorption: Q_abs[r][h][0:512] = bf16(W_UK[h]^T q_nope[r][h]) and the
-//    fp32 residual q_lat - bf16(q_lat) (for the first-order LSE correction).
-//    W_UK[h] = w_kv_b rows [h*256, h*256 + 128).  Thread (ng, c8) loads
-//    W_UK[h][4ng .. 4ng+3][c8*8 .. c8*8+7] as four 16-byte loads once, and
-//    in rounds of 4 rows forms the partial dot products of the round's rows
-//    over those 4 nope dims; the 32 partials of each output are summed
-//    through LDS in a fixed order.  Up to 16 rows share one load of W_UK.
-//  * Rope part: Q_abs[r][h][512:576] = q_pe[r][h], rotated at the query's
-//    position p = L_b - Sq + j when `rotate` is set (latent block 0).
-//  * New tokens (when c_new is given): cache row of token p of sequence b =
-//    [c_new[r] | rot(k_new[r], p)] (head 0 writes the latent, head 1 of
-//    latent block 0 the rope part).
-//  * Workgroup (8, 0, 0) zeroes the decode kernel's zero row and builds the
+//  * Absorption (x < 8): Q_abs[r][h][64x .. 64x + 64) = bf16(W_UK[h]^T
+//    q_nope[r][h]) on those columns and the fp32 residual q_lat - bf16(q_lat)
+//    (for the first-order LSE correction).  W_UK[h] = w_kv_b rows [h*256,
+//    h*256 + 128).  Thread (ng, c8) loads W_UK[h][4ng .. 4ng+3][c8*8 ..
+//    c8*8+7] (four 16-byte loads) and the block's query rows once; in rounds
+//    of 4 rows it forms the partial dot products over its 4 nope dims, and the
+//    32 partials of each output are summed through LDS in a fixed order.
+//  * Rope part and new tokens (x = 8, head h): Q_abs[r][h][512:576] = q_pe[r][h],
+//    rotated at the query's position p = L_b - Sq + j when `rotate` is set;
+//    with c_new given, head 0 writes the new tokens' latent into their cache
+//    rows (a bit copy, or quantised for the 8-bit format) and head 1 their
+//    rope keys (rotated at p).  These run beside the absorption instead of
+//    after it, since the fp64 angle arithmetic is long.
+//  * Workgroup (9, 0, 0) zeroes the decode kernel's zero row and builds the
 //    split schedule (the other workgroups of that column exit at once).
 // ---------------------------------------------------------------------------
 constexpr int kPrepRows = 4;        // rows of one reduction round
 constexpr int kPrepRowsMax = 16;    // rows of one workgroup (its W_UK block is loaded once)
+constexpr int kPrepRopeCol = kLatent / 64;       // grid column of the rope part and new tokens
+constexpr int kPrepSchedCol = kPrepRopeCol + 1;  // grid column of the schedule
 
-// The outputs of query row r for head h and latent block cblk, from this
-// thread's column `col` of the absorbed query (acc, fp32): Q_abs and the
-// residual, the rope part, and the new token's cache row.  One wave per row,
-// so every branch below is uniform across a wave.
-__device__ __forceinline__ void prep_row(const PrepParams& p, int r, int h, int cblk, int col, float acc) {
-  const size_t hrow = (size_t)r * kHeads + h;
-  uint16_t* dst = p.qabs + hrow * kRow;
-  const uint16_t qb = f32_to_bf16(acc);
-  dst[cblk * 64 + col] = qb;
-  p.qres[hrow * kLatent + cblk * 64 + col] = acc - bf16_to_f32(qb);
+// Position of query row r (clamped length) and its sequence.
+__device__ __forceinline__ int query_pos(const PrepParams& p, int r, int* b) {
+  *b = r / p.Sq;
+  bool bad;   // raised by the schedule
+  return clamp_ctx_len(p.ctx_lens[*b], p.Sq, p.max_ctx_len, &bad) - p.Sq + (r - *b * p.Sq);
+}
 
-  const int b = r / p.Sq;
-  bool bad_len;   // raised by the schedule
-  const int pos = clamp_ctx_len(p.ctx_lens[b], p.Sq, p.max_ctx_len, &bad_len) - p.Sq + (r - b * p.Sq);
-  const int half = kRope / 2;
-  if (cblk == 0) {
-    const uint16_t* src = p.q_pe + hrow * kRope;
-    if (!p.rotate) {
-      dst[kLatent + col] = src[col];
-    } else if (col < half) {
+// Cache slot of the new token at position pos of sequence b, or -1 when its
+// page lies outside the pool (the fault is raised when `flag`).
+__device__ __forceinline__ int64_t new_token_slot(const PrepParams& p, int b, int pos, bool flag) {
+  if (p.paged) {
+    const int page = p.block_table[(size_t)b * p.max_pages + pos / kPage];
+    if (!page_ok(page, p.num_pages)) {
+      if (flag) raise_fault(p.faults, kFaultPage);
+      return -1;
+    }
+    return (int64_t)page * kPage + pos % kPage;
+  }
+  return (int64_t)b * p.stride_tokens + pos;
+}
+
+// Rope part of Q_abs for head h and (heads 0 and 1) the new tokens' cache
+// rows, query rows [r0, r1).
+__device__ void prep_rope_and_rows(const PrepParams& p, int h, int r0, int r1) {
+  const int t = threadIdx.x;
+  constexpr int half = kRope / 2;
+  if (p.rotate) {
+    for (int i = t; i < (r1 - r0) * half; i += 256) {
+      const int r = r0 + i / half, k = i % half;
+      int b;
+      const int pos = query_pos(p, r, &b);
+      const size_t hrow = (size_t)r * kHeads + h;
+      const uint16_t* src = p.q_pe + hrow * kRope;
       uint16_t lo, hi;
-      rope_pair(src[col], src[col + half], (double)pos * p.inv.v[col], &lo, &hi);
-      dst[kLatent + col] = lo;
-      dst[kLatent + col + half] = hi;
+      rope_pair(src[k], src[k + half], (double)pos * p.inv.v[k], &lo, &hi);
+      uint16_t* dst = p.qabs + hrow * kRow + kLatent;
+      dst[k] = lo;
+      dst[k + half] = hi;
+    }
+  } else {
+    for (int i = t; i < (r1 - r0) * kRope; i += 256) {
+      const size_t hrow = (size_t)(r0 + i / kRope) * kHeads + h;
+      p.qabs[hrow * kRow + kLatent + i % kRope] = p.q_pe[hrow * kRope + i % kRope];
     }
   }
-  if (p.c_new != nullptr && p.fp8 && pos >= 0 && ((h == 0 && cblk < 4) || (h == 1 && cblk == 0))) {
-    // 8-bit row: latent group cblk (128 values, 2 per lane of this row's wave)
-    // quantised with its own scale; the rope key rotated into bf16 at byte 528
-    int64_t slot;
-    if (p.paged) {
-      const int page = p.block_table[(size_t)b * p.max_pages + pos / kPage];
-      if (!page_ok(page, p.num_pages)) {   // no row is written for a page outside the pool
-        if (col == 0) raise_fault(p.faults, kFaultPage);
-        return;
-      }
-      slot = (int64_t)page * kPage + pos % kPage;
-    } else {
-      slot = (int64_t)b * p.stride_tokens + pos;
-    }
-    uint8_t* row = p.cache + slot * kF8Row;
+  if (p.c_new == nullptr || h > 1) return;
+  // one wave per new token's row
+  const int wave = t >> 6, lane = t & 63;
+  for (int r = r0 + wave; r < r1; r += 4) {
+    int b;
+    const int pos = query_pos(p, r, &b);
+    const int64_t slot = new_token_slot(p, b, pos, lane == 0);
+    if (slot < 0) continue;   // wave-uniform
     if (h == 0) {
-      const uint32_t two = *(const uint32_t*)(p.c_new + r * p.ld_c + cblk * kF8Group + 2 * col);
-      const float x0 = __uint_as_float(two << 16), x1 = __uint_as_float(two & 0xFFFF0000u);
-      float amax = fmaxf(fabsf(x0), fabsf(x1));
+      const uint4 v = *(const uint4*)(p.c_new + r * p.ld_c + 8 * lane);
+      if (!p.fp8) {
+        *(uint4*)(p.cache + slot * kRowBytes + 16 * lane) = v;
+      } else {
+        // lane l holds latent values [8l, 8l + 8) of group l / 16; the 16
+        // lanes of a group agree on amax, scale = amax / 448 and the codes
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        float x[8];
 #pragma unroll
-      for (int d = 32; d >= 1; d >>= 1) amax = fmaxf(amax, __shfl_xor(amax, d, 64));
-      const float scale = amax / kE4M3Max;
-      const uint32_t q0 = scale > 0.f ? f32_to_e4m3(x0 / scale) : 0u;
-      const uint32_t q1 = scale > 0.f ? f32_to_e4m3(x1 / scale) : 0u;
-      *(uint16_t*)(row + cblk * kF8Group + 2 * col) = (uint16_t)(q0 | (q1 << 8));
-      if (col == 0) *(float*)(row + kF8ScaleOff + 4 * cblk) = scale;
-    } else {
-      uint16_t* rope = (uint16_t*)(row + kF8RopeOff);
-      const uint16_t* src = p.k_new + r * p.ld_k;
-      if (!p.rotate) {
-        rope[col] = src[col];
-      } else if (col < half) {
-        uint16_t lo, hi;
-        rope_pair(src[col], src[col + half], (double)pos * p.inv.v[col], &lo, &hi);
-        rope[col] = lo;
-        rope[col + half] = hi;
+        for (int k = 0; k < 4; ++k) {
+          x[2 * k] = __uint_as_float(w[k] << 16);
+          x[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+        }
+        float amax = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(x[k]));
+#pragma unroll
+        for (int d = 8; d >= 1; d >>= 1) amax = fmaxf(amax, __shfl_xor(amax, d, 16));
+        const float scale = amax / kE4M3Max;
+        uint32_t q[2] = {0u, 0u};
+        if (scale > 0.f) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) q[k >> 2] |= f32_to_e4m3(x[k] / scale) << (8 * (k & 3));
+        }
+        uint8_t* row = p.cache + slot * kF8Row;
+        *(uint2*)(row + 8 * lane) = make_uint2(q[0], q[1]);
+        if ((lane & 15) == 0) *(float*)(row + kF8ScaleOff + 4 * (lane >> 4)) = scale;
       }
-    }
-  }
-  if (p.c_new != nullptr && !p.fp8 && pos >= 0 && (h == 0 || (h == 1 && cblk == 0))) {
-    int64_t slot;
-    if (p.paged) {
-      const int page = p.block_table[(size_t)b * p.max_pages + pos / kPage];
-      if (!page_ok(page, p.num_pages)) {   // no row is written for a page outside the pool
-        if (col == 0) raise_fault(p.faults, kFaultPage);
-        return;
-      }
-      slot = (int64_t)page * kPage + pos % kPage;
-    } else {
-      slot = (int64_t)b * p.stride_tokens + pos;
-    }
-    uint16_t* crow = (uint16_t*)(p.cache + slot * kRowBytes);
-    if (h == 0) {
-      crow[cblk * 64 + col] = p.c_new[r * p.ld_c + cblk * 64 + col];
-    } else {
+    } else if (lane < half) {
       const uint16_t* src = p.k_new + r * p.ld_k;
+      uint16_t* rope = p.fp8 ? (uint16_t*)(p.cache + slot * kF8Row + kF8RopeOff)
+                             : (uint16_t*)(p.cache + slot * kRowBytes) + kLatent;
       if (!p.rotate) {
-        crow[kLatent + col] = src[col];
-      } else if (col < half) {
+        rope[lane] = src[lane];
+        rope[lane + half] = src[lane + half];
+      } else {
         uint16_t lo, hi;
-        rope_pair(src[col], src[col + half], (double)pos * p.inv.v[col], &lo, &hi);
-        crow[kLatent + col] = lo;
-        crow[kLatent + col + half] = hi;
+        rope_pair(src[lane], src[lane + half], (double)pos * p.inv.v[lane], &lo, &hi);
+        rope[lane] = lo;
+        rope[lane + half] = hi;
       }
     }
   }
@@ -311,12 +319,17 @@ __global__ void __launch_bounds__(256) prep_query(PrepParams p) {
   const int cblk = blockIdx.x;
   const int h = blockIdx.y;
   const int r0 = blockIdx.z * p.rows_per_wg;
+  const int r1 = min(r0 + p.rows_per_wg, p.rows);
   const int t = threadIdx.x;
-  if (cblk == kLatent / 64) {           // the extra column: schedule and zero row
+  if (cblk == kPrepSchedCol) {
     if (h == 0 && r0 == 0) {
       if (t < kChunksPerRow) ((uint4*)p.zero_row)[t] = make_uint4(0, 0, 0, 0);
       build_schedule(p, (int*)&red[0][0][0]);
     }
+    return;
+  }
+  if (cblk == kPrepRopeCol) {
+    prep_rope_and_rows(p, h, r0, r1);
     return;
   }
   const int c8 = t & 7, ng = t >> 3;
@@ -324,20 +337,21 @@ __global__ void __launch_bounds__(256) prep_query(PrepParams p) {
   uint4 w[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) w[k] = *(const uint4*)(wk + (size_t)k * kLatent);
-  // rounds of kPrepRows rows; the W_UK block stays in registers
-  for (int rc = 0; rc < p.rows_per_wg; rc += kPrepRows) {
-    const int rb = r0 + rc;
-    if (rb >= p.rows) break;            // uniform across the workgroup
-    uint2 q[kPrepRows];
+  uint2 q[kPrepRowsMax];   // the block's query rows, this thread's 4 nope dims
 #pragma unroll
-    for (int rr = 0; rr < kPrepRows; ++rr) {
-      const int r = min(rb + rr, p.rows - 1);
+  for (int rr = 0; rr < kPrepRowsMax; ++rr) {
+    if (rr < p.rows_per_wg) {
+      const int r = min(r0 + rr, p.rows - 1);
       q[rr] = *(const uint2*)(p.q_nope + ((size_t)r * kHeads + h) * kNope + 4 * ng);
     }
+  }
+#pragma unroll
+  for (int rc = 0; rc < kPrepRowsMax; rc += kPrepRows) {
+    if (rc >= p.rows_per_wg || r0 + rc >= p.rows) break;   // uniform across the workgroup
 #pragma unroll
     for (int rr = 0; rr < kPrepRows; ++rr) {
-      const float qv[4] = {__uint_as_float(q[rr].x << 16), __uint_as_float(q[rr].x & 0xFFFF0000u),
-                           __uint_as_float(q[rr].y << 16), __uint_as_float(q[rr].y & 0xFFFF0000u)};
+      const float qv[4] = {__uint_as_float(q[rc + rr].x << 16), __uint_as_float(q[rc + rr].x & 0xFFFF0000u),
+                           __uint_as_float(q[rc + rr].y << 16), __uint_as_float(q[rc + rr].y & 0xFFFF0000u)};
       float acc[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] = 0.f;
@@ -355,12 +369,15 @@ __global__ void __launch_bounds__(256) prep_query(PrepParams p) {
     }
     __syncthreads();
     const int rr = t >> 6, col = t & 63;
-    const int r = rb + rr;
+    const int r = r0 + rc + rr;
     if (r < p.rows) {
       float acc = 0.f;
 #pragma unroll
       for (int k = 0; k < 32; ++k) acc += red[rr][k][col];
-      prep_row(p, r, h, cblk, col, acc);
+      const size_t hrow = (size_t)r * kHeads + h;
+      const uint16_t qb = f32_to_bf16(acc);
+      p.qabs[hrow * kRow + cblk * 64 + col] = qb;
+      p.qres[hrow * kLatent + cblk * 64 + col] = acc - bf16_to_f32(qb);
     }
     __syncthreads();                    // red is written again by the next round
   }
@@ -371,7 +388,8 @@ __global__ void __launch_bounds__(256) prep_query(PrepParams p) {
 // W_UV up-projection.  Grid (8 latent blocks of 64 columns, 32 heads, blocks
 // of RB query rows); a workgroup of 256 threads handles head h of rows
 // r0 .. r0 + RB - 1 on columns [64 cb, 64 cb + 64), RB = rows_per_wg (a power
-// of two up to 16), so that the block's W_UV share is read once for RB rows:
+// of two from 2 to 16; calls with one row per workgroup take combine_one_row
+// below), so that the block's W_UV share is read once for RB rows:
 //  1. 16 groups of 16 lanes, 16 / RB groups per row; the groups of a row take
 //     every (16 / RB)-th of its sequence's segments, 16 per batch with every
 //     load in flight, each lane 4 columns, keeping a running max; a row's
@@ -388,18 +406,19 @@ constexpr int kCombGroups = 16;
 constexpr int kCombBatch = 16;
 constexpr int kCombRowsMax = 16;
 
+template <int RB>
 __global__ void __launch_bounds__(256) combine_blocks(CombineParams p) {
+  static_assert(RB >= 2 && RB <= kCombRowsMax && (RB & (RB - 1)) == 0, "rows per workgroup");
   __shared__ f32x4 red_acc[kCombGroups][16];
   __shared__ float red_m[kCombGroups], red_w[kCombGroups];
-  __shared__ float olat[kCombRowsMax][64];
+  __shared__ float olat[RB][64];
   const int cb = blockIdx.x;
   const int h = blockIdx.y;
-  const int RB = p.rows_per_wg;
   const int r0 = blockIdx.z * RB;
   const int rows = p.hrows / kHeads;
   const int t = threadIdx.x;
   const int grp = t >> 4, c4 = t & 15;
-  const int gpr = kCombGroups / RB;     // lane groups per row
+  constexpr int gpr = kCombGroups / RB; // lane groups per row
   const int rr = grp / gpr, gi = grp - rr * gpr;
   const int r = r0 + rr;
 
@@ -515,6 +534,130 @@ __global__ void __launch_bounds__(256) combine_blocks(CombineParams p) {
     up += __shfl_xor(up, 1, 2);
     if (half == 0) p.up_part[(((size_t)r2 * kHeads + h) * 8 + cb) * kVDim + v] = up;
   }
+}
+
+// The same for one query row per workgroup (calls with fewer than 16 query
+// rows, e.g. a single sequence decoding one token), written for that case:
+// wave 0 merges the 16 groups, and the share goes straight to the workspace.
+// At one row it measured 0.5 us per call faster than combine_blocks<1>.
+__global__ void __launch_bounds__(256) combine_one_row(CombineParams p) {
+  __shared__ f32x4 red_acc[kCombGroups][16];
+  __shared__ float red_m[kCombGroups], red_w[kCombGroups];
+  __shared__ float olat[64];
+  const int cb = blockIdx.x;
+  const int h = blockIdx.y;
+  const int r = blockIdx.z;
+  const int b = r / p.Sq;
+  const int j = r - b * p.Sq;
+  const size_t hrow = (size_t)r * kHeads + h;
+  const int t = threadIdx.x;
+  const int grp = t >> 4, c4 = t & 15;
+
+  // W_UV[h][v][64 cb + 32 half .. + 32): thread (v, half), requested first
+  const int v = t >> 1, half = t & 1;
+  const uint16_t* wrow = p.w_kv_b + ((size_t)h * kWRowsPerHead + kNope + v) * kLatent + cb * 64 + 32 * half;
+  uint4 wu[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) wu[k] = *(const uint4*)(wrow + 8 * k);
+  float4 qr = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (t < 16) qr = *(const float4*)(p.qres + hrow * kLatent + cb * 64 + 4 * t);
+
+  const int seg0 = p.seg_start[b];
+  const int nseg = min(p.seg_start[b + 1], p.max_segs) - seg0;
+  const size_t unit_rows = (size_t)p.Sq * kHeads;
+  const uint16_t* obase = p.part_o + ((size_t)seg0 * unit_rows + j * kHeads + h) * kLatent + cb * 64 + 4 * c4;
+  const float* lbase = p.part_lse + (size_t)seg0 * unit_rows + j * kHeads + h;
+  const size_t ostride = unit_rows * kLatent;
+
+  float m = kNegInf, wsum = 0.f;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = grp; s0 < nseg; s0 += kCombGroups * kCombBatch) {
+    float l[kCombBatch];
+    uint2 o4[kCombBatch];   // 4 bf16 values
+#pragma unroll
+    for (int k = 0; k < kCombBatch; ++k) {
+      const int s = min(s0 + k * kCombGroups, nseg - 1);   // past the end: re-read, weight 0 below
+      l[k] = lbase[s * unit_rows];
+      o4[k] = *(const uint2*)(obase + s * ostride);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // every load of the batch in flight before the first use
+#pragma unroll
+    for (int k = 0; k < kCombBatch; ++k)
+      if (s0 + k * kCombGroups >= nseg) l[k] = kNegInf;
+    float bm = m;
+#pragma unroll
+    for (int k = 0; k < kCombBatch; ++k) bm = fmaxf(bm, l[k]);
+    const float sc = (m == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m - bm);
+    wsum *= sc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] *= sc;
+    m = bm;
+#pragma unroll
+    for (int k = 0; k < kCombBatch; ++k) {
+      const float wt = (l[k] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(l[k] - bm);
+      wsum += wt;
+      const float ov[4] = {__uint_as_float(o4[k].x << 16), __uint_as_float(o4[k].x & 0xFFFF0000u),
+                           __uint_as_float(o4[k].y << 16), __uint_as_float(o4[k].y & 0xFFFF0000u)};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = fmaf(wt, ov[i], acc[i]);
+    }
+  }
+  red_acc[grp][c4] = acc;
+  if (c4 == 0) {
+    red_m[grp] = m;
+    red_w[grp] = wsum;
+  }
+  __syncthreads();
+  if (t < 64) {   // wave 0: merge the groups, this block's o_lat and share of qres . o_lat
+    float M = red_m[0];
+#pragma unroll
+    for (int g2 = 1; g2 < kCombGroups; ++g2) M = fmaxf(M, red_m[g2]);
+    float W = 0.f;
+    f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int g2 = 0; g2 < kCombGroups; ++g2) {
+      const float sc = (red_m[g2] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(red_m[g2] - M);
+      W = fmaf(red_w[g2], sc, W);
+      const f32x4 a = red_acc[g2][t & 15];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = fmaf(a[i], sc, o[i]);
+    }
+    const float inv = (W > 0.f) ? 1.f / W : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] *= inv;
+    float c = 0.f;
+    if (t < 16) {
+      *(f32x4*)(olat + 4 * t) = o;
+      c = qr.x * o[0];
+      c = fmaf(qr.y, o[1], c);
+      c = fmaf(qr.z, o[2], c);
+      c = fmaf(qr.w, o[3], c);
+    }
+#pragma unroll
+    for (int d = 8; d >= 1; d >>= 1) c += __shfl_xor(c, d, 16);
+    if (t == 0) {
+      p.corr_part[hrow * 8 + cb] = c;
+      if (cb == 0) {
+        p.stat[2 * hrow] = M;
+        p.stat[2 * hrow + 1] = W;
+      }
+    }
+  }
+  __syncthreads();
+
+  float up = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t wd[4] = {wu[k].x, wu[k].y, wu[k].z, wu[k].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int c = 32 * half + 8 * k + 2 * e;
+      up = fmaf(__uint_as_float(wd[e] << 16), olat[c], up);
+      up = fmaf(__uint_as_float(wd[e] & 0xFFFF0000u), olat[c + 1], up);
+    }
+  }
+  up += __shfl_xor(up, 1, 2);
+  if (half == 0) p.up_part[(hrow * 8 + cb) * kVDim + v] = up;
 }
 
 // ---------------------------------------------------------------------------
@@ -645,14 +788,21 @@ hipError_t launch_append_fp8(uint8_t* cache, int64_t num_slots, const uint16_t* 
 
 hipError_t launch_prep(const PrepParams& p, hipStream_t stream) {
   const unsigned rb = (unsigned)((p.rows + p.rows_per_wg - 1) / p.rows_per_wg);
-  hipLaunchKernelGGL(prep_query, dim3(kLatent / 64 + 1, kHeads, rb), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(prep_query, dim3(kPrepSchedCol + 1, kHeads, rb), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
 hipError_t launch_combine_upproject(const CombineParams& p, hipStream_t stream) {
   const unsigned rows = (unsigned)(p.hrows / kHeads);
   const unsigned rblocks = (rows + p.rows_per_wg - 1) / p.rows_per_wg;
-  hipLaunchKernelGGL(combine_blocks, dim3(kLatent / 64, kHeads, rblocks), dim3(256), 0, stream, p);
+  const dim3 grid(kLatent / 64, kHeads, rblocks);
+  switch (p.rows_per_wg) {
+    case 1: hipLaunchKernelGGL(combine_one_row, grid, dim3(256), 0, stream, p); break;
+    case 2: hipLaunchKernelGGL(combine_blocks<2>, grid, dim3(256), 0, stream, p); break;
+    case 4: hipLaunchKernelGGL(combine_blocks<4>, grid, dim3(256), 0, stream, p); break;
+    case 8: hipLaunchKernelGGL(combine_blocks<8>, grid, dim3(256), 0, stream, p); break;
+    default: hipLaunchKernelGGL(combine_blocks<16>, grid, dim3(256), 0, stream, p); break;
+  }
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   hipLaunchKernelGGL(finalize_out, dim3((unsigned)((p.hrows + 1) / 2)), dim3(256), 0, stream, p);
   return hipGetLastError();
