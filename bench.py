@@ -406,7 +406,8 @@ def summarize_counters(fetch_csv: str, write_csv: str, copy_bytes: int, workload
         res[f"{counter}_copy_kib"] = copy_kib
         res[f"{counter}_scale"] = scale
         for short, key in (("splitkv_decode", "splitkv_decode<"), ("combine_blocks", "combine_blocks"),
-                           ("finalize_out", "finalize_out"), ("prep_query", "prep_query")):
+                           ("combine_one_row", "combine_one_row"), ("finalize_out", "finalize_out"),
+                           ("prep_query", "prep_query")):
             vals = [v for (cn, kn), vs in rows.items() if cn == counter and key in kn for v in vs]
             if vals:
                 kib = statistics.mean(vals)
@@ -451,7 +452,7 @@ def counters_only(k: int, steps: int, layers: int, cache_dtype: str, kv_chunk):
 
 
 def _short_kernel(name: str) -> str:
-    n = name.replace("void ", "").replace("mla::(anonymous namespace)::", "")
+    n = name.replace("void ", "").replace("mla::(anonymous namespace)::", "").replace("(anonymous namespace)::", "")
     return n.split("(")[0]
 
 
@@ -499,7 +500,8 @@ def summarize_pmc(paths, title: str, command: str):
 def summarize_trace(path: str, title: str, command: str, splitkv: str):
     """Markdown summary of a rocprofv3 --kernel-trace CSV: per kernel the calls and durations, and
     the median durations over back-to-back layer sequences (prep_query -> the split-KV kernel whose
-    name starts with `splitkv` -> combine_blocks -> finalize_out, gaps under 2 us)."""
+    name starts with `splitkv` -> the combine (combine_one_row or combine_blocks<RB>) -> finalize_out,
+    gaps under 2 us)."""
     import csv
     import statistics
     ks = []
@@ -516,23 +518,27 @@ def summarize_trace(path: str, title: str, command: str, splitkv: str):
     for n, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
         lines.append(f"| {n[:70]} | {len(v)} | {statistics.mean(v):.2f} | {statistics.median(v):.2f} | {min(v):.2f} | "
                      f"{max(v):.2f} | {sum(v) / total:.1%} |")
-    seq = {"prep_query": [], "split": [], "combine_blocks": [], "finalize_out": [], "layer": []}
+    seq = {"prep_query": [], "split": [], "combine": [], "finalize_out": [], "layer": []}
+    combine_names = set()
     for i in range(len(ks) - 3):
         names = [ks[i + k][2] for k in range(4)]
-        if names[0] != "prep_query" or not names[1].startswith(splitkv) or names[2] != "combine_blocks" \
+        if names[0] != "prep_query" or not names[1].startswith(splitkv) or not names[2].startswith("combine") \
                 or names[3] != "finalize_out":
             continue
         if any(ks[i + k + 1][0] - ks[i + k][1] > 2000 for k in range(3)):
             continue
-        for k, key in enumerate(("prep_query", "split", "combine_blocks", "finalize_out")):
+        combine_names.add(names[2])
+        for k, key in enumerate(("prep_query", "split", "combine", "finalize_out")):
             seq[key].append((ks[i + k][1] - ks[i + k][0]) / 1e3)
         seq["layer"].append((ks[i + 3][1] - ks[i][0]) / 1e3)
     if seq["layer"]:
-        lines += ["", f"Back-to-back layer sequences (prep_query -> {splitkv}* -> combine_blocks -> finalize_out, "
+        comb = " / ".join(sorted(combine_names))
+        lines += ["", f"Back-to-back layer sequences (prep_query -> {splitkv}* -> {comb} -> finalize_out, "
                       f"gaps < 2 us; {len(seq['layer'])} found), median durations:", "", "| kernel | median us |",
                   "|---|---:|"]
-        for key in ("prep_query", "split", "combine_blocks", "finalize_out"):
-            lines.append(f"| {splitkv if key == 'split' else key} | {statistics.median(seq[key]):.2f} |")
+        for key in ("prep_query", "split", "combine", "finalize_out"):
+            label = {"split": splitkv, "combine": comb}.get(key, key)
+            lines.append(f"| {label} | {statistics.median(seq[key]):.2f} |")
         lines.append(f"| one layer, first start to last end | {statistics.median(seq['layer']):.2f} |")
     print("\n".join(lines))
 
