@@ -192,14 +192,15 @@ __device__ void build_schedule(const PrepParams& p, int* lds) {
 
 // ---------------------------------------------------------------------------
 // Preparation of one decode call.  Grid (8 latent blocks of 64 + 2, 32
-// heads, blocks of rows_per_wg query rows, 4 or 16); row r = b*Sq + j.
+// heads, blocks of 16 query rows); row r = b*Sq + j.
 //  * Absorption (x < 8): Q_abs[r][h][64x .. 64x + 64) = bf16(W_UK[h]^T
 //    q_nope[r][h]) on those columns and the fp32 residual q_lat - bf16(q_lat)
 //    (for the first-order LSE correction).  W_UK[h] = w_kv_b rows [h*256,
-//    h*256 + 128).  Thread (ng, c8) loads W_UK[h][4ng .. 4ng+3][c8*8 ..
-//    c8*8+7] (four 16-byte loads) and the block's query rows once; in rounds
-//    of 4 rows it forms the partial dot products over its 4 nope dims, and the
-//    32 partials of each output are summed through LDS in a fixed order.
+//    h*256 + 128).  On the matrix cores: the block's W_UK columns go to LDS
+//    transposed (each column's 128 nope dims contiguous), and wave w forms
+//    columns [64x + 16w, 64x + 16w + 16) of the 16 rows with four steps of
+//    v_mfma_f32_16x16x32_bf16 (fp32 sums of exact bf16 products), the
+//    columns as A, the query rows as B.
 //  * Rope part and new tokens (x = 8, head h): Q_abs[r][h][512:576] = q_pe[r][h],
 //    rotated at the query's position p = L_b - Sq + j when `rotate` is set;
 //    with c_new given, head 0 writes the new tokens' latent into their cache
@@ -209,8 +210,9 @@ __device__ void build_schedule(const PrepParams& p, int* lds) {
 //  * Workgroup (9, 0, 0) zeroes the decode kernel's zero row and builds the
 //    split schedule (the other workgroups of that column exit at once).
 // ---------------------------------------------------------------------------
-constexpr int kPrepRows = 4;        // rows of one reduction round
-constexpr int kPrepRowsMax = 16;    // rows of one workgroup (its W_UK block is loaded once)
+constexpr int kWtStride = kNope + 8;   // bf16 per transposed W_UK column in LDS (272 bytes)
+constexpr int kPrepLds = 64 * kWtStride * 2;
+static_assert(kPrepLds >= (2 * kSchedLds + 1) * (int)sizeof(int), "schedule scratch");
 constexpr int kPrepRopeCol = kLatent / 64;       // grid column of the rope part and new tokens
 constexpr int kPrepSchedCol = kPrepRopeCol + 1;  // grid column of the schedule
 
@@ -314,8 +316,7 @@ __device__ void prep_rope_and_rows(const PrepParams& p, int h, int r0, int r1) {
 }
 
 __global__ void __launch_bounds__(256) prep_query(PrepParams p) {
-  __shared__ float red[kPrepRows][32][64];
-  static_assert(sizeof(red) >= (2 * kSchedLds + 1) * sizeof(int), "schedule scratch");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kPrepLds];
   const int cblk = blockIdx.x;
   const int h = blockIdx.y;
   const int r0 = blockIdx.z * p.rows_per_wg;
@@ -324,7 +325,7 @@ __global__ void __launch_bounds__(256) prep_query(PrepParams p) {
   if (cblk == kPrepSchedCol) {
     if (h == 0 && r0 == 0) {
       if (t < kChunksPerRow) ((uint4*)p.zero_row)[t] = make_uint4(0, 0, 0, 0);
-      build_schedule(p, (int*)&red[0][0][0]);
+      build_schedule(p, (int*)smem);
     }
     return;
   }
@@ -332,54 +333,59 @@ __global__ void __launch_bounds__(256) prep_query(PrepParams p) {
     prep_rope_and_rows(p, h, r0, r1);
     return;
   }
-  const int c8 = t & 7, ng = t >> 3;
-  const uint16_t* wk = p.w_kv_b + ((size_t)h * kWRowsPerHead + 4 * ng) * kLatent + cblk * 64 + c8 * 8;
-  uint4 w[4];
+  const int lane = t & 63, wave = t >> 6;
+  const int g = lane >> 4, n16 = lane & 15;
+  // B operand: query row r0 + n16 (zero past the last row), nope dims
+  // 32 ks + 8 g .. + 8 of step ks
+  const int rq = r0 + n16;
+  bf16x8 qb[kNope / 32];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) w[k] = *(const uint4*)(wk + (size_t)k * kLatent);
-  uint2 q[kPrepRowsMax];   // the block's query rows, this thread's 4 nope dims
+  for (int ks = 0; ks < kNope / 32; ++ks) qb[ks] = bf16x8{};
+  if (rq < p.rows) {
+    const uint16_t* qs = p.q_nope + ((size_t)rq * kHeads + h) * kNope + 8 * g;
 #pragma unroll
-  for (int rr = 0; rr < kPrepRowsMax; ++rr) {
-    if (rr < p.rows_per_wg) {
-      const int r = min(r0 + rr, p.rows - 1);
-      q[rr] = *(const uint2*)(p.q_nope + ((size_t)r * kHeads + h) * kNope + 4 * ng);
+    for (int ks = 0; ks < kNope / 32; ++ks) qb[ks] = *(const bf16x8*)(qs + 32 * ks);
+  }
+  // W_UK[h] rows 2 kp and 2 kp + 1 (kp = t % 64), the block's columns
+  // [16 cg, 16 cg + 16) (cg = t / 64), written transposed: LDS dword
+  // c * kWtStride / 2 + kp holds (W[2kp][c], W[2kp + 1][c])
+  {
+    const int kp = t & 63, cg = t >> 6;
+    const uint16_t* w0 = p.w_kv_b + ((size_t)h * kWRowsPerHead + 2 * kp) * kLatent + cblk * 64 + 16 * cg;
+    const uint4 a0 = *(const uint4*)w0, a1 = *(const uint4*)(w0 + 8);
+    const uint4 b0 = *(const uint4*)(w0 + kLatent), b1 = *(const uint4*)(w0 + kLatent + 8);
+    const uint32_t ra[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    const uint32_t rb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+    uint32_t* wt = (uint32_t*)smem + (16 * cg) * (kWtStride / 2) + kp;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      wt[(2 * i) * (kWtStride / 2)] = (ra[i] & 0xFFFFu) | (rb[i] << 16);
+      wt[(2 * i + 1) * (kWtStride / 2)] = (ra[i] >> 16) | (rb[i] & 0xFFFF0000u);
     }
   }
+  __syncthreads();
+  // D^T[col][row] = sum_k W[k][col] q[row][k]: wave w the 16 columns
+  // [16 w, 16 w + 16) of the block; A operand = column 16 w + n16, dims
+  // 32 ks + 8 g .. + 8 (16 bytes of LDS)
+  f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint8_t* arow = smem + ((16 * wave + n16) * kWtStride + 8 * g) * 2;
 #pragma unroll
-  for (int rc = 0; rc < kPrepRowsMax; rc += kPrepRows) {
-    if (rc >= p.rows_per_wg || r0 + rc >= p.rows) break;   // uniform across the workgroup
+  for (int ks = 0; ks < kNope / 32; ++ks)
+    d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(arow + 64 * ks), qb[ks], d, 0, 0, 0);
+  // lane (g, n16) holds row r0 + n16, columns 64 cblk + 16 w + 4 g + i
+  if (rq < p.rows) {
+    const size_t hrow = (size_t)rq * kHeads + h;
+    const int col = cblk * 64 + 16 * wave + 4 * g;
+    s16x4 qv;
+    f32x4 res;
 #pragma unroll
-    for (int rr = 0; rr < kPrepRows; ++rr) {
-      const float qv[4] = {__uint_as_float(q[rc + rr].x << 16), __uint_as_float(q[rc + rr].x & 0xFFFF0000u),
-                           __uint_as_float(q[rc + rr].y << 16), __uint_as_float(q[rc + rr].y & 0xFFFF0000u)};
-      float acc[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t wd[4] = {w[k].x, w[k].y, w[k].z, w[k].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[2 * e] = fmaf(qv[k], __uint_as_float(wd[e] << 16), acc[2 * e]);
-          acc[2 * e + 1] = fmaf(qv[k], __uint_as_float(wd[e] & 0xFFFF0000u), acc[2 * e + 1]);
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) red[rr][ng][c8 * 8 + e] = acc[e];
+    for (int i = 0; i < 4; ++i) {
+      const uint16_t qbits = f32_to_bf16(d[i]);
+      qv[i] = (short)qbits;
+      res[i] = d[i] - bf16_to_f32(qbits);
     }
-    __syncthreads();
-    const int rr = t >> 6, col = t & 63;
-    const int r = r0 + rc + rr;
-    if (r < p.rows) {
-      float acc = 0.f;
-#pragma unroll
-      for (int k = 0; k < 32; ++k) acc += red[rr][k][col];
-      const size_t hrow = (size_t)r * kHeads + h;
-      const uint16_t qb = f32_to_bf16(acc);
-      p.qabs[hrow * kRow + cblk * 64 + col] = qb;
-      p.qres[hrow * kLatent + cblk * 64 + col] = acc - bf16_to_f32(qb);
-    }
-    __syncthreads();                    // red is written again by the next round
+    *(s16x4*)(p.qabs + hrow * kRow + col) = qv;
+    *(f32x4*)(p.qres + hrow * kLatent + col) = res;
   }
 }
 

@@ -240,11 +240,12 @@ struct CombineParams {
   float* stat;                  // fp32 [rows*32][2]: combined (M, W), log2 domain
 };
 
-// Query rows per workgroup of the preparation and combine kernels: enough
-// rows that W_UK and W_UV (4 MiB each) are not read once per query row from
-// L2 when a call has many rows, few enough that a call with few rows still
-// spreads over the compute units.  Powers of two up to 16.
-inline int prep_rows_per_wg(int rows) { return rows >= 32 ? 16 : 4; }
+// Query rows per workgroup of the preparation kernel: one 16-row tile of
+// its matrix-core absorption.  Query rows per workgroup of the combine:
+// enough rows that W_UV (4 MiB) is not read once per query row from L2 when
+// a call has many rows, few enough that a call with few rows still spreads
+// over the compute units; powers of two up to 16.
+inline int prep_rows_per_wg(int) { return 16; }
 inline int combine_rows_per_wg(int rows) {
   int rb = 1;
   while (rb < 16 && 8 * rb <= rows) rb *= 2;
