@@ -130,7 +130,8 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode_fp8(DecodeParams p
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kSlots * kSlotLds];
   // P'_G = bf16(p * scale_G) for the four latent groups G, [G][row group]
   // [32-token step][row][32 tokens in MFMA k order]; 16-byte granule q of row
-  // r is stored at granule q ^ ((r % 16) >> 2)
+  // r is stored at granule q ^ ((r >> 1) & 3) (conflict-free 16-byte reads
+  // of 8 consecutive rows, as in decode.hip)
   __shared__ __attribute__((aligned(16))) uint8_t pbuf[4 * RG * 2 * 16 * 64];
   __shared__ float stat[3][TPW][ROWS];   // per score wave and row: slot max, sum, true max
   __shared__ int flags[kWaves];
@@ -247,7 +248,7 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode_fp8(DecodeParams p
   const int v_off = vtok * kF8Row + (lane & 1) * 8 + kCbPerWave * wave * 16;
   const int pgrp = wave >> 1;
   // lane (n16, g) of a value wave reads granule g of P' row n16 of its group
-  const int pb_rd = pgrp * (RG * 2 * 16 * 64) + n16 * 64 + ((g ^ (n16 >> 2)) * 16);
+  const int pb_rd = pgrp * (RG * 2 * 16 * 64) + n16 * 64 + ((g ^ ((n16 >> 1) & 3)) * 16);
 
   f32x4 o[kCbPerWave][RG];
 #pragma unroll
@@ -349,7 +350,7 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode_fp8(DecodeParams p
       f32x4 sc[4];   // the four group scales of token 4g + i of the block
 #pragma unroll
       for (int i = 0; i < 4; ++i) sc[i] = *(lds_f32x4_t*)(T + (t16 + 4 * g + i) * kF8Row + kF8ScaleOff);
-      uint8_t* pw = pbuf + ((rg * 2 + ks) * 16 + n16) * 64 + ((g ^ (n16 >> 2)) * 16) + bb * 8;
+      uint8_t* pw = pbuf + ((rg * 2 + ks) * 16 + n16) * 64 + ((g ^ ((n16 >> 1) & 3)) * 16) + bb * 8;
 #pragma unroll
       for (int G = 0; G < 4; ++G) {
         bf16x4 v;
