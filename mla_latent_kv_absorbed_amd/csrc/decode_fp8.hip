@@ -45,7 +45,9 @@ constexpr int kSlotTok = 64;
 constexpr int kSlotBytes = kSlotTok * kF8Row;              // 41984
 constexpr int kChunks = kSlotBytes / 16;                   // 2624 sixteen-byte chunks
 constexpr int kF8ChunksPerRow = kF8Row / 16;               // 41
-constexpr int kLoadsPerLane = (kChunks + kDmaLanes - 1) / kDmaLanes;   // 11
+constexpr int kRowLds = kF8Row + 16;                       // 672: a row in LDS and a 16-byte pad
+constexpr int kRowChunksLds = kRowLds / 16;                // 42
+constexpr int kLoadsPerLane = (kSlotTok * kRowChunksLds + kDmaLanes - 1) / kDmaLanes;   // 11
 constexpr int kSlotLds = kLoadsPerLane * kDmaLanes * 16;   // 45056: the slot and a pad
 constexpr int kSlots = 3;
 constexpr int kCbPerWave = kLatent / 16 / kWaves;          // 4 column blocks of 16 per wave
@@ -160,9 +162,26 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode_fp8(DecodeParams p
   const int s0 = t_begin / kSlotTok;
   const int nslot = (t_end - t_begin + kSlotTok - 1) / kSlotTok;
 
-  // A slot is copied linearly by waves 0-3: LDS byte 16 P <- slot byte 16 P
-  // for P = (wave * kLoadsPerLane + i) * 64 + lane; chunks past the slot fill
-  // a pad from the zero row.
+  // A slot is copied by waves 0-3 into 672-byte LDS rows: LDS chunk
+  // P = (wave * kLoadsPerLane + i) * 64 + lane is chunk c = P % 42 of token
+  // P / 42, i.e. slot chunk P - P / 42 (the row pad c = 41 repeats the row's
+  // chunk 0; positions past the 64th row re-read the slot's first chunks).
+  // With 672-byte rows (mod 256 the same as the bf16 kernel's 1,184-byte
+  // rows) the 16-byte score reads of 16 consecutive rows are free of bank
+  // conflicts, which the bank-conflict counter showed for 656-byte rows.
+  // dma_off: the slot byte offsets of this lane's loads, two per register.
+  uint32_t dma_off[(kLoadsPerLane + 1) / 2];
+#pragma unroll
+  for (int i = 0; i < (kLoadsPerLane + 1) / 2; ++i) dma_off[i] = 0u;
+#pragma unroll
+  for (int i = 0; i < kLoadsPerLane; ++i) {
+    const int P = (wave * kLoadsPerLane + i) * 64 + lane;
+    const int tok = (P * 3121) >> 17;   // P / 42 for P < 4096
+    const int c = P - kRowChunksLds * tok;
+    int chunk = P - tok - (c == kF8ChunksPerRow ? kF8ChunksPerRow : 0);
+    if (tok >= kSlotTok) chunk -= kChunks;
+    dma_off[i >> 1] |= (uint32_t)(16 * chunk) << (16 * (i & 1));
+  }
   auto issue = [&](int ts, int r) {
     if (!dma_wave) return;
     const uint8_t* src;
@@ -180,23 +199,16 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode_fp8(DecodeParams p
     }
     const uint32_t dst = ring_lds + r * kSlotLds + wave * kLoadsPerLane * 1024;
     if (nval == kSlotTok) {
-      // a whole slot: byte offset 16 P from the slot's (wave-uniform) start;
-      // the pad positions P >= kChunks re-read the slot's first chunks.  (The
-      // lane's offset is recomputed here, not kept in a register.)
-      uint32_t dma_base = (uint32_t)lane;
-      asm volatile("" : "+v"(dma_base));
-      dma_base = 16u * (dma_base + (uint32_t)(wave * kLoadsPerLane * 64));
 #pragma unroll
-      for (int i = 0; i < kLoadsPerLane; ++i) {
-        const bool pad = wave * kLoadsPerLane + i >= kChunks / 64;
-        dma16s(src, dma_base + 1024u * i - (pad ? (uint32_t)kSlotBytes : 0u), dst + i * 1024);
-      }
+      for (int i = 0; i < kLoadsPerLane; ++i) dma16s(src, (dma_off[i >> 1] >> (16 * (i & 1))) & 0xFFFFu, dst + i * 1024);
     } else {
 #pragma unroll
       for (int i = 0; i < kLoadsPerLane; ++i) {
         const int P = (wave * kLoadsPerLane + i) * 64 + lane;
-        const int tok = (P < kChunks) ? P / kF8ChunksPerRow : kSlotTok;
-        const uint8_t* a = (tok < nval) ? src + P * 16 : p.zero_row + (P % kF8ChunksPerRow) * 16;
+        const int tok = (P * 3121) >> 17;
+        const int c = P - kRowChunksLds * tok;
+        const int cc = c < kF8ChunksPerRow ? c : 0;
+        const uint8_t* a = (tok < nval) ? src + (tok * kF8ChunksPerRow + cc) * 16 : p.zero_row + cc * 16;
         dma16(a, dst + i * 1024);
       }
     }
@@ -245,7 +257,7 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode_fp8(DecodeParams p
   // cb = 4*wave + c, all in latent group wave / 2.
   const int r8 = (lane & 15) >> 1;
   const int vtok = (r8 < 4) ? 4 * g + r8 : 12 + 4 * g + r8;
-  const int v_off = vtok * kF8Row + (lane & 1) * 8 + kCbPerWave * wave * 16;
+  const int v_off = vtok * kRowLds + (lane & 1) * 8 + kCbPerWave * wave * 16;
   const int pgrp = wave >> 1;
   // lane (n16, g) of a value wave reads granule g of P' row n16 of its group
   const int pb_rd = pgrp * (RG * 2 * 16 * 64) + n16 * 64 + ((g ^ ((n16 >> 1) & 3)) * 16);
@@ -273,7 +285,7 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode_fp8(DecodeParams p
 #pragma unroll
     for (int blk = 0; blk < NBLK; ++blk) {
       __builtin_amdgcn_sched_barrier(0);
-      lds_cu8* rowb = T + (tok0 + 16 * blk + n16) * kF8Row + g * 16;
+      lds_cu8* rowb = T + (tok0 + 16 * blk + n16) * kRowLds + g * 16;
       f32x4 sg[5];
 #pragma unroll
       for (int k = 0; k < 5; ++k) sg[k] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -307,7 +319,7 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode_fp8(DecodeParams p
       // combine the groups with the tokens' scales, scale, mask
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const f32x4 sc = *(lds_f32x4_t*)(T + (tok0 + 16 * blk + 4 * g + i) * kF8Row + kF8ScaleOff);
+        const f32x4 sc = *(lds_f32x4_t*)(T + (tok0 + 16 * blk + 4 * g + i) * kRowLds + kF8ScaleOff);
         float v = sg[4][i];
 #pragma unroll
         for (int k = 0; k < 4; ++k) v = fmaf(sc[k], sg[k][i], v);
@@ -349,7 +361,7 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode_fp8(DecodeParams p
       const int ks = t16 >> 5, bb = (t16 >> 4) & 1;
       f32x4 sc[4];   // the four group scales of token 4g + i of the block
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sc[i] = *(lds_f32x4_t*)(T + (t16 + 4 * g + i) * kF8Row + kF8ScaleOff);
+      for (int i = 0; i < 4; ++i) sc[i] = *(lds_f32x4_t*)(T + (t16 + 4 * g + i) * kRowLds + kF8ScaleOff);
       uint8_t* pw = pbuf + ((rg * 2 + ks) * 16 + n16) * 64 + ((g ^ ((n16 >> 1) & 3)) * 16) + bb * 8;
 #pragma unroll
       for (int G = 0; G < 4; ++G) {
@@ -369,7 +381,7 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode_fp8(DecodeParams p
       i32x2 cv[kCbPerWave];
 #pragma unroll
       for (int c = 0; c < kCbPerWave; ++c)
-        cv[c] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)(T + ks * 32 * kF8Row + v_off + c * 16));
+        cv[c] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)(T + ks * 32 * kRowLds + v_off + c * 16));
       bf16x8 pb[RG];
 #pragma unroll
       for (int r2 = 0; r2 < RG; ++r2) pb[r2] = *(const bf16x8*)(pbuf + pb_rd + (r2 * 2 + ks) * (16 * 64));
