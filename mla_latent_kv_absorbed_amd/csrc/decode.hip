@@ -121,8 +121,12 @@ __device__ __forceinline__ int tile_slot(int tok, int c) {
   return c < 64 ? (c ^ (tok & 15)) : (64 + ((c - 64) ^ ((tok >> 1) & 7)));
 }
 
+// The work of one workgroup: query tokens j0 .. j0 + QG - 1 (QG = 1 or 2)
+// against segment `unit`.  The LDS buffers are the kernel's (sized for
+// QG = 2), so that both instantiations called from one kernel share them.
 template <int QG, bool PAGED>
-__global__ void __launch_bounds__(kThreads, 1) splitkv_decode(DecodeParams p) {
+__device__ __forceinline__ void splitkv_body(const DecodeParams& p, int unit, int j0, uint8_t* ring, uint8_t* pbuf,
+                                             float* stat_lds, int* flags) {
   constexpr int RG = 2 * QG;           // row groups of 16 query rows
   constexpr int ROWS = 16 * RG;
   constexpr int TPW = kWaves / RG;     // score waves per row group
@@ -132,16 +136,8 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode(DecodeParams p) {
   static_assert((ROWS * kChunksPerRow) % (kQLoads * 64) == 0, "query rows fill whole waves' loads");
   static_assert(ROWS * kRowBytes <= kSlotLds, "query rows fit in a ring position");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[kSlots * kSlotLds];
-  // P in bf16, [row group][32-token step][row][32 tokens in MFMA k order];
-  // 16-byte granule q of row r is stored at granule q ^ ((r >> 1) & 3), so
-  // that the value product's 16-byte reads of rows 0..7 (and 8..15) fall on
-  // distinct banks (with q ^ ((r % 16) >> 2) rows r and r + 2 collided: the
-  // bank-conflict counter read 5.8 million cycles per verify 32x2 launch, now
-  // 0.13 million)
-  __shared__ __attribute__((aligned(16))) uint8_t pbuf[RG * 2 * 16 * 64];
-  __shared__ float stat[3][TPW][ROWS];   // per score wave and row: slot max, sum, true max
-  __shared__ int flags[kWaves];
+  // per score wave and row: slot max, sum, true max
+  float (*stat)[TPW][ROWS] = reinterpret_cast<float (*)[TPW][ROWS]>(stat_lds);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -149,16 +145,13 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode(DecodeParams p) {
   const int g = lane >> 4, n16 = lane & 15;
   const int rg = wave % RG, tq = wave / RG;   // score role: row group, token share
 
-  int unit, grp;   // segment (tokens [t_begin, t_end) of sequence b) and query group
-  work_item(p.groups, unit, grp);
-  if (unit >= p.segments) return;
-  const int4 seg = p.seg_desc[unit];
+  const int4 seg = p.seg_desc[unit];   // tokens [t_begin, t_end) of sequence b
   const int b = seg.x, t_begin = seg.y, t_end = seg.z, L = seg.w;
   if (b < 0 || t_begin >= t_end) return;   // no segment: the combine never reads it
 
-  // Query token of the score role's rows; a repeat of token Sq - 1 (computed,
-  // never written) fills the second half of the last group when Sq is odd.
-  const int j_grp = QG * grp + (rg >> 1);
+  // Query token of the score role's rows (j0 + QG <= Sq: a last group with
+  // fewer tokens runs as QG = 1).
+  const int j_grp = j0 + (rg >> 1);
   const int j = j_grp < p.Sq ? j_grp : p.Sq - 1;
   const int limit = min(t_end, L - p.Sq + j + 1);   // rows of this wave see tokens < limit
 
@@ -226,7 +219,7 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode(DecodeParams p) {
       const int P = (wave * kQLoads + i) * 64 + lane;
       const int r = P / kChunksPerRow;
       const int c = tile_slot(r, P - r * kChunksPerRow);
-      const int jj = min(QG * grp + (r >> 5), p.Sq - 1);
+      const int jj = min(j0 + (r >> 5), p.Sq - 1);
       const uint8_t* src = (const uint8_t*)p.qabs + (((size_t)b * p.Sq + jj) * 32 + (r & 31)) * kRowBytes + c * 16;
       dma16(src, dst + i * 1024);
     }
@@ -410,11 +403,11 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode(DecodeParams p) {
   }
 
   // ---- finalize: row r = r2*16 + n16 of the group is query token
-  // QG*grp + r/32, head r%32; partial rows [unit][j*32 + h][512] bf16
+  // j0 + r/32, head r%32; partial rows [unit][j*32 + h][512] bf16
   const size_t unit_rows = (size_t)unit * p.Sq * 32;
 #pragma unroll
   for (int r2 = 0; r2 < RG; ++r2) {
-    const int jr = QG * grp + (r2 >> 1);
+    const int jr = j0 + (r2 >> 1);
     if (jr >= p.Sq) continue;
     const int r = r2 * 16 + n16;
     float lrow = stat[1][0][r];
@@ -432,6 +425,33 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode(DecodeParams p) {
     if (tq == 0 && r2 == rg && g == 0)
       p.part_lse[unit_rows + (size_t)jr * 32 + (r & 31)] = (lrow > 0.f) ? m_ref + __log2f(lrow) : kNegInf;
   }
+}
+
+template <int QG, bool PAGED>
+__global__ void __launch_bounds__(kThreads, 1) splitkv_decode(DecodeParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kSlots * kSlotLds];
+  // P in bf16, [row group][32-token step][row][32 tokens in MFMA k order];
+  // 16-byte granule q of row r is stored at granule q ^ ((r >> 1) & 3), so
+  // that the value product's 16-byte reads of rows 0..7 (and 8..15) fall on
+  // distinct banks (with q ^ ((r % 16) >> 2) rows r and r + 2 collided: the
+  // bank-conflict counter read 5.8 million cycles per verify 32x2 launch, now
+  // 0.13 million)
+  __shared__ __attribute__((aligned(16))) uint8_t pbuf[2 * QG * 2 * 16 * 64];
+  __shared__ float stat[3 * kWaves * 16];   // [3][score waves per row group][rows of the group]
+  __shared__ int flags[kWaves];
+  int unit, grp;   // segment and query group
+  work_item(p.groups, unit, grp);
+  if (unit >= p.segments) return;
+  const int j0 = QG * grp;
+  if constexpr (QG > 1) {
+    // the last group of an odd Sq holds one token: its workgroups run the
+    // one-token body, instead of computing a repeat of the token beside it
+    if (j0 + 1 == p.Sq) {
+      splitkv_body<1, PAGED>(p, unit, j0, ring, pbuf, stat, flags);
+      return;
+    }
+  }
+  splitkv_body<QG, PAGED>(p, unit, j0, ring, pbuf, stat, flags);
 }
 
 }  // namespace

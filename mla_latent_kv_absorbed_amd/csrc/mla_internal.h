@@ -134,7 +134,7 @@ struct DecodeParams {
 // Query tokens per split-KV workgroup, and the number of such query groups
 // that cover Sq tokens.  A group of two keeps 64 query rows (4 row groups of
 // 16); a single query token uses 32 rows.  For odd Sq > 1 the last group
-// repeats token Sq - 1 in its second half and writes nothing for it.  The
+// holds one token, and its workgroups run as one-token workgroups.  The
 // 8-bit cache kernel takes one query token per workgroup: with two, its
 // per-wave registers (query rows, accumulators, widened codes) exceed what
 // two waves per SIMD leave.
