@@ -191,7 +191,7 @@ __device__ void build_schedule(const PrepParams& p, int* lds) {
 }
 
 // ---------------------------------------------------------------------------
-// Preparation of one decode call.  Grid (8 latent blocks of 64 + 2, 32
+// Preparation of one decode call.  Grid (8 latent blocks of 64 + 4 + 1, 32
 // heads, blocks of 16 query rows); row r = b*Sq + j.
 //  * Absorption (x < 8): Q_abs[r][h][64x .. 64x + 64) = bf16(W_UK[h]^T
 //    q_nope[r][h]) on those columns and the fp32 residual q_lat - bf16(q_lat)
@@ -201,20 +201,22 @@ __device__ void build_schedule(const PrepParams& p, int* lds) {
 //    columns [64x + 16w, 64x + 16w + 16) of the 16 rows with four steps of
 //    v_mfma_f32_16x16x32_bf16 (fp32 sums of exact bf16 products), the
 //    columns as A, the query rows as B.
-//  * Rope part and new tokens (x = 8, head h): Q_abs[r][h][512:576] = q_pe[r][h],
+//  * Rope part and new tokens (x = 8 .. 11, head h, a quarter of the block's
+//    rows each): Q_abs[r][h][512:576] = q_pe[r][h],
 //    rotated at the query's position p = L_b - Sq + j when `rotate` is set;
 //    with c_new given, head 0 writes the new tokens' latent into their cache
 //    rows (a bit copy, or quantised for the 8-bit format) and head 1 their
 //    rope keys (rotated at p).  These run beside the absorption instead of
 //    after it, since the fp64 angle arithmetic is long.
-//  * Workgroup (9, 0, 0) zeroes the decode kernel's zero row and builds the
+//  * Workgroup (12, 0, 0) zeroes the decode kernel's zero row and builds the
 //    split schedule (the other workgroups of that column exit at once).
 // ---------------------------------------------------------------------------
 constexpr int kWtStride = kNope + 8;   // bf16 per transposed W_UK column in LDS (272 bytes)
 constexpr int kPrepLds = 64 * kWtStride * 2;
 static_assert(kPrepLds >= (2 * kSchedLds + 1) * (int)sizeof(int), "schedule scratch");
-constexpr int kPrepRopeCol = kLatent / 64;       // grid column of the rope part and new tokens
-constexpr int kPrepSchedCol = kPrepRopeCol + 1;  // grid column of the schedule
+constexpr int kPrepRopeCol = kLatent / 64;       // first grid column of the rope part and new tokens
+constexpr int kPrepRopeCols = 4;                 // rope columns: 4 of the block's 16 rows each
+constexpr int kPrepSchedCol = kPrepRopeCol + kPrepRopeCols;   // grid column of the schedule
 
 // Position of query row r (clamped length) and its sequence.
 __device__ __forceinline__ int query_pos(const PrepParams& p, int r, int* b) {
@@ -329,8 +331,10 @@ __global__ void __launch_bounds__(256) prep_query(PrepParams p) {
     }
     return;
   }
-  if (cblk == kPrepRopeCol) {
-    prep_rope_and_rows(p, h, r0, r1);
+  if (cblk >= kPrepRopeCol) {
+    const int part = (p.rows_per_wg + kPrepRopeCols - 1) / kPrepRopeCols;
+    const int a = r0 + (cblk - kPrepRopeCol) * part;
+    prep_rope_and_rows(p, h, a, min(a + part, r1));
     return;
   }
   const int lane = t & 63, wave = t >> 6;
