@@ -409,7 +409,9 @@ __global__ void __launch_bounds__(256) prep_query(PrepParams p) {
 //  2. for every row, share[v] = sum over the block's columns of
 //     W_UV[h][v][c] o_lat[c] (W_UV[h] = w_kv_b rows [h*256 + 128, h*256 + 256))
 //     and the block's share of qres . o_lat go to the workspace; block 0
-//     also stores (M, W).
+//     also stores (M, W).  The shares of the RB rows are one matrix-core
+//     product (W_UV as A, the rows as B, each fp32 o_lat split into bf16
+//     hi + lo); on the vector units this product bounded the kernel.
 // finalize_out then adds the 8 shares in block order.
 // ---------------------------------------------------------------------------
 constexpr int kCombGroups = 16;
@@ -432,12 +434,18 @@ __global__ void __launch_bounds__(256) combine_blocks(CombineParams p) {
   const int rr = grp / gpr, gi = grp - rr * gpr;
   const int r = r0 + rr;
 
-  // W_UV[h][v][64 cb + 32 half .. + 32): thread (v, half), requested first
-  const int v = t >> 1, half = t & 1;
-  const uint16_t* wrow = p.w_kv_b + ((size_t)h * kWRowsPerHead + kNope + v) * kLatent + cb * 64 + 32 * half;
-  uint4 wu[4];
+  // A operands of the up-projection, requested first: wave w takes the 32
+  // values v = 32 w + 16 vt + n16 (vt = 0, 1), lane (g, n16) the columns
+  // 64 cb + 32 ks + 8 g .. + 8 of W_UV[h][v] (ks = 0, 1)
+  const int lane = t & 63, wave = t >> 6;
+  const int g = lane >> 4, n16 = lane & 15;
+  bf16x8 wa[2][2];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) wu[k] = *(const uint4*)(wrow + 8 * k);
+  for (int vt = 0; vt < 2; ++vt)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      wa[vt][ks] = *(const bf16x8*)(p.w_kv_b + ((size_t)h * kWRowsPerHead + kNope + 32 * wave + 16 * vt + n16) * kLatent +
+                                    cb * 64 + 32 * ks + 8 * g);
   // qres of row t / 16 of the block, 4 columns
   float4 qr = make_float4(0.f, 0.f, 0.f, 0.f);
   if (t < 16 * RB && r0 + (t >> 4) < rows)
@@ -527,22 +535,33 @@ __global__ void __launch_bounds__(256) combine_blocks(CombineParams p) {
   }
   __syncthreads();
 
-  for (int rr2 = 0; rr2 < RB; ++rr2) {
-    const int r2 = r0 + rr2;
-    if (r2 >= rows) break;
-    float up = 0.f;
+  // share^T[v][row] = sum over the block's columns of W_UV[h][v][c] o_lat[row][c]
+  // on the matrix cores: B = the block's rows (row n16, zero past RB), each
+  // fp32 value split into bf16 hi + lo (hi + lo equals it to 16 significant
+  // bits), one product for each, fp32 sums
+  bf16x8 bhi[2], blo[2];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t wd[4] = {wu[k].x, wu[k].y, wu[k].z, wu[k].w};
+  for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int c = 32 * half + 8 * k + 2 * e;
-        up = fmaf(__uint_as_float(wd[e] << 16), olat[rr2][c], up);
-        up = fmaf(__uint_as_float(wd[e] & 0xFFFF0000u), olat[rr2][c + 1], up);
-      }
+    for (int e = 0; e < 8; ++e) {
+      const float x = (n16 < RB) ? olat[n16 < RB ? n16 : 0][32 * ks + 8 * g + e] : 0.f;
+      const uint16_t hb = f32_to_bf16(x);
+      bhi[ks][e] = __builtin_bit_cast(__bf16, hb);
+      blo[ks][e] = __builtin_bit_cast(__bf16, f32_to_bf16(x - bf16_to_f32(hb)));
     }
-    up += __shfl_xor(up, 1, 2);
-    if (half == 0) p.up_part[(((size_t)r2 * kHeads + h) * 8 + cb) * kVDim + v] = up;
+  }
+  const int r2 = r0 + n16;
+#pragma unroll
+  for (int vt = 0; vt < 2; ++vt) {
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[vt][ks], bhi[ks], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[vt][ks], blo[ks], acc, 0, 0, 0);
+    }
+    // lane (g, n16): row r0 + n16, values 32 w + 16 vt + 4 g .. + 4
+    if (n16 < RB && r2 < rows)
+      *(f32x4*)(p.up_part + (((size_t)r2 * kHeads + h) * 8 + cb) * kVDim + 32 * wave + 16 * vt + 4 * g) = acc;
   }
 }
 
