@@ -247,6 +247,9 @@ FUSED = [
     (1, (1, 65, 700)),
     (2, (2, 130, 64)),
     (3, (3, 200)),
+    # 35 query rows: three 16-row blocks of the preparation kernel, whose four
+    # rope columns take 4 rows each (the last block's partly empty)
+    (5, (5, 70, 300, 64, 129, 200, 1000)),
 ]
 
 
