@@ -56,6 +56,7 @@ typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2_t;
 typedef __attribute__((address_space(3))) const i32x4 lds_i32x4_t;
 typedef __attribute__((address_space(3))) const uint8_t lds_cu8;
@@ -113,9 +114,14 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(i32x2 w) {
   return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-// Chunk <-> row position swizzle of the bf16 query rows (as in decode.hip).
-__device__ __forceinline__ int tile_slot(int tok, int c) {
-  return c < 64 ? (c ^ (tok & 15)) : (64 + ((c - 64) ^ ((tok >> 1) & 7)));
+
+// One latent group's scores on the 8-bit matrix path: codes (unit scale) times
+// the query's hi and lo pieces, whose block scales are byte K of sh and sl.
+template <int K>
+__device__ __forceinline__ f32x4 mfma_q8(const i32x8& a, const i32x8& qh, const i32x8& ql, uint32_t sh, uint32_t sl,
+                                         f32x4 c) {
+  c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qh, c, 0, 0, 0, 127, K, (int)sh);
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, ql, c, 0, 0, 0, 127, K, (int)sl);
 }
 
 template <int QG, bool PAGED>
@@ -125,9 +131,9 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode_fp8(DecodeParams p
   constexpr int TPW = kWaves / RG;     // score waves per row group
   constexpr int TOKW = kSlotTok / TPW; // tokens of each slot one score wave handles
   constexpr int NBLK = TOKW / 16;      // 16-token score blocks per slot and wave
-  constexpr int NQ = ROWS * kChunksPerRow / kDmaLanes;   // query-row loads per DMA lane
-  static_assert(NQ * kDmaLanes == ROWS * kChunksPerRow, "query rows split");
-  static_assert(ROWS * kRowBytes <= (kSlots - 1) * kSlotLds, "query rows fit in ring positions 1..2");
+  constexpr int NQ = ROWS * (kQRecBytes / 16) / kDmaLanes;   // query-record loads per DMA lane
+  static_assert(NQ * kDmaLanes * 16 == ROWS * kQRecBytes, "query records split");
+  static_assert(ROWS * kQRecBytes <= (kSlots - 1) * kSlotLds, "query records fit in ring positions 1..2");
 
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kSlots * kSlotLds];
   // P'_G = bf16(p * scale_G) for the four latent groups G, [G][row group]
@@ -214,38 +220,44 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode_fp8(DecodeParams p
     }
   };
 
-  // Score reads of the bf16 query rows (swizzled like bf16 cache tiles): the
-  // codes of a row are read 16 bytes a lane, lane g taking latent columns
-  // 64m + 16g .. 64m + 16g + 15 of 64-column block m, whose halves are MFMA
-  // steps 2m and 2m + 1; so step ks needs query chunk c = 8(ks/2) + 2g + ks%2,
-  // stored at c ^ n16.  Rope chunks 64 + ((4kk + g) ^ (n16 >> 1)).
-  auto q_chunk = [&](int ks) -> int {
-    return n16 * kRowBytes + (ks < 16 ? (((8 * (ks >> 1) + 2 * g + (ks & 1)) ^ n16) << 4)
-                                      : ((64 + ((4 * (ks - 16) + g) ^ (n16 >> 1))) << 4));
-  };
 
-  // ---- prologue: the query rows (row r of the group as "token" r, bf16,
-  // swizzled) into ring positions 1..2, the first slot into position 0
+  // ---- prologue: the 32 query records of the group (head order, kQRecBytes
+  // each, contiguous in the workspace) into ring positions 1..2, copied
+  // linearly, the first slot into position 0
   if (dma_wave) {
     const uint32_t dst = ring_lds + kSlotLds + wave * NQ * 1024;
+    const uint8_t* src = (const uint8_t*)p.qabs + ((size_t)b * p.Sq + QG * grp) * 32 * kQRecBytes;
 #pragma unroll
-    for (int i = 0; i < NQ; ++i) {
-      const int P = (wave * NQ + i) * 64 + lane;
-      const int r = P / kChunksPerRow;
-      const int c = tile_slot(r, P - r * kChunksPerRow);
-      const int jj = min(QG * grp + (r >> 5), p.Sq - 1);
-      const uint8_t* src = (const uint8_t*)p.qabs + (((size_t)b * p.Sq + jj) * 32 + (r & 31)) * kRowBytes + c * 16;
-      dma16(src, dst + i * 1024);
-    }
+    for (int i = 0; i < NQ; ++i) dma16(src + ((wave * NQ + i) * 64 + lane) * 16, dst + i * 1024);
   }
   issue(s0, 0);
   wait_slots_ahead(1);   // the query rows (older than the first slot) have landed
   lds_barrier();
-  bf16x8 q[18];   // this wave's 16 query rows as MFMA B operands: lane holds row n16, 8 dims
+  // This wave's 16 query rows as MFMA B operands, lane (g, n16) holding row
+  // n16: for latent group k the E4M3 pieces of columns 128k + 16g .. + 16 and
+  // 128k + 64 + 16g .. + 16 (the columns of the cache codes the lane reads;
+  // the matrix instruction pairs element i of A and B lanes of one group, and
+  // takes the scale of the 32 columns 128k + 32b .. of row n from lane
+  // (b, n)), the scale bytes of blocks 4k + g for k = 0..3 in one register,
+  // and the bf16 rope part (dims 8 (4kk + g) .. + 8).
+  i32x8 qh[4], ql[4];
+  bf16x8 qrope[2];
+  uint32_t qsh, qsl;
   {
-    const uint8_t* qb = ring + kSlotLds + rg * 16 * kRowBytes;
+    const uint8_t* qb = ring + kSlotLds + (rg * 16 + n16) * kQRecBytes;
 #pragma unroll
-    for (int ks = 0; ks < 18; ++ks) q[ks] = *(const bf16x8*)(qb + q_chunk(ks));
+    for (int k = 0; k < 4; ++k) {
+      const i32x4 h0 = *(const i32x4*)(qb + kQRecHi + 128 * k + 16 * g);
+      const i32x4 h1 = *(const i32x4*)(qb + kQRecHi + 128 * k + 64 + 16 * g);
+      const i32x4 l0 = *(const i32x4*)(qb + kQRecLo + 128 * k + 16 * g);
+      const i32x4 l1 = *(const i32x4*)(qb + kQRecLo + 128 * k + 64 + 16 * g);
+      qh[k] = i32x8{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+      ql[k] = i32x8{l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) qrope[kk] = *(const bf16x8*)(qb + kQRecRope + (4 * kk + g) * 16);
+    qsh = *(const uint32_t*)(qb + kQRecScaleOff + 4 * g);
+    qsl = qsh - 0x04040404u;   // lo pieces carry a factor 16 (scale bytes are at least 4)
   }
   lds_barrier();   // every wave has its query rows before slots 1..2 overwrite them
   const int pro = min(kSlots, nslot);
@@ -299,11 +311,14 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode_fp8(DecodeParams p
           for (int i = 0; i < 2; ++i) nxt[i] = *(const lds_i32x4_t*)(rowb + (2 * (k + 1) + i) * 64);
         }
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const i32x4 w = cur[i >> 1];
-          const i32x2 h = (i & 1) ? i32x2{w[2], w[3]} : i32x2{w[0], w[1]};
-          sg[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(h), q[4 * k + i], sg[k], 0, 0, 0);
+        {
+          // codes x (hi + lo / 16) * 2^-e on the 8-bit matrix path: the codes
+          // with unit scale (127), the query pieces with their block scales
+          const i32x8 a = i32x8{cur[0][0], cur[0][1], cur[0][2], cur[0][3], cur[1][0], cur[1][1], cur[1][2], cur[1][3]};
+          sg[k] = k == 0 ? mfma_q8<0>(a, qh[k], ql[k], qsh, qsl, sg[k])
+                  : k == 1 ? mfma_q8<1>(a, qh[k], ql[k], qsh, qsl, sg[k])
+                  : k == 2 ? mfma_q8<2>(a, qh[k], ql[k], qsh, qsl, sg[k])
+                           : mfma_q8<3>(a, qh[k], ql[k], qsh, qsl, sg[k]);
         }
         __builtin_amdgcn_sched_barrier(0);
         if (k < 3) {
@@ -314,7 +329,7 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode_fp8(DecodeParams p
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const bf16x8 rp = *(lds_bf16x8_t*)(rowb + kF8RopeOff + kk * 64);
-        sg[4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rp, q[16 + kk], sg[4], 0, 0, 0);
+        sg[4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rp, qrope[kk], sg[4], 0, 0, 0);
       }
       // combine the groups with the tokens' scales, scale, mask
 #pragma unroll

@@ -253,14 +253,15 @@ __device__ void prep_rope_and_rows(const PrepParams& p, int h, int r0, int r1) {
       const uint16_t* src = p.q_pe + hrow * kRope;
       uint16_t lo, hi;
       rope_pair(src[k], src[k + half], (double)pos * p.inv.v[k], &lo, &hi);
-      uint16_t* dst = p.qabs + hrow * kRow + kLatent;
+      uint16_t* dst = p.fp8 ? (uint16_t*)((uint8_t*)p.qabs + hrow * kQRecBytes + kQRecRope) : p.qabs + hrow * kRow + kLatent;
       dst[k] = lo;
       dst[k + half] = hi;
     }
   } else {
     for (int i = t; i < (r1 - r0) * kRope; i += 256) {
       const size_t hrow = (size_t)(r0 + i / kRope) * kHeads + h;
-      p.qabs[hrow * kRow + kLatent + i % kRope] = p.q_pe[hrow * kRope + i % kRope];
+      uint16_t* dst = p.fp8 ? (uint16_t*)((uint8_t*)p.qabs + hrow * kQRecBytes + kQRecRope) : p.qabs + hrow * kRow + kLatent;
+      dst[i % kRope] = p.q_pe[hrow * kRope + i % kRope];
     }
   }
   if (p.c_new == nullptr || h > 1) return;
@@ -319,6 +320,7 @@ __device__ void prep_rope_and_rows(const PrepParams& p, int h, int r0, int r1) {
 
 __global__ void __launch_bounds__(256) prep_query(PrepParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kPrepLds];
+  __shared__ float bmax[4][16];   // 8-bit records: each wave's 16-column row maxima
   const int cblk = blockIdx.x;
   const int h = blockIdx.y;
   const int r0 = blockIdx.z * p.rows_per_wg;
@@ -377,19 +379,56 @@ __global__ void __launch_bounds__(256) prep_query(PrepParams p) {
   for (int ks = 0; ks < kNope / 32; ++ks)
     d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(arow + 64 * ks), qb[ks], d, 0, 0, 0);
   // lane (g, n16) holds row r0 + n16, columns 64 cblk + 16 w + 4 g + i
-  if (rq < p.rows) {
-    const size_t hrow = (size_t)rq * kHeads + h;
-    const int col = cblk * 64 + 16 * wave + 4 * g;
-    s16x4 qv;
-    f32x4 res;
+  const size_t hrow = (size_t)rq * kHeads + h;
+  const int col = cblk * 64 + 16 * wave + 4 * g;
+  s16x4 qv;
+  f32x4 res, qf;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint16_t qbits = f32_to_bf16(d[i]);
-      qv[i] = (short)qbits;
-      res[i] = d[i] - bf16_to_f32(qbits);
+  for (int i = 0; i < 4; ++i) {
+    const uint16_t qbits = f32_to_bf16(d[i]);
+    qv[i] = (short)qbits;
+    qf[i] = bf16_to_f32(qbits);
+    res[i] = d[i] - qf[i];
+  }
+  if (!p.fp8) {
+    if (rq < p.rows) {
+      *(s16x4*)(p.qabs + hrow * kRow + col) = qv;
+      *(f32x4*)(p.qres + hrow * kLatent + col) = res;
     }
-    *(s16x4*)(p.qabs + hrow * kRow + col) = qv;
+    return;
+  }
+  // The 8-bit cache kernel's record: bf16(q) = (hi + lo / 16) * 2^-e for the
+  // 32-column block of waves 2m, 2m + 1, with e = 7 - exponent(block max), so
+  // |q| * 2^e < 256; hi is q * 2^e rounded to E4M3, lo the remainder times 16
+  // rounded to E4M3 (exact for every value above 2^-13 of the block max).
+  float m = fmaxf(fmaxf(fabsf(qf[0]), fabsf(qf[1])), fmaxf(fabsf(qf[2]), fabsf(qf[3])));
+  m = fmaxf(m, __shfl_xor(m, 16, 64));
+  m = fmaxf(m, __shfl_xor(m, 32, 64));
+  if (g == 0) bmax[wave][n16] = m;
+  __syncthreads();
+  const float bm = fmaxf(bmax[wave & ~1][n16], bmax[wave | 1][n16]);
+  const int E = (int)((__float_as_uint(bm) >> 23) & 0xFFu) - 127;
+  const bool zero = !(bm >= 1.17549435e-38f) || E < -116;   // zero, subnormal or below 2^-116: all zero codes
+  const int e = 7 - E;
+  const float f = zero ? 0.f : __uint_as_float((uint32_t)(127 + e) << 23);
+  uint32_t hw = 0u, lw = 0u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float x = qf[i] * f;   // exact: a power of two
+    const uint32_t hc = f32_to_e4m3(x);
+    const uint32_t lc = f32_to_e4m3((x - e4m3_to_f32(hc)) * 16.0f);
+    hw |= hc << (8 * i);
+    lw |= lc << (8 * i);
+  }
+  if (rq < p.rows) {
+    uint8_t* rec = (uint8_t*)p.qabs + hrow * kQRecBytes;
+    *(uint32_t*)(rec + kQRecHi + col) = hw;
+    *(uint32_t*)(rec + kQRecLo + col) = lw;
     *(f32x4*)(p.qres + hrow * kLatent + col) = res;
+    if (g == 0 && (wave & 1) == 0) {
+      const int bi = col / 32;
+      rec[kQRecScaleOff + 4 * (bi % 4) + bi / 4] = (uint8_t)(zero ? 127 : 127 - e);
+    }
   }
 }
 

@@ -32,6 +32,20 @@ constexpr int kF8Group = 128;
 constexpr int kF8Tile = kPage * kF8Row;         // 41984 bytes per page
 constexpr float kE4M3Max = 448.0f;
 
+// The absorbed query row of one (query token, head) as the 8-bit cache kernel
+// takes it (kQRecBytes per head row): the bf16 latent part q split exactly
+// into two E4M3 pieces with a power-of-two scale per 32 columns,
+//     q[c] = (hi[c] + lo[c] / 16) * 2^(s_b - 127),   b = c / 32,
+// then the rope part in bf16 and the 16 scale bytes s_b (E8M0), stored at
+// kQRecScaleOff + 4 (b % 4) + b / 4.  The bf16 kernel takes the same region
+// as bf16 rows of kRow values.
+constexpr int kQRecHi = 0;
+constexpr int kQRecLo = kLatent;                       // 512
+constexpr int kQRecRope = 2 * kLatent;                 // 1024: bf16 [64]
+constexpr int kQRecScaleOff = kQRecRope + 2 * kRope;   // 1152
+constexpr int kQRecBytes = 1280;                       // 80 sixteen-byte chunks
+static_assert(kQRecScaleOff + 16 <= kQRecBytes && kQRecBytes >= kRowBytes, "query record");
+
 // Fault bits of the per-device fault word (values as MLA_FAULT_* in mla.h).
 // A kernel that meets an index outside its documented range skips or clamps
 // that item, so that every access stays inside the caller's buffers, and ORs
@@ -74,7 +88,8 @@ constexpr int kMinTilesPerSplit = 2;
 // Workspace layout of one decode call (byte offsets, each 256-aligned).
 // rows = B * Sq query tokens; a "head row" is one (query token, head).
 struct WorkspaceLayout {
-  size_t qabs;      // bf16 [rows][32][576]: [W_UK^T q_nope | rotated q_pe]
+  size_t qabs;      // [rows][32] query rows of kQRecBytes: bf16 [W_UK^T q_nope | rotated q_pe]
+                    // at a kRow stride (bf16 cache), or the 8-bit kernel's records
   size_t qres;      // fp32 [rows][32][512]: W_UK^T q_nope - bf16(W_UK^T q_nope)
   size_t part_o;    // bf16 [max_segs][Sq*32][512]: normalised segment partials
   size_t part_lse;  // fp32 [max_segs][Sq*32], log2 domain
@@ -94,7 +109,7 @@ inline WorkspaceLayout workspace_layout(int B, int Sq, int max_segs) {
   const size_t seq_rows = size_t(Sq) * kHeads;
   const size_t hrows = size_t(B) * seq_rows;
   size_t off = 0;
-  w.qabs = off;      off = align256(off + hrows * kRow * 2);
+  w.qabs = off;      off = align256(off + hrows * kQRecBytes);
   w.qres = off;      off = align256(off + hrows * kLatent * 4);
   w.part_o = off;    off = align256(off + size_t(max_segs) * seq_rows * kLatent * 2);
   w.part_lse = off;  off = align256(off + size_t(max_segs) * seq_rows * 4);
@@ -181,6 +196,14 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
     code = code > 0x7Eu ? 0x7Eu : code;              // 448 is the largest finite code
   }
   return code | sign;
+}
+
+// The value of an OCP FP8 E4M3 code (finite codes).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
+  const uint32_t e = (code >> 3) & 15u, m = code & 7u;
+  const float a = e == 0 ? (float)m * 0.001953125f                        // m * 2^-9
+                         : __uint_as_float(((e + 120u) << 23) | (m << 20));  // (1 + m/8) * 2^(e - 7)
+  return (code & 0x80u) ? -a : a;
 }
 
 // Everything that precedes the split-KV pass: the absorbed query rows, the
