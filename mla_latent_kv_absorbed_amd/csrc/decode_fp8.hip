@@ -7,14 +7,16 @@
 // on the dequantised latent c = code * scale:
 //     s_t = scale_softmax * (sum_g scale_{t,g} (q_lat,g . code_{t,g}) + q_pe . k_pe_t)
 //     O   = sum_t p_t sum_g scale_{t,g} code_{t,g} / sum_t p_t
-// E4M3 values are exact in bf16, so both products stay on bf16 MFMA.  The
-// work is split as in the bf16 kernel (8 waves, two per SIMD; scores by row
-// group and token share, the value product by latent columns, P through LDS):
-//  * scores: the codes of 64 latent columns are read as 16 bytes per lane
-//    (ds_read_b128), two MFMA steps, and widened to bf16 exactly; each
-//    128-column group has its own score accumulator, and the four are
-//    combined with the tokens' scales (the rope part has its own
-//    accumulator, unscaled);
+// The work is split as in the bf16 kernel (8 waves, two per SIMD; scores by
+// row group and token share, the value product by latent columns, P through
+// LDS):
+//  * scores: the codes of a 128-column group are read as 32 bytes per lane
+//    (two ds_read_b128) and multiplied on the 8-bit matrix path
+//    (v_mfma_scale_f32_16x16x128_f8f6f4) by the absorbed query, which the
+//    preparation kernel split exactly into two E4M3 pieces with a
+//    power-of-two scale per 32 columns (the instruction's block scales);
+//    each group has its own score accumulator, and the four are combined
+//    with the tokens' scales (the rope part has its own bf16 accumulator);
 //  * values: O^T = C^T P'^T with P'_g = bf16(p * scale_{t,g}) for the
 //    columns of group g: the score waves write P'_g of all four groups to
 //    LDS, and each value wave (its 64 columns lie in one group) reads its
@@ -22,10 +24,11 @@
 //    read ds_read_b64_tr_b8
 //    (lanes 2r, 2r+1 of a 16-lane group supply the two halves of row r's 16
 //    bytes; lane i receives byte i of rows 0..7), which gives each lane 8
-//    tokens of one column in the MFMA k order, and widened to bf16 exactly.
+//    tokens of one column in the MFMA k order, and widened to bf16 exactly
+//    (E4M3 values are exact in bf16) for v_mfma_f32_16x16x32_bf16.
 // Slots of 64 tokens (41,984 bytes) stream through a three-slot LDS ring, so
 // two slots are in flight while one is consumed; waves 0-3 issue the direct
-// loads.  The query rows arrive the same way ahead of the first slot.  A
+// loads.  The query records arrive the same way ahead of the first slot.  A
 // workgroup serves one query token (32 rows); several query tokens of a
 // split are served by workgroups that read the split together (work_item).
 // The kernel is instantiated for QG = 1 only.
