@@ -192,3 +192,35 @@ def test_fp8_fullsize_verify_b32_sq2():
         s = compare(go[b], gl[b], ref_o, ref_l)
         print(f"fp8 verify 32x2 seq {b} (L={wl.lens[b]}): max_abs={s[0]:.3e} rel_l2={s[1]:.3e} lse={s[2]:.3e}",
               flush=True)
+
+
+def test_fp8_query_pieces_over_extreme_block_scales():
+    # The 8-bit kernel takes the absorbed query as two E4M3 pieces with a
+    # power-of-two scale per 32 columns.  Heads whose query is zero, below the
+    # pieces' range (2^-120: taken as zero), small (2^-30) or large (2^3), and
+    # one 32-column block of head 4's W_UK scaled by 2^-60 (a block far below
+    # its row's others), against the oracle on the same inputs.
+    lens = (70, 300)
+    sq = 2
+    wl = Workload(102, "fp8-qscale", len(lens), sq, 1, lens, True)
+    dw = DeviceWorkload(wl, kv_chunk=64, cache_dtype="fp8")
+    li = dw.build_layer(0)
+    qscale = {0: 0.0, 1: 2.0 ** -120, 2: 2.0 ** -30, 3: 2.0 ** 3}
+    qn_host = li.q_nope.double().cpu()
+    for h, f in qscale.items():
+        qn_host[:, :, h] *= f
+    li.q_nope.copy_(qn_host.to(torch.bfloat16))
+    li.w_kv_b.view(32, 256, 512)[4, :128, 64:96] *= 2.0 ** -60
+    lse = torch.empty((len(lens), sq, 32), dtype=torch.float32, device=DEV)
+    out, lse = dw.step(li, lse=lse)
+    torch.cuda.synchronize()
+    go, gl = gpu_out(out), lse.cpu().numpy()
+    w = weights(wl.seed, 0).copy()
+    w.reshape(32, 256, 512)[4, :128, 64:96] *= 2.0 ** -60
+    for b, L in enumerate(lens):
+        qn, qp, c, k = sequence_inputs_fp8(wl.seed, 0, L, sq, b)
+        for h, f in qscale.items():
+            qn[:, h] *= f
+        ref_o, ref_l = O.mla_attention_unabsorbed(qn, qp, c, k, w, O.softmax_scale())
+        s = compare(go[b], gl[b], ref_o, ref_l)
+        print(f"fp8 query scales seq {b}: max_abs={s[0]:.3e} rel_l2={s[1]:.3e} lse={s[2]:.3e}", flush=True)
