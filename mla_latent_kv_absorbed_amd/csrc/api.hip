@@ -46,7 +46,7 @@ const DeviceSymbols* device_symbols() {
 }
 
 constexpr int kMaxSq = 16;
-constexpr int64_t kMaxRows = 65535;   // B * Sq: one grid dimension of the combine
+constexpr int64_t kMaxRows = 65535;   // B * Sq: the supported range of query rows per call
 
 // Opt-in kernel timing (mla_timing_*): event pairs around split-KV launches.
 struct Timing {

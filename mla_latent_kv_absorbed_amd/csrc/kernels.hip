@@ -436,8 +436,8 @@ __global__ void __launch_bounds__(256) prep_query(PrepParams p) {
 // LSE combine of the segment partials with this column block's share of the
 // W_UV up-projection.  Grid (8 latent blocks of 64 columns, 32 heads, blocks
 // of RB query rows); a workgroup of 256 threads handles head h of rows
-// r0 .. r0 + RB - 1 on columns [64 cb, 64 cb + 64), RB = rows_per_wg (a power
-// of two from 2 to 16; calls with one row per workgroup take combine_one_row
+// r0 .. r0 + RB - 1 on columns [64 cb, 64 cb + 64), RB = rows_per_wg (16, the
+// one instantiation; calls with one row per workgroup take combine_one_row
 // below), so that the block's W_UV share is read once for RB rows:
 //  1. 16 groups of 16 lanes, 16 / RB groups per row; the groups of a row take
 //     every (16 / RB)-th of its sequence's segments, 16 per batch with every
@@ -864,13 +864,8 @@ hipError_t launch_combine_upproject(const CombineParams& p, hipStream_t stream) 
   const unsigned rows = (unsigned)(p.hrows / kHeads);
   const unsigned rblocks = (rows + p.rows_per_wg - 1) / p.rows_per_wg;
   const dim3 grid(kLatent / 64, kHeads, rblocks);
-  switch (p.rows_per_wg) {
-    case 1: hipLaunchKernelGGL(combine_one_row, grid, dim3(256), 0, stream, p); break;
-    case 2: hipLaunchKernelGGL(combine_blocks<2>, grid, dim3(256), 0, stream, p); break;
-    case 4: hipLaunchKernelGGL(combine_blocks<4>, grid, dim3(256), 0, stream, p); break;
-    case 8: hipLaunchKernelGGL(combine_blocks<8>, grid, dim3(256), 0, stream, p); break;
-    default: hipLaunchKernelGGL(combine_blocks<16>, grid, dim3(256), 0, stream, p); break;
-  }
+  if (p.rows_per_wg == 1) hipLaunchKernelGGL(combine_one_row, grid, dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL(combine_blocks<kCombRowsMax>, grid, dim3(256), 0, stream, p);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   hipLaunchKernelGGL(finalize_out, dim3((unsigned)((p.hrows + 1) / 2)), dim3(256), 0, stream, p);
   return hipGetLastError();

@@ -264,16 +264,13 @@ struct CombineParams {
 };
 
 // Query rows per workgroup of the preparation kernel: one 16-row tile of
-// its matrix-core absorption.  Query rows per workgroup of the combine:
-// enough rows that W_UV (4 MiB) is not read once per query row from L2 when
-// a call has many rows, few enough that a call with few rows still spreads
-// over the compute units; powers of two up to 16.
+// its matrix-core absorption.  Query rows per workgroup of the combine: 16
+// from 16 rows on (one matrix-core tile of the up-projection, W_UV read once
+// per 16 rows; 4 rows per workgroup measured 1.3% slower per paged 16x64K
+// layer), else one (combine_one_row, which spreads a few rows over more
+// compute units).
 inline int prep_rows_per_wg(int) { return 16; }
-inline int combine_rows_per_wg(int rows) {
-  int rb = 1;
-  while (rb < 16 && 8 * rb <= rows) rb *= 2;
-  return rb;
-}
+inline int combine_rows_per_wg(int rows) { return rows >= 16 ? 16 : 1; }
 
 // Launchers (each enqueues on `stream`; return hipError_t of the launch).
 // ev_start / ev_stop (may be null): recorded by the dispatches themselves at

@@ -299,7 +299,7 @@ def test_balanced_schedule_over_many_short_sequences():
 
 
 def test_widest_batch_takes_the_schedules_serial_path():
-    # B * Sq = 4095 * 16 = 65,520 rows (the combine's grid allows 65,535) and
+    # B * Sq = 4095 * 16 = 65,520 rows (calls accept up to 65,535) and
     # B > 2,048 sequences, so the device schedule takes its serial path;
     # short ragged contexts, the balanced and a fixed split; a sample of
     # sequences (both sides of 2,048 among them) against the oracle.
