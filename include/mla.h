@@ -178,7 +178,10 @@ mla_status mla_cache_append(const mla_shape* shape /* host */, void* cache, int6
  *   max_ctx_len  host upper bound of ctx_lens, <= stride_tokens
  *   kv_chunk     tokens per split, a multiple of 64, or 0 to let the
  *                library choose (splits sized from the actual ctx_lens on the
- *                device, about one workgroup per compute unit).  When the
+ *                device, about one workgroup per compute unit; a sequence
+ *                with 16 or more such splits deals its 64-token tiles out to
+ *                them in turn, so a split is then not a contiguous range; the
+ *                result differs only by rounding).  When the
  *                chunks of a call are fewer than the device's compute units
  *                (per query group), each chunk is cut into 2^k equal
  *                sub-splits of at least 128 tokens, within that count; the

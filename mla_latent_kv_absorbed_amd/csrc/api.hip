@@ -254,7 +254,7 @@ mla_status decode_common(const mla_shape* shape, const StepInputs& step, const v
   pp.fixed_tiles = kv_chunk / kPage;
   pp.target_segs = std::max(1, target / groups);   // about one workgroup per compute unit
   pp.max_segs = (int)segs;
-  pp.seg_desc = (int4*)(ws + wl.seg_desc);
+  pp.seg_desc = (SegDesc*)(ws + wl.seg_desc);
   pp.seg_start = (int32_t*)(ws + wl.seg_start);
   if (launch_prep(pp, s) != hipSuccess) return MLA_ERR_DEVICE;
 

@@ -145,15 +145,15 @@ __device__ __forceinline__ void splitkv_body(const DecodeParams& p, int unit, in
   const int g = lane >> 4, n16 = lane & 15;
   const int rg = wave % RG, tq = wave / RG;   // score role: row group, token share
 
-  const int4 seg = p.seg_desc[unit];   // tokens [t_begin, t_end) of sequence b
-  const int b = seg.x, t_begin = seg.y, t_end = seg.z, L = seg.w;
-  if (b < 0 || t_begin >= t_end) return;   // no segment: the combine never reads it
+  const SegDesc seg = p.seg_desc[unit];   // slots first + i * stride (i < ntiles) of sequence b
+  const int b = seg.b, L = seg.L;
+  if (b < 0 || seg.ntiles < 1) return;   // no segment: the combine never reads it
 
   // Query token of the score role's rows (j0 + QG <= Sq: a last group with
   // fewer tokens runs as QG = 1).
   const int j_grp = j0 + (rg >> 1);
   const int j = j_grp < p.Sq ? j_grp : p.Sq - 1;
-  const int limit = min(t_end, L - p.Sq + j + 1);   // rows of this wave see tokens < limit
+  const int limit = L - p.Sq + j + 1;   // rows of this wave see tokens < limit
 
   // Slot loads: wave-wide load I of a slot fills LDS bytes [1024 I,
   // 1024 (I + 1)) of the ring position; waves 0..1 issue loads 10w .. 10w + 9,
@@ -173,15 +173,15 @@ __device__ __forceinline__ void splitkv_body(const DecodeParams& p, int unit, in
   }
   const uint32_t ring_lds = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)ring);
 
-  const int s0 = t_begin / kSlotTok;                    // first slot index of the split
-  const int nslot = (t_end - t_begin + kSlotTok - 1) / kSlotTok;
+  const int nslot = seg.ntiles;
+  auto slot_at = [&](int i) { return seg.first + i * seg.stride; };   // absolute slot index
 
-  // Enqueue the split's slot `ts` (absolute slot index) into ring slot
-  // `r`; rows past the end of the split come from the zero row, so masked
-  // tokens multiply zeros.
+  // Enqueue slot `ts` (absolute slot index) of the sequence into ring slot
+  // `r`; rows at or past L come from the zero row, so masked tokens
+  // multiply zeros.
   auto issue = [&](int ts, int r) {
     const uint8_t* src;
-    int nval = min(kSlotTok, t_end - ts * kSlotTok);
+    int nval = min(kSlotTok, L - ts * kSlotTok);
     if constexpr (PAGED) {
       const int page = p.block_table[(size_t)b * p.max_pages + ts];
       src = p.cache + (size_t)page * kTileBytes;
@@ -224,7 +224,7 @@ __device__ __forceinline__ void splitkv_body(const DecodeParams& p, int unit, in
       dma16(src, dst + i * 1024);
     }
   }
-  issue(s0, 0);
+  issue(slot_at(0), 0);
   wait_slots_ahead(wide, 1);   // the query rows (older than the first slot) have landed
   lds_barrier();
   bf16x8 q[18];   // this wave's 16 query rows as MFMA B operands: lane holds row n16, 8 dims
@@ -239,7 +239,7 @@ __device__ __forceinline__ void splitkv_body(const DecodeParams& p, int unit, in
     }
   }
   lds_barrier();   // every wave has its query rows before the second slot overwrites them
-  if (nslot > 1) issue(s0 + 1, 1);
+  if (nslot > 1) issue(slot_at(1), 1);
 
   // Score reads of a slot: token n16 of a 16-token block, chunk 4*ks + g
   // (rope chunks 64 + 4kk + g follow the latent ones): one base per lane.
@@ -370,8 +370,8 @@ __device__ __forceinline__ void splitkv_body(const DecodeParams& p, int unit, in
     for (int it = 0; it < nslot; ++it) {
       wait_slots_ahead(wide, (it == 0 && nslot > 1) ? 1 : 0);
       lds_barrier();
-      if (it >= 1 && it + 1 < nslot) issue(s0 + it + 1, (it + 1) % kSlots);
-      process(slot_base(ring_lds + (it % kSlots) * kSlotLds), s0 + it, it == 0);
+      if (it >= 1 && it + 1 < nslot) issue(slot_at(it + 1), (it + 1) % kSlots);
+      process(slot_base(ring_lds + (it % kSlots) * kSlotLds), slot_at(it), it == 0);
     }
     // row sums and true maxima of each score wave's token share
     float lsum = l_part;
@@ -399,7 +399,7 @@ __device__ __forceinline__ void splitkv_body(const DecodeParams& p, int unit, in
 #pragma unroll
       for (int r2 = 0; r2 < RG; ++r2) o[c][r2] = f32x4{0.f, 0.f, 0.f, 0.f};
     lds_barrier();   // flags and stat read by everyone before they are written again
-    for (int k = 0; k < min(kSlots, nslot); ++k) issue(s0 + k, k);
+    for (int k = 0; k < min(kSlots, nslot); ++k) issue(slot_at(k), k);
   }
 
   // ---- finalize: row r = r2*16 + n16 of the group is query token

@@ -154,22 +154,22 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode_fp8(DecodeParams p
   const int rg = wave % RG, tq = wave / RG;   // score role: row group, token share
   const bool dma_wave = wave < kDmaLanes / 64;
 
-  int unit, grp;   // segment (tokens [t_begin, t_end) of sequence b) and query group
+  int unit, grp;   // segment and query group
   work_item(p.groups, unit, grp);
   if (unit >= p.segments) return;
-  const int4 seg = p.seg_desc[unit];
-  const int b = seg.x, t_begin = seg.y, t_end = seg.z, L = seg.w;
-  if (b < 0 || t_begin >= t_end) return;   // no segment: the combine never reads it
+  const SegDesc seg = p.seg_desc[unit];   // slots first + i * stride (i < ntiles) of sequence b
+  const int b = seg.b, L = seg.L;
+  if (b < 0 || seg.ntiles < 1) return;   // no segment: the combine never reads it
 
   // Query token of the score role's rows; a repeat of token Sq - 1 (computed,
   // never written) fills the second half of the last group when Sq is odd.
   const int j_grp = QG * grp + (rg >> 1);
   const int j = j_grp < p.Sq ? j_grp : p.Sq - 1;
-  const int limit = min(t_end, L - p.Sq + j + 1);   // rows of this wave see tokens < limit
+  const int limit = L - p.Sq + j + 1;   // rows of this wave see tokens < limit
 
   const uint32_t ring_lds = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)ring);
-  const int s0 = t_begin / kSlotTok;
-  const int nslot = (t_end - t_begin + kSlotTok - 1) / kSlotTok;
+  const int nslot = seg.ntiles;
+  auto slot_at = [&](int i) { return seg.first + i * seg.stride; };   // absolute slot index
 
   // A slot is copied by waves 0-3 into 672-byte LDS rows: LDS chunk
   // P = (wave * kLoadsPerLane + i) * 64 + lane is chunk c = P % 42 of token
@@ -194,7 +194,7 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode_fp8(DecodeParams p
   auto issue = [&](int ts, int r) {
     if (!dma_wave) return;
     const uint8_t* src;
-    int nval = min(kSlotTok, t_end - ts * kSlotTok);
+    int nval = min(kSlotTok, L - ts * kSlotTok);
     if constexpr (PAGED) {
       const int page = p.block_table[(size_t)b * p.max_pages + ts];
       src = p.cache + (size_t)page * kF8Tile;
@@ -233,7 +233,7 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode_fp8(DecodeParams p
 #pragma unroll
     for (int i = 0; i < NQ; ++i) dma16(src + ((wave * NQ + i) * 64 + lane) * 16, dst + i * 1024);
   }
-  issue(s0, 0);
+  issue(slot_at(0), 0);
   wait_slots_ahead(1);   // the query rows (older than the first slot) have landed
   lds_barrier();
   // This wave's 16 query rows as MFMA B operands, lane (g, n16) holding row
@@ -264,7 +264,7 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode_fp8(DecodeParams p
   }
   lds_barrier();   // every wave has its query rows before slots 1..2 overwrite them
   const int pro = min(kSlots, nslot);
-  for (int k = 1; k < pro; ++k) issue(s0 + k, k);
+  for (int k = 1; k < pro; ++k) issue(slot_at(k), k);
 
   // value reads: lanes 2r, 2r+1 of the 16-lane group g fetch token
   // t(g, r) = 4g + r (r < 4) or 16 + 4g + r - 4 (+32 for the second step),
@@ -421,8 +421,8 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode_fp8(DecodeParams p
     for (int it = 0; it < nslot; ++it) {
       wait_slots_ahead(it == 0 ? pro - 1 : min(nslot, it + 2) - it - 1);
       lds_barrier();
-      if (it >= 1 && it + 2 < nslot) issue(s0 + it + 2, (it + 2) % kSlots);
-      process(slot_base(ring_lds + (it % kSlots) * kSlotLds), s0 + it, it == 0);
+      if (it >= 1 && it + 2 < nslot) issue(slot_at(it + 2), (it + 2) % kSlots);
+      process(slot_base(ring_lds + (it % kSlots) * kSlotLds), slot_at(it), it == 0);
     }
     // row sums and true maxima of each score wave's token share
     float lsum = l_part;
@@ -450,7 +450,7 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode_fp8(DecodeParams p
 #pragma unroll
       for (int r2 = 0; r2 < RG; ++r2) o[c][r2] = f32x4{0.f, 0.f, 0.f, 0.f};
     lds_barrier();   // flags and stat read by everyone before they are written again
-    for (int k = 0; k < pro; ++k) issue(s0 + k, k);
+    for (int k = 0; k < pro; ++k) issue(slot_at(k), k);
   }
 
   // ---- finalize: row r = r2*16 + n16 of the group is query token

@@ -153,7 +153,21 @@ __device__ void build_schedule(const PrepParams& p, int* lds) {
       c = min(tmax, max(c + 1, (int)(((long long)c * n + p.target_segs - 1) / p.target_segs)));
     }
   }
-  const int chunk = c * kPage;
+  // segment k of the n of a sequence: a contiguous run of c tiles, or with
+  // the balanced schedule and at least kDealMinSplits splits, every n-th tile
+  // from tile k
+  auto desc = [&](int b, int k, int n, int L) {
+    const int tiles = (L + kPage - 1) / kPage;
+    const bool dealt = p.fixed_tiles == 0 && n >= kDealMinSplits;
+    SegDesc d;
+    d.b = b;
+    d.first = dealt ? k : k * c;
+    d.stride = dealt ? n : 1;
+    d.ntiles = dealt ? (tiles - k + n - 1) / n : min(c, tiles - k * c);
+    d.L = L;
+    d.pad[0] = d.pad[1] = d.pad[2] = 0;
+    return d;
+  };
   int carry = 0;
   for (int base = 0; base < p.B; base += 256) {
     const int b = base + t;
@@ -166,8 +180,7 @@ __device__ void build_schedule(const PrepParams& p, int* lds) {
       if (in_lds) {
         starts[b] = first;
       } else {
-        for (int k = 0; k < n && first + k < p.max_segs; ++k)
-          p.seg_desc[first + k] = make_int4(b, k * chunk, min(L, (k + 1) * chunk), L);
+        for (int k = 0; k < n && first + k < p.max_segs; ++k) p.seg_desc[first + k] = desc(b, k, n, L);
       }
     }
     carry += total;
@@ -182,11 +195,15 @@ __device__ void build_schedule(const PrepParams& p, int* lds) {
         if (starts[mid] <= w) lo = mid;
         else hi = mid - 1;
       }
-      const int k = w - starts[lo], L = lens[lo];
-      p.seg_desc[w] = make_int4(lo, k * chunk, min(L, (k + 1) * chunk), L);
+      const int L = lens[lo];
+      p.seg_desc[w] = desc(lo, w - starts[lo], ((L + kPage - 1) / kPage + c - 1) / c, L);
     }
   }
-  for (int w = carry + t; w < p.max_segs; w += 256) p.seg_desc[w] = make_int4(-1, 0, 0, 0);
+  for (int w = carry + t; w < p.max_segs; w += 256) {
+    SegDesc d = {};
+    d.b = -1;
+    p.seg_desc[w] = d;
+  }
   if (bad_len) raise_fault(p.faults, kFaultCtxLen);
 }
 

@@ -75,15 +75,36 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
-// Split schedule.  A sequence's cached tokens are cut into splits of `c`
-// tiles (64 tokens each); every split is one segment, processed by one
+// Split schedule.  A sequence's tiles (64 tokens each) are dealt out to
+// splits of about `c` tiles; every split is one segment, processed by one
 // workgroup of the split-KV kernel.  Segments are numbered sequence by
 // sequence; seg_start[b] is the first segment of sequence b and
-// seg_start[B] the count.  With a fixed kv_chunk, c = kv_chunk / 64; with
-// kv_chunk = 0 the preparation kernel chooses c on the device from the
+// seg_start[B] the count.  With a fixed kv_chunk, c = kv_chunk / 64 and each
+// split is a contiguous run of c tiles (a chunk, or an equal part of one);
+// with kv_chunk = 0 the preparation kernel chooses c on the device from the
 // actual context lengths so that all sequences together give about one
-// segment per compute unit (never below kMinTilesPerSplit tiles).
+// segment per compute unit (never below kMinTilesPerSplit tiles), and when a
+// sequence gets n = ceil(tiles / c) >= kDealMinSplits splits, they take its
+// tiles in turn: split k holds tiles k, k + n, k + 2n, ...  Dealt out this
+// way, the workgroups of a long sequence read neighbouring tiles at any
+// moment instead of regions a split apart, which streams a contiguous cache
+// faster (the LSE combine does not depend on which tokens a split holds).
+// With a few splits per sequence the contiguous runs measured slightly
+// faster.
 constexpr int kMinTilesPerSplit = 2;
+constexpr int kDealMinSplits = 16;
+
+// One segment: tiles first + i * stride (i < ntiles) of sequence b, whose
+// clamped length is L (tokens at or past L are masked; the tile that holds
+// token L - 1 is the only partial one).
+struct alignas(16) SegDesc {
+  int32_t b;        // sequence; -1: no segment (its workgroup returns, the combine never reads it)
+  int32_t first;    // first tile of the segment
+  int32_t stride;   // tile step: 1 for a contiguous run
+  int32_t ntiles;   // tiles of the segment, at least 1
+  int32_t L;        // clamped length of sequence b
+  int32_t pad[3];
+};
 
 // Workspace layout of one decode call (byte offsets, each 256-aligned).
 // rows = B * Sq query tokens; a "head row" is one (query token, head).
@@ -93,7 +114,7 @@ struct WorkspaceLayout {
   size_t qres;      // fp32 [rows][32][512]: W_UK^T q_nope - bf16(W_UK^T q_nope)
   size_t part_o;    // bf16 [max_segs][Sq*32][512]: normalised segment partials
   size_t part_lse;  // fp32 [max_segs][Sq*32], log2 domain
-  size_t seg_desc;  // int4 [max_segs]: {b, first token, end token, L_b}; b = -1: none
+  size_t seg_desc;  // SegDesc [max_segs]
   size_t seg_start; // int32 [B + 1]
   size_t up_part;   // fp32 [rows*32][8][128]: W_UV shares of the 8 latent blocks
   size_t corr_part; // fp32 [rows*32][8]
@@ -113,7 +134,7 @@ inline WorkspaceLayout workspace_layout(int B, int Sq, int max_segs) {
   w.qres = off;      off = align256(off + hrows * kLatent * 4);
   w.part_o = off;    off = align256(off + size_t(max_segs) * seq_rows * kLatent * 2);
   w.part_lse = off;  off = align256(off + size_t(max_segs) * seq_rows * 4);
-  w.seg_desc = off;  off = align256(off + size_t(max_segs) * 16);
+  w.seg_desc = off;  off = align256(off + size_t(max_segs) * sizeof(SegDesc));
   w.seg_start = off; off = align256(off + (size_t(B) + 1) * 4);
   w.up_part = off;   off = align256(off + hrows * 8 * kVDim * 4);
   w.corr_part = off; off = align256(off + hrows * 8 * 4);
@@ -134,7 +155,7 @@ struct DecodeParams {
   int64_t stride_tokens;        // contiguous layout: tokens per sequence block
   const int32_t* block_table;   // paged layout: [B][max_pages]
   int32_t max_pages;
-  const int4* seg_desc;         // [segments]
+  const SegDesc* seg_desc;      // [segments]
   int32_t segments;             // segment records (grid capacity)
   int32_t groups;               // query groups per segment (see work_item)
   int32_t Sq;                   // query tokens per sequence
@@ -241,7 +262,7 @@ struct PrepParams {
   int32_t fixed_tiles;          // tiles per split, or 0: balance on the device
   int32_t target_segs;          // balanced: aim at no more segments than this
   int32_t max_segs;             // capacity of seg_desc / part_o
-  int4* seg_desc;
+  SegDesc* seg_desc;
   int32_t* seg_start;
 };
 

@@ -65,6 +65,7 @@ RAGGED = [
     (3, (3, 70, 200)),
     (4, (4, 100, 500)),
     (16, (16, 40, 300)),
+    (2, (2500, 9)),   # chunk 0: 20 splits of 2 tiles dealt out tile by tile, the last tile partial
 ]
 
 

@@ -144,6 +144,12 @@ RAGGED = [
     (4, (4, 64, 1000)),
     (5, (5, 130)),
     (16, (16, 17, 300)),
+    # with the balanced schedule (chunk 0) the 4,000- and 2,500-token sequences
+    # get 32 and 20 splits of 2 tiles, dealt out tile by tile (every 32nd /
+    # 20th tile from tile k), their last tiles partial; the 1,300-token one
+    # gets 11 contiguous splits
+    (1, (4000, 7)),
+    (3, (3, 2500, 1300, 90)),
 ]
 
 
