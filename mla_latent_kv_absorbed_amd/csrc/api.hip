@@ -278,7 +278,7 @@ mla_status decode_common(const mla_shape* shape, const StepInputs& step, const v
   {
     hipEvent_t ev0 = timed ? g_timing.ev[2 * g_timing.used] : nullptr;
     hipEvent_t ev1 = timed ? g_timing.ev[2 * g_timing.used + 1] : nullptr;
-    const hipError_t e = fp8 ? launch_decode_fp8(p, (int)segs, paged, s, ev0, ev1)
+    const hipError_t e = fp8 ? launch_decode_fp8(p, (int)segs, query_group(Sq, true), paged, s, ev0, ev1)
                              : launch_decode(p, (int)segs, query_group(Sq, false), paged, s, ev0, ev1);
     if (e != hipSuccess) return MLA_ERR_DEVICE;
   }

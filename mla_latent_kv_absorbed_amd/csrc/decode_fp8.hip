@@ -26,12 +26,13 @@
 //    bytes; lane i receives byte i of rows 0..7), which gives each lane 8
 //    tokens of one column in the MFMA k order, and widened to bf16 exactly
 //    (E4M3 values are exact in bf16) for v_mfma_f32_16x16x32_bf16.
-// Slots of 64 tokens (41,984 bytes) stream through a three-slot LDS ring, so
+// Slots of 64 tokens (41,984 bytes, 43,008 in LDS) stream through a three-slot LDS ring, so
 // two slots are in flight while one is consumed; waves 0-3 issue the direct
 // loads.  The query records arrive the same way ahead of the first slot.  A
-// workgroup serves one query token (32 rows); several query tokens of a
-// split are served by workgroups that read the split together (work_item).
-// The kernel is instantiated for QG = 1 only.
+// workgroup serves QG query tokens of 32 rows each (QG = 1 when Sq = 1, else
+// 2: two tokens' P' buffers and the ring fill LDS to within 480 bytes);
+// further query groups of a split are served by workgroups that read the
+// split together (work_item).
 #include "mla_internal.h"
 
 #include <hip/hip_ext.h>
@@ -50,8 +51,10 @@ constexpr int kChunks = kSlotBytes / 16;                   // 2624 sixteen-byte 
 constexpr int kF8ChunksPerRow = kF8Row / 16;               // 41
 constexpr int kRowLds = kF8Row + 16;                       // 672: a row in LDS and a 16-byte pad
 constexpr int kRowChunksLds = kRowLds / 16;                // 42
-constexpr int kLoadsPerLane = (kSlotTok * kRowChunksLds + kDmaLanes - 1) / kDmaLanes;   // 11
-constexpr int kSlotLds = kLoadsPerLane * kDmaLanes * 16;   // 45056: the slot and a pad
+constexpr int kSlotWaveLoads = kSlotTok * kRowChunksLds / 64;   // 42 wave-wide 16-byte loads per slot
+constexpr int kLoadsPerLane = (kSlotWaveLoads + 3) / 4;    // 11: waves 0-2
+constexpr int kLoadsLastWave = kSlotWaveLoads - 3 * kLoadsPerLane;   // 9: wave 3
+constexpr int kSlotLds = kSlotWaveLoads * 1024;            // 43008: the slot's 64 rows of 672 bytes
 constexpr int kSlots = 3;
 constexpr int kCbPerWave = kLatent / 16 / kWaves;          // 4 column blocks of 16 per wave
 
@@ -79,12 +82,19 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Wait until at most `ahead` slots' worth of direct loads are outstanding
-// (waves that issue none pass at once).
-__device__ __forceinline__ void wait_slots_ahead(int ahead) {
-  if (ahead >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kLoadsPerLane) : "memory");
-  else if (ahead == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerLane) : "memory");
+// Wait until at most `ahead` slots' worth of direct loads (N per slot) are
+// outstanding.
+template <int N>
+__device__ __forceinline__ void wait_loads_ahead(int ahead) {
+  if (ahead >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * N) : "memory");
+  else if (ahead == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+// The same for this wave: waves 0-2 issue kLoadsPerLane loads per slot,
+// wave 3 kLoadsLastWave (waves that issue none pass at once).
+__device__ __forceinline__ void wait_slots_ahead(int ahead, bool last_dma_wave) {
+  if (last_dma_wave) wait_loads_ahead<kLoadsLastWave>(ahead);
+  else wait_loads_ahead<kLoadsPerLane>(ahead);
 }
 
 // One 16-byte direct global->LDS load from a wave-uniform base plus a
@@ -153,6 +163,7 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode_fp8(DecodeParams p
   const int g = lane >> 4, n16 = lane & 15;
   const int rg = wave % RG, tq = wave / RG;   // score role: row group, token share
   const bool dma_wave = wave < kDmaLanes / 64;
+  const bool last_dma_wave = wave == kDmaLanes / 64 - 1;
 
   int unit, grp;   // segment and query group
   work_item(p.groups, unit, grp);
@@ -174,7 +185,8 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode_fp8(DecodeParams p
   // A slot is copied by waves 0-3 into 672-byte LDS rows: LDS chunk
   // P = (wave * kLoadsPerLane + i) * 64 + lane is chunk c = P % 42 of token
   // P / 42, i.e. slot chunk P - P / 42 (the row pad c = 41 repeats the row's
-  // chunk 0; positions past the 64th row re-read the slot's first chunks).
+  // chunk 0); the 42 wave-wide loads are loads 0..10 of waves 0-2 and 0..8
+  // of wave 3.
   // With 672-byte rows (mod 256 the same as the bf16 kernel's 1,184-byte
   // rows) the 16-byte score reads of 16 consecutive rows are free of bank
   // conflicts, which the bank-conflict counter showed for 656-byte rows.
@@ -209,10 +221,14 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode_fp8(DecodeParams p
     const uint32_t dst = ring_lds + r * kSlotLds + wave * kLoadsPerLane * 1024;
     if (nval == kSlotTok) {
 #pragma unroll
-      for (int i = 0; i < kLoadsPerLane; ++i) dma16s(src, (dma_off[i >> 1] >> (16 * (i & 1))) & 0xFFFFu, dst + i * 1024);
+      for (int i = 0; i < kLoadsPerLane; ++i) {
+        if (i >= kLoadsLastWave && last_dma_wave) break;
+        dma16s(src, (dma_off[i >> 1] >> (16 * (i & 1))) & 0xFFFFu, dst + i * 1024);
+      }
     } else {
 #pragma unroll
       for (int i = 0; i < kLoadsPerLane; ++i) {
+        if (i >= kLoadsLastWave && last_dma_wave) break;
         const int P = (wave * kLoadsPerLane + i) * 64 + lane;
         const int tok = (P * 3121) >> 17;
         const int c = P - kRowChunksLds * tok;
@@ -224,17 +240,24 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode_fp8(DecodeParams p
   };
 
 
-  // ---- prologue: the 32 query records of the group (head order, kQRecBytes
-  // each, contiguous in the workspace) into ring positions 1..2, copied
-  // linearly, the first slot into position 0
+  // ---- prologue: the ROWS query records of the group (token by token, head
+  // order, kQRecBytes each, contiguous in the workspace) into ring positions
+  // 1..2, copied linearly (the records of a token past Sq - 1, in the last
+  // group of an odd Sq, repeat those of token Sq - 1), the first slot into
+  // position 0
   if (dma_wave) {
     const uint32_t dst = ring_lds + kSlotLds + wave * NQ * 1024;
     const uint8_t* src = (const uint8_t*)p.qabs + ((size_t)b * p.Sq + QG * grp) * 32 * kQRecBytes;
+    const int tokens_here = p.Sq - QG * grp;   // query tokens of this group present (>= 1)
 #pragma unroll
-    for (int i = 0; i < NQ; ++i) dma16(src + ((wave * NQ + i) * 64 + lane) * 16, dst + i * 1024);
+    for (int i = 0; i < NQ; ++i) {
+      int off = ((wave * NQ + i) * 64 + lane) * 16;
+      if (QG > 1 && off >= tokens_here * 32 * kQRecBytes) off -= 32 * kQRecBytes;
+      dma16(src + off, dst + i * 1024);
+    }
   }
   issue(slot_at(0), 0);
-  wait_slots_ahead(1);   // the query rows (older than the first slot) have landed
+  wait_slots_ahead(1, last_dma_wave);   // the query rows (older than the first slot) have landed
   lds_barrier();
   // This wave's 16 query rows as MFMA B operands, lane (g, n16) holding row
   // n16: for latent group k the E4M3 pieces of columns 128k + 16g .. + 16 and
@@ -419,7 +442,7 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode_fp8(DecodeParams p
   // slot it.  A second pass runs only if some row outgrew its reference.
   for (;;) {
     for (int it = 0; it < nslot; ++it) {
-      wait_slots_ahead(it == 0 ? pro - 1 : min(nslot, it + 2) - it - 1);
+      wait_slots_ahead(it == 0 ? pro - 1 : min(nslot, it + 2) - it - 1, last_dma_wave);
       lds_barrier();
       if (it >= 1 && it + 2 < nslot) issue(slot_at(it + 2), (it + 2) % kSlots);
       process(slot_base(ring_lds + (it % kSlots) * kSlotLds), slot_at(it), it == 0);
@@ -480,11 +503,16 @@ __global__ void __launch_bounds__(kThreads, 1) splitkv_decode_fp8(DecodeParams p
 
 }  // namespace
 
-hipError_t launch_decode_fp8(const DecodeParams& p, int segments, bool paged, hipStream_t stream,
+hipError_t launch_decode_fp8(const DecodeParams& p, int segments, int qg, bool paged, hipStream_t stream,
                              hipEvent_t ev_start, hipEvent_t ev_stop) {
   const dim3 grid(decode_grid(segments, p.groups)), block(kThreads);
-  if (paged) hipExtLaunchKernelGGL((splitkv_decode_fp8<1, true>), grid, block, 0, stream, ev_start, ev_stop, 0, p);
-  else hipExtLaunchKernelGGL((splitkv_decode_fp8<1, false>), grid, block, 0, stream, ev_start, ev_stop, 0, p);
+  if (qg == 2) {
+    if (paged) hipExtLaunchKernelGGL((splitkv_decode_fp8<2, true>), grid, block, 0, stream, ev_start, ev_stop, 0, p);
+    else hipExtLaunchKernelGGL((splitkv_decode_fp8<2, false>), grid, block, 0, stream, ev_start, ev_stop, 0, p);
+  } else {
+    if (paged) hipExtLaunchKernelGGL((splitkv_decode_fp8<1, true>), grid, block, 0, stream, ev_start, ev_stop, 0, p);
+    else hipExtLaunchKernelGGL((splitkv_decode_fp8<1, false>), grid, block, 0, stream, ev_start, ev_stop, 0, p);
+  }
   return hipGetLastError();
 }
 

@@ -170,11 +170,10 @@ struct DecodeParams {
 // Query tokens per split-KV workgroup, and the number of such query groups
 // that cover Sq tokens.  A group of two keeps 64 query rows (4 row groups of
 // 16); a single query token uses 32 rows.  For odd Sq > 1 the last group
-// holds one token, and its workgroups run as one-token workgroups.  The
-// 8-bit cache kernel takes one query token per workgroup: with two, its
-// per-wave registers (query rows, accumulators, widened codes) exceed what
-// two waves per SIMD leave.
-inline int query_group(int Sq, bool fp8) { return (Sq == 1 || fp8) ? 1 : kMaxQueryGroup; }
+// holds one token: the bf16 kernel's workgroups of that group run as
+// one-token workgroups, the 8-bit kernel's compute a repeat of token Sq - 1
+// in the second half (never written).
+inline int query_group(int Sq, bool) { return Sq == 1 ? 1 : kMaxQueryGroup; }
 inline int query_groups(int Sq, bool fp8) { return (Sq + query_group(Sq, fp8) - 1) / query_group(Sq, fp8); }
 
 // Workgroups of one split-KV launch: every (segment, query group) pair.
@@ -317,7 +316,7 @@ hipError_t launch_prefill(const uint16_t* q_nope, const uint16_t* q_pe, const ui
                           int32_t L, int32_t Tq, float scale_log2, uint16_t* kv, uint16_t* out, float* lse,
                           uint32_t* faults, hipStream_t stream);
 size_t prefill_workspace_bytes(int32_t L);
-hipError_t launch_decode_fp8(const DecodeParams& p, int segments, bool paged, hipStream_t stream,
+hipError_t launch_decode_fp8(const DecodeParams& p, int segments, int qg, bool paged, hipStream_t stream,
                              hipEvent_t ev_start, hipEvent_t ev_stop);
 
 }  // namespace mla
