@@ -121,14 +121,15 @@ def test_fp8_fused_step_equals_separate_calls_and_is_deterministic(paged):
         np.testing.assert_array_equal(r[1], res[0][1])
 
 
-def test_fp8_paged_equals_contiguous_bitwise():
+@pytest.mark.parametrize("sq", [1, 3])   # one token per workgroup; two, with an odd last group
+def test_fp8_paged_equals_contiguous_bitwise(sq):
     lens = (1000, 64, 130)
-    wl = Workload(100, "fp8-same", len(lens), 1, 1, lens, True, permute_pages=True)
+    wl = Workload(100, "fp8-same", len(lens), sq, 1, lens, True, permute_pages=True)
     outs = []
     for paged in (False, True):
         dw = DeviceWorkload(wl, paged=paged, kv_chunk=128, cache_dtype="fp8")
         li = dw.build_layer(0)
-        lse = torch.empty((len(lens), 1, 32), dtype=torch.float32, device=DEV)
+        lse = torch.empty((len(lens), sq, 32), dtype=torch.float32, device=DEV)
         o, l = dw.step(li, lse=lse)
         outs.append((o.view(torch.int16).cpu().numpy(), l.cpu().numpy().copy()))
     np.testing.assert_array_equal(outs[0][0], outs[1][0])
