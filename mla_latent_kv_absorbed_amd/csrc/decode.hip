@@ -10,8 +10,8 @@
 // W_UV up-projection of the partials follow in kernels.hip.
 //
 // Work decomposition (one workgroup of 8 waves, two per SIMD, per split and
-// query group; a segment record {b, first token, end token, L_b} of the
-// call's schedule describes the split):
+// query group; a segment record of the call's schedule names the split's
+// sequence, its 64-token tiles (first + i * stride) and the sequence length):
 //  * The split streams through LDS in 64-token slots (one page) of a
 //    two-slot ring, filled by direct global->LDS 16-byte loads (9 or 10 per
 //    lane per slot): while the waves consume one slot the next is in flight.

@@ -91,8 +91,8 @@ __device__ __forceinline__ int block_scan256(int v, int* red4, int* total) {
 // of c tiles, c fixed (and sub-split when the chunks leave compute units
 // idle) or chosen here so that the segments of all sequences number at most
 // target_segs where the lengths allow; then the first
-// segment of every sequence and the segment descriptors {b, first token, end
-// token, L_b} in sequence order.  Up to kSchedLds sequences, the lengths and
+// segment of every sequence and the segment descriptors (SegDesc: sequence,
+// first tile, tile stride, tiles, length) in sequence order.  Up to kSchedLds sequences, the lengths and
 // segment starts stay in LDS (`lds`, 2 * kSchedLds + 1 ints) and each
 // descriptor is found by binary search; larger batches take a serial path.
 constexpr int kSchedLds = 2048;
