@@ -64,11 +64,18 @@ def log(msg):
 
 
 def source_hash() -> str:
-    """Hash of the split-KV kernel's sources (the kernel file and the shared definitions)."""
+    """Hash of the split-KV kernel's sources (the kernel file and the shared definitions) with
+    comments and whitespace runs removed: an edit of the code invalidates a counter record, an
+    edit of a comment does not."""
+    import re
+
     h = hashlib.sha256()
     for path in DECODE_SRC:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path, encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
