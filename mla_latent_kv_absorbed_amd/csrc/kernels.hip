@@ -257,40 +257,47 @@ __device__ __forceinline__ int64_t new_token_slot(const PrepParams& p, int b, in
 }
 
 // Rope part of Q_abs for head h and (heads 0 and 1) the new tokens' cache
-// rows, query rows [r0, r1).
+// rows, query rows [r0, r1).  Waves 0-1 rotate the query rope parts, waves
+// 2-3 write the cache rows at the same time (two independent chains of a
+// length load, rotations or a slot lookup, and stores).
 __device__ void prep_rope_and_rows(const PrepParams& p, int h, int r0, int r1) {
   const int t = threadIdx.x;
   constexpr int half = kRope / 2;
-  if (p.rotate) {
-    for (int i = t; i < (r1 - r0) * half; i += 256) {
+  if (t < 128) {
+    for (int i = t; i < (r1 - r0) * half; i += 128) {
       const int r = r0 + i / half, k = i % half;
-      int b;
-      const int pos = query_pos(p, r, &b);
       const size_t hrow = (size_t)r * kHeads + h;
       const uint16_t* src = p.q_pe + hrow * kRope;
-      uint16_t lo, hi;
-      rope_pair(src[k], src[k + half], (double)pos * p.inv.v[k], &lo, &hi);
+      uint16_t lo = src[k], hi = src[k + half];
+      if (p.rotate) {
+        int b;
+        const int pos = query_pos(p, r, &b);
+        rope_pair(lo, hi, (double)pos * p.inv.v[k], &lo, &hi);
+      }
       uint16_t* dst = p.fp8 ? (uint16_t*)((uint8_t*)p.qabs + hrow * kQRecBytes + kQRecRope) : p.qabs + hrow * kRow + kLatent;
       dst[k] = lo;
       dst[k + half] = hi;
     }
-  } else {
-    for (int i = t; i < (r1 - r0) * kRope; i += 256) {
-      const size_t hrow = (size_t)(r0 + i / kRope) * kHeads + h;
-      uint16_t* dst = p.fp8 ? (uint16_t*)((uint8_t*)p.qabs + hrow * kQRecBytes + kQRecRope) : p.qabs + hrow * kRow + kLatent;
-      dst[i % kRope] = p.q_pe[hrow * kRope + i % kRope];
-    }
+    return;
   }
   if (p.c_new == nullptr || h > 1) return;
-  // one wave per new token's row
-  const int wave = t >> 6, lane = t & 63;
-  for (int r = r0 + wave; r < r1; r += 4) {
+  // waves 2 and 3: one new token's row at a time, its values requested
+  // before the slot lookup
+  const int wave = (t >> 6) - 2, lane = t & 63;
+  for (int r = r0 + wave; r < r1; r += 2) {
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    uint16_t klo = 0, khi = 0;
+    if (h == 0) {
+      v = *(const uint4*)(p.c_new + r * p.ld_c + 8 * lane);
+    } else if (lane < half) {
+      klo = p.k_new[r * p.ld_k + lane];
+      khi = p.k_new[r * p.ld_k + lane + half];
+    }
     int b;
     const int pos = query_pos(p, r, &b);
     const int64_t slot = new_token_slot(p, b, pos, lane == 0);
     if (slot < 0) continue;   // wave-uniform
     if (h == 0) {
-      const uint4 v = *(const uint4*)(p.c_new + r * p.ld_c + 8 * lane);
       if (!p.fp8) {
         *(uint4*)(p.cache + slot * kRowBytes + 16 * lane) = v;
       } else {
@@ -319,15 +326,14 @@ __device__ void prep_rope_and_rows(const PrepParams& p, int h, int r0, int r1) {
         if ((lane & 15) == 0) *(float*)(row + kF8ScaleOff + 4 * (lane >> 4)) = scale;
       }
     } else if (lane < half) {
-      const uint16_t* src = p.k_new + r * p.ld_k;
       uint16_t* rope = p.fp8 ? (uint16_t*)(p.cache + slot * kF8Row + kF8RopeOff)
                              : (uint16_t*)(p.cache + slot * kRowBytes) + kLatent;
       if (!p.rotate) {
-        rope[lane] = src[lane];
-        rope[lane + half] = src[lane + half];
+        rope[lane] = klo;
+        rope[lane + half] = khi;
       } else {
         uint16_t lo, hi;
-        rope_pair(src[lane], src[lane + half], (double)pos * p.inv.v[lane], &lo, &hi);
+        rope_pair(klo, khi, (double)pos * p.inv.v[lane], &lo, &hi);
         rope[lane] = lo;
         rope[lane + half] = hi;
       }
