@@ -1,5 +1,6 @@
 """Host behaviour of bench.py that needs no GPU: more than one GPU is refused with a
-message, and the counters summary keeps its calibration arithmetic."""
+message, the counters summary keeps its calibration arithmetic, and the counter
+record's source hash ignores comments but not code."""
 import json
 import os
 import subprocess
@@ -30,3 +31,21 @@ def test_committed_counters_record_is_consistent():
     assert abs(c["WRITE_SIZE_copy_kib"] * c["WRITE_SIZE_scale"] * 1024 - c["copy_bytes"]) < 1e-6 * c["copy_bytes"]
     # at least the cache itself is read (37,748,736 B at 32K)
     assert f["bytes_scaled"] >= 37748736
+
+
+def test_counter_record_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):
+    # the record stays valid across a comment edit of the kernel sources and not
+    # across a code edit
+    sys.path.insert(0, ROOT)
+    import bench
+
+    src = tmp_path / "k.hip"
+    hdr = tmp_path / "k.h"
+    src.write_text("// kernel\nint f(int x) { return x + 1; }  /* one */\n")
+    hdr.write_text("#define N 4\n")
+    monkeypatch.setattr(bench, "DECODE_SRC", [str(src), str(hdr)])
+    h0 = bench.source_hash()
+    src.write_text("// the kernel, reworded\nint f(int x) {\n  return x + 1;   /* one,\n two */\n}\n")
+    assert bench.source_hash() == h0
+    src.write_text("// kernel\nint f(int x) { return x + 2; }  /* one */\n")
+    assert bench.source_hash() != h0
